@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W4A4 hot path on one MI355X.
+
+One step = one pass of the whole online path over one batch: quantize_act
+(load bf16 activations, block Walsh-Hadamard, group-128 absmax, INT4 RNE,
+pack) followed by w4a4_gemm (i8 MFMA, int32 per 128-group, fp32 epilogue,
+bf16 output).  Weights are transformed and packed once before timing, as in
+deployment (the offline step).  Default workload: LLaMA-3-8B q_proj prefill,
+X 2048x4096 bf16 with channel outliers and spikes, W 4096x4096.
+
+Inputs are resident in HBM before the timed region.  Independent buffer sets
+(X, qa, sa, Y and a copy of the packed weights) are rotated so that at least
+512 MB is touched between two uses of a set: the 256 MB Infinity Cache
+cannot serve them.
+
+Prints one JSON line (stdout).  Per-kernel times come from HIP events
+recorded on the stream the library launches on; the GEMM is the dominant
+kernel and its int8-MFMA roofline is reported, the quantize kernel's HBM
+roofline beside it.  The CPU oracle is timed on a bounded sample of the same
+workload as a reported baseline (not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 layer TOPS + quantize GB/s (% roofline) at LLaMA-3-8B q_proj shapes"
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA
+MALL_FLUSH_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="q_proj",
+                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+def workload(name):
+    import datagen
+    if name.startswith("decode"):
+        return datagen.make("decode", M=int(name[len("decode"):]))
+    return datagen.make(name)
+
+
+def algorithmic_bytes(wl):
+    """Quantize: read X once, write qa and sa.  GEMM: read qa, sa, qw, sw once, write Y."""
+    M, K, N = wl.M, wl.K, wl.N
+    G = K // 128
+    xb = 2 if wl.x_dtype == "bf16" else 4
+    yb = 2 if wl.y_dtype == "bf16" else 4
+    quant = M * K * xb + M * K // 2 + M * G * 4
+    gemm = M * K // 2 + M * G * 4 + N * K // 2 + N * G * 4 + M * N * yb
+    return quant, gemm
+
+
+def cpu_baseline(wl, rows):
+    """The oracle as it stands on a sample of `rows` tokens: quantize_act + w4a4_gemm.
+
+    Weights are packed by the oracle beforehand (offline, not timed), as on
+    the GPU.  For Rotated Runtime Smooth the group maxima need every token,
+    so the sample's maxima are taken over the sample.
+    """
+    import oracle
+    from tests.helpers import spec_of
+    spec = spec_of(wl)
+    w = oracle.pack_weight(wl.w, spec)
+    x = wl.x[:rows]
+    t0 = time.perf_counter()
+    a = oracle.quantize_act(x, spec, wl.mode)
+    oracle.w4a4_gemm(a["qa"], a["sa"], w["qw"], w["sw"], wl.y_dtype)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return dt, threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards "
+              "without communication (see the design notes) and no multi-GPU run is made.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rotated_w4a4_amd as rw4
+    from tests import gpu_util as gu
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workload(args.workload)
+    M, K, N = wl.M, wl.K, wl.N
+    G = K // 128
+    log(f"workload {wl.name} M={M} K={K} N={N} transform={wl.transform} mode={wl.mode} "
+        f"device={torch.cuda.get_device_name(dev)}")
+
+    t = gu.transform_for(wl)
+    x0 = gu.x_to_device(wl.x, wl.x_dtype)
+    w0 = torch.from_numpy(wl.w).to(dev)
+    qw0, sw0 = rw4.pack_weight(t, w0)
+    torch.cuda.synchronize()
+    del w0
+
+    ydt = torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32
+    qbytes, gbytes = algorithmic_bytes(wl)
+    set_bytes = qbytes + gbytes
+    nsets = max(2, math.ceil(MALL_FLUSH_BYTES / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            x=x0.clone(),
+            qa=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            sa=torch.empty((M, G), dtype=torch.float32, device=dev),
+            qw=qw0.clone(), sw=sw0.clone(),
+            y=torch.empty((M, N), dtype=ydt, device=dev),
+            ws=torch.zeros((max(G, 4),), dtype=torch.float32, device=dev)))
+    del x0
+    torch.cuda.synchronize()
+    log(f"{nsets} rotating buffer sets of {set_bytes / 2**20:.1f} MiB")
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"])
+        if ev is not None:
+            ev[1].record()
+        rw4.w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"])
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, events on the launch stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [e[0].elapsed_time(e[1]) for e in events]
+    g_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    ops = 2.0 * M * N * K
+    q_us, g_us = 1e3 * float(np.mean(q_ms)), 1e3 * float(np.mean(g_ms))
+    layer_tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (g_us * 1e-6) / 1e12
+    quant_gbps = qbytes / (q_us * 1e-6) / 1e9
+    gemm_gbps = gbytes / (g_us * 1e-6) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
+        f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
+
+    decode = M <= 16
+    if decode:
+        # the small-M GEMM streams the packed weights: HBM-bound
+        roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gemm_gbps / PEAK_HBM_GBPS, "traffic": None,
+                "kernel": "gemm_small_kernel", "algorithmic_bytes_per_launch": gbytes,
+                "avg_launch_us": g_us}
+    else:
+        roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                "frac": gemm_tops / PEAK_I8_TOPS, "traffic": None,
+                "kernel": "gemm_prefill_kernel", "ops_per_launch": ops, "avg_launch_us": g_us,
+                "note": "integer ops (2 per int8 MAC) against the dense int8 MFMA peak"}
+    out = {
+        "metric": METRIC,
+        "value": layer_tops,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on i8 MFMA, int32 accumulate, fp32 transform and epilogue",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} M={M} K={K} N={N}", "M": M, "K": K, "N": N,
+                   "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,
+                   "x_dtype": wl.x_dtype, "y_dtype": wl.y_dtype, "weights": "packed offline",
+                   "buffer_sets": nsets},
+        "roofline": roof,
+        "quantize": {"avg_launch_us": q_us, "gbps": quant_gbps, "frac_hbm": quant_gbps / PEAK_HBM_GBPS,
+                     "algorithmic_bytes": qbytes},
+        "gemm": {"avg_launch_us": g_us, "tops": gemm_tops, "frac_i8_mfma": gemm_tops / PEAK_I8_TOPS,
+                 "gbps": gemm_gbps},
+        "layer_us": ms_per_step * 1e3,
+    }
+
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or (M if M <= 64 else max(16, min(M, 256 * 4096 // K)))
+        dt, threads = cpu_baseline(wl, rows)
+        if dt < 5.0 and rows < M:  # aim for 10-30 s of CPU work
+            rows = min(M, int(rows * 12.0 / max(dt, 1e-3)))
+            dt, threads = cpu_baseline(wl, rows)
+        cpu_tops = 2.0 * rows * N * K / dt / 1e12
+        out["cpu_baseline"] = {"value": cpu_tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+                               "sample": f"{rows} of {M} tokens of the same layer, quantize_act + "
+                                         f"w4a4_gemm (float64 numpy), weights packed beforehand",
+                               "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+        log(f"cpu oracle: {rows} rows in {dt:.2f} s = {cpu_tops * 1e3:.3f} GOPS on {threads} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,13 +63,14 @@ __all__ = [
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 (ties to even), returned as float64.
 
-    Direct rounding from float64 (8 significant bits kept), so there is no
-    double rounding through float32.  Inputs here are finite and far from the
-    bf16 overflow and subnormal ranges.
+    Direct rounding from float64, so there is no double rounding through
+    float32: normal values keep 8 significant bits; below 2^-126 the grid is
+    the subnormal spacing 2^-133.  Inputs must lie below the bf16 maximum.
     """
     x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)  # x = m * 2**e, 0.5 <= |m| < 1
-    return np.ldexp(np.rint(m * 256.0), e - 8)
+    _, e = np.frexp(x)  # x = m * 2**e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)
 
 
 def bf16_bits(x_bf16_valued: np.ndarray) -> np.ndarray:

@@ -1,0 +1,231 @@
+"""Rotated W4A4 hot path on AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``librw4.so`` (C ABI in ``include/rw4.h``): it
+takes torch tensors, passes their device pointers, sizes and the current
+HIP stream, allocates the outputs with torch and turns a non-OK status into
+``RuntimeError``.  Every step of the path runs in the library's HIP
+kernels; there is no fallback.  Importing fails loudly when the library has
+not been built (``python -m rotated_w4a4_amd._build``).
+
+    t = Transform.hadamard(K, block=128)             # or Transform.givens(...)
+    qw, sw = pack_weight(t, w)                       # w: [K, N] (offline)
+    qa, sa = quantize_act(t, x)                      # x: [M, K] bf16 / fp32
+    y = w4a4_gemm(qa, sa, qw, sw, torch.bfloat16)    # [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
+    "status_str", "version", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librw4.so")
+
+RW4_OK = 0
+RW4_F32, RW4_BF16 = 0, 1
+MODES = {"group128": 0, "rrs": 1}
+
+EXPORTED_SYMBOLS = (
+    "rw4_transform_hadamard", "rw4_transform_givens", "rw4_transform_destroy", "rw4_transform_k",
+    "rw4_quantize_act", "rw4_pack_weight", "rw4_w4a4_gemm", "rw4_status_str", "rw4_version",
+)
+
+
+def _load():
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7)
+    # as the system ROCm that librw4.so links against.  Loading torch first
+    # makes the process use one runtime, torch's, for both; the other order
+    # leaves torch on a runtime it was not built for.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m rotated_w4a4_amd._build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+lib.rw4_status_str.restype = ctypes.c_char_p
+lib.rw4_status_str.argtypes = [ctypes.c_int]
+lib.rw4_version.restype = ctypes.c_char_p
+lib.rw4_transform_hadamard.argtypes = [_i64, _i32, _p, ctypes.POINTER(_p)]
+lib.rw4_transform_givens.argtypes = [_i64, _i32, _p, _p, _p, _p, ctypes.POINTER(_p)]
+lib.rw4_transform_destroy.argtypes = [_p]
+lib.rw4_transform_k.argtypes = [_p]
+lib.rw4_transform_k.restype = _i64
+lib.rw4_quantize_act.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
+lib.rw4_pack_weight.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
+lib.rw4_w4a4_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+for _name in ("rw4_transform_hadamard", "rw4_transform_givens", "rw4_transform_destroy",
+              "rw4_quantize_act", "rw4_pack_weight", "rw4_w4a4_gemm"):
+    getattr(lib, _name).restype = ctypes.c_int
+
+
+class RW4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)}")
+        self.status = status
+
+
+def status_str(status: int) -> str:
+    return lib.rw4_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return lib.rw4_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != RW4_OK:
+        raise RW4Error(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RW4_F32
+    if t.dtype == torch.bfloat16:
+        return RW4_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Transform:
+    """Owns a library transform object (a host struct plus device tables)."""
+
+    def __init__(self, handle: ctypes.c_void_p, K: int, kind: str):
+        self._h = handle
+        self.K = K
+        self.kind = kind
+
+    @property
+    def handle(self):
+        return self._h
+
+    @classmethod
+    def hadamard(cls, K: int, block: int = 128, stream=None) -> "Transform":
+        h = ctypes.c_void_p()
+        _check(lib.rw4_transform_hadamard(int(K), int(block), stream, ctypes.byref(h)),
+               "rw4_transform_hadamard")
+        return cls(h, int(K), f"hadamard{block}")
+
+    @classmethod
+    def givens(cls, K: int, pairs, theta, beta, stream=None) -> "Transform":
+        """pairs uint8 [K/128, L, 64, 2] (0xFF = empty), theta fp32 [K/128, L, 64], beta fp32 [K]."""
+        pairs = np.ascontiguousarray(pairs, dtype=np.uint8)
+        theta = np.ascontiguousarray(theta, dtype=np.float32)
+        beta = np.ascontiguousarray(beta, dtype=np.float32)
+        G = int(K) // 128
+        L = pairs.shape[1]
+        if pairs.shape != (G, L, 64, 2) or theta.shape != (G, L, 64) or beta.shape != (int(K),):
+            raise ValueError("pairs/theta/beta shapes do not match K")
+        h = ctypes.c_void_p()
+        _check(lib.rw4_transform_givens(int(K), int(L), pairs.ctypes.data, theta.ctypes.data,
+                                        beta.ctypes.data, stream, ctypes.byref(h)),
+               "rw4_transform_givens")
+        return cls(h, int(K), f"givens{L}")
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _check(lib.rw4_transform_destroy(self._h), "rw4_transform_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, workspace=None):
+    """Transform + INT4-quantize activations x [M, K] (bf16/fp32, unit stride in K).
+
+    Returns (qa uint8 [M, K/2], sa fp32 [M, K/128]).  For mode="rrs" a
+    workspace of K/128 fp32 is allocated unless given (it receives s_g).
+    """
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    M, K = x.shape
+    G = K // 128
+    if qa is None:
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    if mode == "rrs" and workspace is None:
+        workspace = torch.empty((max(G, 4),), dtype=torch.float32, device=x.device)
+    _check(lib.rw4_quantize_act(t.handle, MODES[mode], _ptr(x), _dtype_code(x), M, x.stride(0),
+                                _ptr(qa), _ptr(sa), _ptr(workspace), _stream(x.device)),
+           "rw4_quantize_act")
+    return qa, sa
+
+
+def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None):
+    """Transform + INT4-pack weights. layout "kn": w is [K, N]; "nk": w is [N, K] (nn.Linear).
+
+    Returns (qw uint8 [N, K/2], sw fp32 [N, K/128]).
+    """
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    if layout == "kn":
+        K, N = w.shape
+        sk, sn = w.stride(0), w.stride(1)
+    elif layout == "nk":
+        N, K = w.shape
+        sn, sk = w.stride(0), w.stride(1)
+    else:
+        raise ValueError(layout)
+    if qw is None:
+        qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    if sw is None:
+        sw = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
+    _check(lib.rw4_pack_weight(t.handle, _ptr(w), _dtype_code(w), N, sk, sn, _ptr(qw), _ptr(sw),
+                               _stream(w.device)),
+           "rw4_pack_weight")
+    return qw, sw
+
+
+def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
+    """Y [M, N] = sum over groups of sa * sw * int32 group products (fp32 epilogue)."""
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    M, Kh = qa.shape
+    N = qw.shape[0]
+    K = Kh * 2
+    if qw.shape[1] != Kh or sa.shape != (M, K // 128) or sw.shape != (N, K // 128):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    if out.stride(1) != 1:
+        raise ValueError("out must have unit stride along N")
+    for tns in (qa, sa, qw, sw):
+        if not tns.is_contiguous():
+            raise ValueError("qa/sa/qw/sw must be contiguous")
+    _check(lib.rw4_w4a4_gemm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, _ptr(out),
+                             _dtype_code(out), out.stride(0), _stream(qa.device)),
+           "rw4_w4a4_gemm")
+    return out

@@ -1,0 +1,213 @@
+// C ABI of the rotated W4A4 library: argument checks, transform objects,
+// dispatch to the kernel launchers.  See include/rw4.h for the contract.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/rw4.h"
+#include "rw4_internal.h"
+
+struct rw4_transform {
+  rw4::TransformDev dev;
+  int device;
+};
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int kSlots = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+rw4_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return RW4_OK;
+  if (e == hipErrorOutOfMemory) return RW4_ERR_NOMEM;
+  return RW4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rw4_status_str(rw4_status s) {
+  switch (s) {
+    case RW4_OK: return "RW4_OK";
+    case RW4_ERR_ARG: return "RW4_ERR_ARG: invalid argument (null, unknown enum, misaligned, or bad table)";
+    case RW4_ERR_SHAPE: return "RW4_ERR_SHAPE: invalid shape (K % 128, K mismatch, block, layers)";
+    case RW4_ERR_UNSUPPORTED: return "RW4_ERR_UNSUPPORTED: valid but unimplemented combination";
+    case RW4_ERR_HIP: return "RW4_ERR_HIP: HIP runtime call or kernel launch failed";
+    case RW4_ERR_NOMEM: return "RW4_ERR_NOMEM: device allocation failed";
+  }
+  return "RW4_ERR_UNKNOWN";
+}
+
+const char* rw4_version(void) { return "0.1.0"; }
+
+int64_t rw4_transform_k(const rw4_transform* t) { return t ? t->dev.K : 0; }
+
+rw4_status rw4_transform_hadamard(int64_t K, int32_t block, void* stream, rw4_transform** out) {
+  (void)stream;
+  if (!out) return RW4_ERR_ARG;
+  *out = nullptr;
+  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (!pow2(block) || block < 128 || block > K || K % block) return RW4_ERR_SHAPE;
+  if (block > 128 && !rw4::rowh_supported(K)) return RW4_ERR_UNSUPPORTED;
+  auto* t = new (std::nothrow) rw4_transform();
+  if (!t) return RW4_ERR_NOMEM;
+  t->dev = rw4::TransformDev{rw4::TransformKind::Hadamard, K, block, 0, nullptr, nullptr, nullptr, nullptr};
+  if (hipGetDevice(&t->device) != hipSuccess) t->device = -1;
+  *out = t;
+  return RW4_OK;
+}
+
+rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_host,
+                                const float* theta_host, const float* beta_host, void* stream,
+                                rw4_transform** out) {
+  if (!out) return RW4_ERR_ARG;
+  *out = nullptr;
+  if (!pairs_host || !theta_host || !beta_host) return RW4_ERR_ARG;
+  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (layers < 1 || layers > 64) return RW4_ERR_SHAPE;
+  const int64_t G = K / kGroup;
+  const size_t n_slots = size_t(G) * layers * kSlots;
+  std::vector<uint16_t> idx(n_slots);
+  std::vector<float> cs(2 * n_slots);
+  std::vector<float> alpha(K), alpha_inv(K);
+
+  for (int64_t g = 0; g < G; ++g) {
+    for (int l = 0; l < layers; ++l) {
+      const size_t base = (size_t(g) * layers + l) * kSlots;
+      bool used[kGroup] = {};
+      int n_real = 0;
+      // real pairs first, in slot order
+      for (int s = 0; s < kSlots; ++s) {
+        const uint8_t i = pairs_host[(base + s) * 2], j = pairs_host[(base + s) * 2 + 1];
+        if (i == 0xFF && j == 0xFF) continue;
+        if (i >= kGroup || j >= kGroup || i >= j || used[i] || used[j]) return RW4_ERR_ARG;
+        used[i] = used[j] = true;
+        const double th = double(theta_host[base + s]);
+        idx[base + n_real] = uint16_t(i | (j << 8));
+        cs[2 * (base + n_real)] = float(std::cos(th));
+        cs[2 * (base + n_real) + 1] = float(std::sin(th));
+        ++n_real;
+      }
+      // pad with zero-angle pairs of the unused channels: exactly the identity
+      int pending = -1, s = n_real;
+      for (int c = 0; c < kGroup; ++c) {
+        if (used[c]) continue;
+        if (pending < 0) {
+          pending = c;
+        } else {
+          idx[base + s] = uint16_t(pending | (c << 8));
+          cs[2 * (base + s)] = 1.0f;
+          cs[2 * (base + s) + 1] = 0.0f;
+          ++s;
+          pending = -1;
+        }
+      }
+      if (s != kSlots) return RW4_ERR_ARG;  // unreachable: 128 channels always fill 64 slots
+    }
+  }
+  for (int64_t k = 0; k < K; ++k) {
+    const double b = double(beta_host[k]);
+    alpha[k] = float(std::exp(b));
+    alpha_inv[k] = float(std::exp(-b));
+  }
+
+  auto* t = new (std::nothrow) rw4_transform();
+  if (!t) return RW4_ERR_NOMEM;
+  t->dev = rw4::TransformDev{rw4::TransformKind::Givens, K, 0, layers, nullptr, nullptr, nullptr, nullptr};
+  if (hipGetDevice(&t->device) != hipSuccess) {
+    delete t;
+    return RW4_ERR_HIP;
+  }
+  hipError_t e = hipMalloc(&t->dev.lut_idx, n_slots * sizeof(uint16_t));
+  if (e == hipSuccess) e = hipMalloc(&t->dev.lut_cs, n_slots * sizeof(float2));
+  if (e == hipSuccess) e = hipMalloc(&t->dev.alpha, K * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&t->dev.alpha_inv, K * sizeof(float));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(t->dev.lut_idx, idx.data(), n_slots * sizeof(uint16_t), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(t->dev.lut_cs, cs.data(), n_slots * sizeof(float2), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(t->dev.alpha, alpha.data(), K * sizeof(float), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(t->dev.alpha_inv, alpha_inv.data(), K * sizeof(float), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // host staging buffers die on return
+  if (e != hipSuccess) {
+    rw4_transform_destroy(t);
+    return from_hip(e);
+  }
+  *out = t;
+  return RW4_OK;
+}
+
+rw4_status rw4_transform_destroy(rw4_transform* t) {
+  if (!t) return RW4_OK;
+  hipError_t e = hipSuccess;
+  for (void* p : {(void*)t->dev.lut_idx, (void*)t->dev.lut_cs, (void*)t->dev.alpha, (void*)t->dev.alpha_inv}) {
+    if (p) {
+      const hipError_t f = hipFree(p);
+      if (e == hipSuccess) e = f;
+    }
+  }
+  delete t;
+  return from_hip(e);
+}
+
+rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const void* x,
+                            rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
+                            float* workspace, void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (mode != RW4_ACT_GROUP128 && mode != RW4_ACT_RRS_PER_TOKEN) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0) return RW4_ERR_SHAPE;
+  const int64_t K = t->dev.K;
+  const bool rrs = mode == RW4_ACT_RRS_PER_TOKEN;
+  if (rrs && (t->dev.kind != rw4::TransformKind::Hadamard || !rw4::rowh_supported(K)))
+    return RW4_ERR_UNSUPPORTED;
+  if (M == 0) return RW4_OK;
+  if (!x || !qa || !sa) return RW4_ERR_ARG;
+  if (rrs && !workspace) return RW4_ERR_ARG;
+  if (ldx < K) return RW4_ERR_ARG;
+  const int64_t esz = x_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * esz) % 16 || !aligned16(qa) || !aligned16(sa)) return RW4_ERR_ARG;
+  if (rrs && !aligned16(workspace)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_quantize_act(t->dev, rrs, x, x_dtype == RW4_BF16, M, ldx, qa, sa,
+                                           workspace, st));
+}
+
+rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
+                           int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
+                           void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (w_dtype != RW4_F32 && w_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (N < 0) return RW4_ERR_SHAPE;
+  if (N == 0) return RW4_OK;
+  if (!w || !qw || !sw) return RW4_ERR_ARG;
+  if (stride_k <= 0 || stride_n <= 0) return RW4_ERR_ARG;
+  const int64_t esz = w_dtype == RW4_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(w) % esz) || !aligned16(qw) || !aligned16(sw)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_pack_weight(t->dev, w, w_dtype == RW4_BF16, N, stride_k, stride_n, qw,
+                                          sw, st));
+}
+
+rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                         int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype, int64_t ldy,
+                         void* stream) {
+  if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (M == 0 || N == 0) return RW4_OK;
+  if (!qa || !sa || !qw || !sw || !y) return RW4_ERR_ARG;
+  if (ldy < N) return RW4_ERR_ARG;
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(sa) || !aligned16(sw) || !aligned16(y))
+    return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_gemm(qa, sa, qw, sw, M, N, K, y, y_dtype == RW4_BF16, ldy, st));
+}
+
+}  // extern "C"

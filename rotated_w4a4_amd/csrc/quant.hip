@@ -1,0 +1,451 @@
+// Fused transform + INT4 quantize + pack kernels (gfx950).
+//
+// One HBM pass over the activations: load, rotate in registers, group
+// absmax, round, pack, store (the independent-rotation article on
+// codearts.csdn.net, section 3.2, fuses rotate + scale + quantize in one
+// kernel; the QuIP#/QTIP page on mhpn.cn, section 4.2, factors the Hadamard
+// matrix into butterflies).  The same kernels, fed by a strided gather,
+// pack the weights offline.
+//
+// Kernel families:
+//   quant_h128      block-128 Hadamard, group-128 scales.  16 lanes own one
+//                   (row, group); each lane holds 8 consecutive channels:
+//                   3 butterfly stages in registers + 4 across lanes.
+//   quant_rowh      one wave per row for Hadamard blocks up to the whole row
+//                   (K = 512 * E / 8): lane i holds channels 512c + 8i + e,
+//                   so bits 0-2 and 9+ are register stages and bits 3-8 are
+//                   lane stages.  Modes: group-128 scales, or the second
+//                   pass of Rotated Runtime Smooth (divide by the group
+//                   maxima, per-token scale).
+//   rrs_colmax      first RRS pass: the same row transform, then the maximum
+//                   of |x~| over all rows per 128-channel group
+//                   (the Rotated Runtime Smooth page, main equation: s_j is
+//                   a max over tokens; Figure 4 (2): one scale per block).
+//   quant_givens    ParoQuant-style layers of disjoint pair rotations from
+//                   a lookup table, then the alpha scale, in LDS.
+#include "rw4_device.h"
+#include "rw4_internal.h"
+
+namespace rw4 {
+
+// ---------------------------------------------------------------------------
+// quant_h128
+// ---------------------------------------------------------------------------
+// Each wave processes quads of 4 consecutive (row, group) units per
+// iteration; UNITS_PER_ITER quads are loaded before any is transformed.
+template <class Src, int UNROLL>
+__global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t n_units, int64_t G,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s,
+                                                         float post_scale) {
+  const int lane = threadIdx.x & 63;
+  const int seg = lane >> 4;   // which unit of the quad
+  const int sub = lane & 15;   // 8-channel slice of the group
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const int64_t n_quads = (n_units + 3) >> 2;
+
+  for (int64_t quad0 = wave * UNROLL; quad0 < n_quads; quad0 += n_waves * UNROLL) {
+    float v[UNROLL][8];
+    int64_t unit[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      unit[u] = (quad0 + u) * 4 + seg;
+      if (quad0 + u < n_quads && unit[u] < n_units) {
+        const int64_t row = unit[u] / G, grp = unit[u] - row * G;
+        src.load8(row, grp * kGroup + sub * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      fwht8(v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = v[u][e];
+        x = butterfly_x<1>(x, lane);
+        x = butterfly_x<2>(x, lane);
+        x = butterfly_x<4>(x, lane);
+        x = butterfly_x<8>(x, lane);
+        v[u][e] = x;
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+      m = max_x<1>(m);
+      m = max_x<2>(m);
+      m = max_x<4>(m);
+      m = max_x<8>(m);
+      uint32_t b[8];
+      encode<8>(v[u], m, b);
+      const uint32_t packed = pack8_bits(b);
+      if (quad0 + u < n_quads && unit[u] < n_units) {
+        const int64_t row = unit[u] / G, grp = unit[u] - row * G;
+        reinterpret_cast<uint32_t*>(q + row * (G * 64) + grp * 64)[sub] = packed;
+        if (sub == 0) s[row * G + grp] = m * post_scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quant_rowh / rrs_colmax: one wave per row, E = K / 64 channels per lane.
+// ---------------------------------------------------------------------------
+template <int E, class Src>
+__device__ __forceinline__ void load_row(const Src& src, int64_t row, int lane, float v[E]) {
+#pragma unroll
+  for (int c = 0; c < E / 8; ++c) src.load8(row, int64_t(c) * 512 + lane * 8, &v[c * 8]);
+}
+
+// Unnormalized Walsh-Hadamard transform over blocks of 2^log2b channels.
+template <int E>
+__device__ __forceinline__ void fwht_row(float v[E], int lane, int log2b) {
+  // bits 0..2: inside each 8-register chunk
+#pragma unroll
+  for (int c = 0; c < E / 8; ++c) fwht8(&v[c * 8]);
+  // bits 3..8: across lanes (lane bit = index bit - 3)
+  if (log2b > 3) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<1>(v[e], lane);
+  }
+  if (log2b > 4) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<2>(v[e], lane);
+  }
+  if (log2b > 5) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<4>(v[e], lane);
+  }
+  if (log2b > 6) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<8>(v[e], lane);
+  }
+  if (log2b > 7) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<16>(v[e], lane);
+  }
+  if (log2b > 8) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = butterfly_x<32>(v[e], lane);
+  }
+  // bits 9..: across chunks, in registers
+#pragma unroll
+  for (int hc = 1; hc < E / 8; hc <<= 1) {
+    if ((hc << 9) >= (1 << log2b)) break;
+#pragma unroll
+    for (int c = 0; c < E / 8; ++c) {
+      if ((c & hc) == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = v[c * 8 + e], b = v[(c | hc) * 8 + e];
+          v[c * 8 + e] = a + b;
+          v[(c | hc) * 8 + e] = a - b;
+        }
+      }
+    }
+  }
+}
+
+// Max |v| over the 16 lanes x 8 registers of chunk c (one 128-channel group).
+template <int E>
+__device__ __forceinline__ float group_absmax(const float v[E], int c) {
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[c * 8 + e]));
+  m = max_x<1>(m);
+  m = max_x<2>(m);
+  m = max_x<4>(m);
+  m = max_x<8>(m);
+  return m;
+}
+
+template <int E, class Src, bool RRS>
+__global__ __launch_bounds__(256) void quant_rowh_kernel(Src src, int64_t M, int log2b,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s,
+                                                         const float* __restrict__ smooth,
+                                                         float post_scale) {
+  constexpr int NC = E / 8;           // chunks per lane
+  constexpr int64_t G = E / 2;        // K / 128
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const int sub = lane & 15;
+
+  // RRS: reciprocal of this lane's group maxima (group of chunk c = 4c + lane/16)
+  float inv_s[NC], s_g[NC];
+  if constexpr (RRS) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      s_g[c] = smooth[c * 4 + (lane >> 4)];
+      inv_s[c] = safe_inv(s_g[c], 1.0f);
+    }
+  }
+
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+    uint32_t* qrow = reinterpret_cast<uint32_t*>(q + row * (G * 64));
+    if constexpr (!RRS) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float m = group_absmax<E>(v, c);
+        uint32_t b[8];
+        encode<8>(&v[c * 8], m, b);
+        qrow[c * 64 + lane] = pack8_bits(b);
+        if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
+      }
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[c * 8 + e] *= inv_s[c];
+          m = fmaxf(m, fabsf(v[c * 8 + e]));
+        }
+      }
+      m = max_x<1>(m);
+      m = max_x<2>(m);
+      m = max_x<4>(m);
+      m = max_x<8>(m);
+      m = max_x<16>(m);
+      m = max_x<32>(m);
+      const float a_t = m * (1.0f / 7.0f);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint32_t b[8];
+        encode<8>(&v[c * 8], m, b);
+        qrow[c * 64 + lane] = pack8_bits(b);
+        if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
+      }
+    }
+  }
+}
+
+// First RRS pass.  smooth[] must be zero on entry (fill_kernel); it receives
+// max over rows of the unnormalized |H x| per 128-channel group.  Values
+// are non-negative, so their float bit patterns order like unsigned ints.
+template <int E, class Src>
+__global__ __launch_bounds__(256) void rrs_colmax_kernel(Src src, int64_t M, int log2b,
+                                                         float* __restrict__ smooth) {
+  constexpr int NC = E / 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  float gmax[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) gmax[c] = 0.0f;
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gmax[c] = fmaxf(gmax[c], fabsf(v[c * 8 + e]));
+    }
+  }
+  __shared__ float red[4][E / 2];
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float m = gmax[c];
+    m = max_x<1>(m);
+    m = max_x<2>(m);
+    m = max_x<4>(m);
+    m = max_x<8>(m);
+    if ((lane & 15) == 0) red[w][c * 4 + (lane >> 4)] = m;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < E / 2; g += blockDim.x) {
+    const float m = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+    if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(smooth) + g, __float_as_uint(m));
+  }
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float value) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// ---------------------------------------------------------------------------
+// quant_givens: one wave per (group, ROWS rows).  The lookup table holds,
+// per (group, layer, slot), the pair (i | j << 8) and (cos, sin); every
+// layer is a full matching of the 128 channels (padding pairs have angle 0).
+// chan_scale is alpha^-1 for activations (x~ = x R D^-1) and alpha for
+// weights (row n of W~^T is w_n^T R D).
+// ---------------------------------------------------------------------------
+template <class Src, int ROWS>
+__global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, int64_t G, int L,
+                                                          const uint16_t* __restrict__ lut_idx,
+                                                          const float2* __restrict__ lut_cs,
+                                                          const float* __restrict__ chan_scale,
+                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float buf[ROWS][kGroup];
+  const int lane = threadIdx.x;
+  const int64_t grp = blockIdx.x % G;
+  const int64_t row0 = (blockIdx.x / G) * ROWS;
+  const int nrows = int(M - row0 < ROWS ? M - row0 : ROWS);
+
+  for (int r = 0; r < nrows; ++r) {
+    float v[2];
+    src.load2(row0 + r, grp * kGroup + 2 * lane, v);
+    buf[r][2 * lane] = v[0];
+    buf[r][2 * lane + 1] = v[1];
+  }
+  __syncthreads();
+  const uint16_t* idx = lut_idx + grp * L * 64;
+  const float2* cs = lut_cs + grp * L * 64;
+  for (int l = 0; l < L; ++l) {
+    const uint16_t pr = idx[l * 64 + lane];
+    const float2 t = cs[l * 64 + lane];
+    const int i = pr & 0xFF, j = pr >> 8;
+    for (int r = 0; r < nrows; ++r) {
+      const float a = buf[r][i], b = buf[r][j];
+      buf[r][i] = fmaf(t.x, a, t.y * b);
+      buf[r][j] = fmaf(t.x, b, -t.y * a);
+    }
+    __syncthreads();
+  }
+  const float sc0 = chan_scale[grp * kGroup + 2 * lane];
+  const float sc1 = chan_scale[grp * kGroup + 2 * lane + 1];
+  for (int r = 0; r < nrows; ++r) {
+    const float x0 = buf[r][2 * lane] * sc0;
+    const float x1 = buf[r][2 * lane + 1] * sc1;
+    float m = fmaxf(fabsf(x0), fabsf(x1));
+    m = max_x<1>(m);
+    m = max_x<2>(m);
+    m = max_x<4>(m);
+    m = max_x<8>(m);
+    m = max_x<16>(m);
+    m = max_x<32>(m);
+    float xv[2] = {x0, x1};
+    uint32_t b[2];
+    encode<2>(xv, m, b);
+    const uint32_t byte = pack2_bits(b[0], b[1]);
+    const int64_t row = row0 + r;
+    q[row * (G * 64) + grp * 64 + lane] = uint8_t(byte);
+    if (lane == 0) s[row * G + grp] = m * (1.0f / 7.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+int grid_for_waves(int64_t waves_needed, int64_t cap_blocks) {
+  int64_t blocks = (waves_needed + 3) / 4;  // 4 waves per 256-thread block
+  if (blocks > cap_blocks) blocks = cap_blocks;
+  if (blocks < 1) blocks = 1;
+  return int(blocks);
+}
+
+template <class Src>
+hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, float* s, float post,
+                       hipStream_t st) {
+  constexpr int UNROLL = 2;
+  const int64_t n_units = rows * G;
+  const int64_t n_quads = (n_units + 3) / 4;
+  const int grid = grid_for_waves((n_quads + UNROLL - 1) / UNROLL, 256 * 32);
+  hipLaunchKernelGGL((quant_h128_kernel<Src, UNROLL>), dim3(grid), dim3(256), 0, st, src, n_units, G,
+                     q, s, post);
+  return hipGetLastError();
+}
+
+template <int E, class Src>
+hipError_t launch_rowh(const Src& src, int64_t rows, int log2b, bool rrs, uint8_t* q, float* s,
+                       float* smooth, float post, hipStream_t st) {
+  const int grid = grid_for_waves(rows, 256 * 16);
+  if (rrs) {
+    const int64_t G = E / 2;
+    hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, smooth, G, 0.0f);
+    hipLaunchKernelGGL((rrs_colmax_kernel<E, Src>), dim3(grid), dim3(256), 0, st, src, rows, log2b,
+                       smooth);
+    hipLaunchKernelGGL((quant_rowh_kernel<E, Src, true>), dim3(grid), dim3(256), 0, st, src, rows,
+                       log2b, q, s, (const float*)smooth, post);
+  } else {
+    hipLaunchKernelGGL((quant_rowh_kernel<E, Src, false>), dim3(grid), dim3(256), 0, st, src, rows,
+                       log2b, q, s, (const float*)nullptr, post);
+  }
+  return hipGetLastError();
+}
+
+template <class Src>
+hipError_t dispatch_rowh(const Src& src, int64_t K, int64_t rows, int log2b, bool rrs, uint8_t* q,
+                         float* s, float* smooth, float post, hipStream_t st) {
+  switch (K) {
+    case 512: return launch_rowh<8>(src, rows, log2b, rrs, q, s, smooth, post, st);
+    case 1024: return launch_rowh<16>(src, rows, log2b, rrs, q, s, smooth, post, st);
+    case 2048: return launch_rowh<32>(src, rows, log2b, rrs, q, s, smooth, post, st);
+    case 4096: return launch_rowh<64>(src, rows, log2b, rrs, q, s, smooth, post, st);
+    case 8192: return launch_rowh<128>(src, rows, log2b, rrs, q, s, smooth, post, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class Src>
+hipError_t launch_givens(const Src& src, int64_t rows, int64_t G, int L, const uint16_t* idx,
+                         const float2* cs, const float* scale, uint8_t* q, float* s, hipStream_t st) {
+  constexpr int ROWS = 4;
+  const int64_t blocks = G * ((rows + ROWS - 1) / ROWS);
+  hipLaunchKernelGGL((quant_givens_kernel<Src, ROWS>), dim3(blocks), dim3(64), 0, st, src,
+                     rows, G, L, idx, cs, scale, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool rowh_supported(int64_t K) {
+  return K == 512 || K == 1024 || K == 2048 || K == 4096 || K == 8192;
+}
+
+// Activations: X [M, K] row-major.
+hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, bool bf16, int64_t M,
+                               int64_t ldx, uint8_t* q, float* s, float* smooth, hipStream_t st) {
+  const int64_t K = t.K, G = K / kGroup;
+  if (t.kind == TransformKind::Hadamard) {
+    const float post = (rrs ? 1.0f : 1.0f / 7.0f) / sqrtf(float(t.block));
+    int log2b = 0;
+    while ((int64_t(1) << log2b) < t.block) ++log2b;
+    if (t.block == 128 && !rrs) {
+      if (bf16) return launch_h128(RowSrc<true>{x, ldx}, M, G, q, s, post, st);
+      return launch_h128(RowSrc<false>{x, ldx}, M, G, q, s, post, st);
+    }
+    if (bf16) return dispatch_rowh(RowSrc<true>{x, ldx}, K, M, log2b, rrs, q, s, smooth, post, st);
+    return dispatch_rowh(RowSrc<false>{x, ldx}, K, M, log2b, rrs, q, s, smooth, post, st);
+  }
+  // Givens
+  if (bf16)
+    return launch_givens<RowSrc<true>>(RowSrc<true>{x, ldx}, M, G, t.layers, t.lut_idx,
+                                              t.lut_cs, t.alpha_inv, q, s, st);
+  return launch_givens<RowSrc<false>>(RowSrc<false>{x, ldx}, M, G, t.layers, t.lut_idx,
+                                             t.lut_cs, t.alpha_inv, q, s, st);
+}
+
+// Weights: element (k, n) at w[k * sk + n * sn]; rows of the output are n.
+hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
+                              int64_t sn, uint8_t* q, float* s, hipStream_t st) {
+  const int64_t K = t.K, G = K / kGroup;
+  if (t.kind == TransformKind::Hadamard) {
+    const float post = (1.0f / 7.0f) / sqrtf(float(t.block));
+    int log2b = 0;
+    while ((int64_t(1) << log2b) < t.block) ++log2b;
+    if (t.block == 128) {
+      if (bf16) return launch_h128(StridedSrc<true>{w, sk, sn}, N, G, q, s, post, st);
+      return launch_h128(StridedSrc<false>{w, sk, sn}, N, G, q, s, post, st);
+    }
+    if (bf16)
+      return dispatch_rowh(StridedSrc<true>{w, sk, sn}, K, N, log2b, false, q, s, nullptr, post, st);
+    return dispatch_rowh(StridedSrc<false>{w, sk, sn}, K, N, log2b, false, q, s, nullptr, post, st);
+  }
+  if (bf16)
+    return launch_givens<StridedSrc<true>>(StridedSrc<true>{w, sk, sn}, N, G, t.layers,
+                                                 t.lut_idx, t.lut_cs, t.alpha, q, s, st);
+  return launch_givens<StridedSrc<false>>(StridedSrc<false>{w, sk, sn}, N, G, t.layers,
+                                                t.lut_idx, t.lut_cs, t.alpha, q, s, st);
+}
+
+}  // namespace rw4

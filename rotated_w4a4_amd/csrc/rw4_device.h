@@ -1,0 +1,184 @@
+// Device-side building blocks of the rotated W4A4 kernels (gfx950, wave64).
+//
+// Element sources, cross-lane exchanges for the Walsh-Hadamard butterflies,
+// the round-to-nearest-even INT4 encoder and the nibble packer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rw4 {
+
+constexpr int kGroup = 128;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element sources.  A "row" is the K-vector that gets transformed and
+// quantized: a token of X, or an output channel of W.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Row-major rows with a leading dimension; 8 consecutive elements per call
+// through one (bf16) or two (fp32) 16-byte loads.  Requires 16-byte aligned
+// rows (checked on the host).
+template <bool BF16>
+struct RowSrc {
+  const void* p;
+  int64_t ld;  // elements
+  __device__ __forceinline__ void load8(int64_t row, int64_t k0, float v[8]) const {
+    if constexpr (BF16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + row * ld + k0);
+      v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+      v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+      v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+      v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    } else {
+      const float4* q = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + row * ld + k0);
+      const float4 a = q[0], b = q[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  }
+  __device__ __forceinline__ void load2(int64_t row, int64_t k0, float v[2]) const {
+    if constexpr (BF16) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p) + row * ld + k0);
+      v[0] = bf16_lo(u); v[1] = bf16_hi(u);
+    } else {
+      const float2 a = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(p) + row * ld + k0);
+      v[0] = a.x; v[1] = a.y;
+    }
+  }
+};
+
+// Strided gather: element (row, k) at p[k * sk + row * sr].  Used for the
+// offline weight pack, where W arrives as [K, N] or [N, K].
+template <bool BF16>
+struct StridedSrc {
+  const void* p;
+  int64_t sk, sr;
+  __device__ __forceinline__ float at(int64_t row, int64_t k) const {
+    const int64_t off = k * sk + row * sr;
+    if constexpr (BF16) {
+      return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(p)[off]) << 16);
+    } else {
+      return reinterpret_cast<const float*>(p)[off];
+    }
+  }
+  __device__ __forceinline__ void load8(int64_t row, int64_t k0, float v[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = at(row, k0 + e);
+  }
+  __device__ __forceinline__ void load2(int64_t row, int64_t k0, float v[2]) const {
+    v[0] = at(row, k0);
+    v[1] = at(row, k0 + 1);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange: value of lane (lane ^ M).  DPP quad permutes for
+// M = 1, 2; ds_swizzle (bit-mask mode, within 32 lanes) for 4, 8, 16;
+// ds_bpermute for 32.
+// ---------------------------------------------------------------------------
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M < 32) {
+    x = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
+  } else {
+    const int lane = __lane_id();
+    x = __builtin_amdgcn_ds_bpermute((lane ^ M) << 2, x);
+  }
+  return __int_as_float(x);
+}
+
+// One radix-2 butterfly stage of the Walsh-Hadamard transform across lanes
+// that differ in lane bit M: the lane with the bit clear keeps a + b, the
+// lane with the bit set keeps a - b (a = low partner, b = high partner).
+template <int M>
+__device__ __forceinline__ float butterfly_x(float v, int lane) {
+  const float o = lane_xor<M>(v);
+  const float sgn = (lane & M) ? -1.0f : 1.0f;
+  return fmaf(sgn, v, o);
+}
+
+// Butterfly stages on the low 3 index bits held in one lane's 8 registers.
+__device__ __forceinline__ void fwht8(float v[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((e & h) == 0) {
+        const float a = v[e], b = v[e | h];
+        v[e] = a + b;
+        v[e | h] = a - b;
+      }
+    }
+  }
+}
+
+template <int M>
+__device__ __forceinline__ float max_x(float m) {
+  return fmaxf(m, lane_xor<M>(m));
+}
+
+// ---------------------------------------------------------------------------
+// INT4 encoding.  fmaf(v, inv, 1.5 * 2^23) rounds v * inv to the nearest
+// integer with ties to even (the float spacing is exactly 1 there and the
+// constant's mantissa is even), so the low bits of the result hold the
+// two's-complement code.  |v * inv| <= 7 (1 + 2^-23) by construction, so the
+// code lies in [-7, 7] and no clamp is needed.
+// ---------------------------------------------------------------------------
+constexpr float kRoundMagic = 12582912.0f;      // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+
+__device__ __forceinline__ uint32_t rne_code_bits(float v, float inv) {
+  return __float_as_uint(fmaf(v, inv, kRoundMagic));
+}
+
+// Pack 8 codes (given as magic-rounded float bit patterns, code e at nibble
+// e) into one dword: Horner sum of the raw patterns, then subtract the
+// magic constant from every nibble while adding 8 (offset binary, no
+// borrows), then flip the nibble sign bits back to two's complement.
+__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8]) {
+  uint32_t acc = b[7];
+#pragma unroll
+  for (int e = 6; e >= 0; --e) acc = (acc << 4) + b[e];
+  constexpr uint32_t kOnes = 0x11111111u;
+  constexpr uint32_t kFix = (8u - kRoundMagicBits) * kOnes;  // mod 2^32
+  return (acc + kFix) ^ 0x88888888u;
+}
+
+// Two codes into one byte (low nibble = first).
+__device__ __forceinline__ uint32_t pack2_bits(uint32_t b0, uint32_t b1) {
+  const uint32_t acc = (b1 << 4) + b0;
+  constexpr uint32_t kFix2 = (8u - kRoundMagicBits) * 0x11u;
+  return ((acc + kFix2) ^ 0x88u) & 0xFFu;
+}
+
+__device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f ? num / m : 0.0f; }
+
+// Encoder for a group (or row) whose absolute maximum is m >= 0.  When m is
+// so small that 7 / m would overflow, the values are first scaled by 2^64
+// (exact) so the reciprocal stays finite.  Codes are identical either way.
+constexpr float kTinyMax = 0x1p-100f;
+constexpr float kTinyLift = 0x1p64f;
+
+template <int N>
+__device__ __forceinline__ void encode(float v[N], float m, uint32_t b[N]) {
+  if (m > 0.0f && m < kTinyMax) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] *= kTinyLift;
+    m *= kTinyLift;
+  }
+  const float inv = safe_inv(m, 7.0f);
+#pragma unroll
+  for (int e = 0; e < N; ++e) b[e] = rne_code_bits(v[e], inv);
+}
+
+}  // namespace rw4

@@ -1,0 +1,172 @@
+"""C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments on the host before any device work (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rw4.h")
+
+rw4 = pytest.importorskip("rotated_w4a4_amd", reason="librw4.so not built")
+lib = rw4.lib
+
+OK, ARG, SHAPE, UNSUP, HIP, NOMEM = range(6)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rw4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_hot_calls():
+    names = _declared_functions()
+    for n in ("rw4_quantize_act", "rw4_pack_weight", "rw4_w4a4_gemm"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(rw4.EXPORTED_SYMBOLS)
+
+
+def test_status_strings_and_version():
+    for s in range(6):
+        assert lib.rw4_status_str(s).decode().startswith("RW4_")
+    assert rw4.version() == "0.1.0"
+
+
+def _had(K, block):
+    h = ctypes.c_void_p()
+    st = lib.rw4_transform_hadamard(K, block, None, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("K,block,expect", [
+    (0, 128, SHAPE), (100, 128, SHAPE), (4096, 64, SHAPE), (4096, 96, SHAPE),
+    (4096, 8192, SHAPE), (384, 256, SHAPE), (14336, 256, UNSUP), (4096, 128, OK),
+    (4096, 4096, OK), (14336, 128, OK)])
+def test_hadamard_transform_validation(K, block, expect):
+    st, h = _had(K, block)
+    assert st == expect
+    if st == OK:
+        assert lib.rw4_transform_k(h) == K
+        assert lib.rw4_transform_destroy(h) == OK
+    else:
+        assert not h.value
+
+
+def test_null_out_pointer():
+    assert lib.rw4_transform_hadamard(4096, 128, None, None) == ARG
+
+
+def _givens_tables(K=256, L=2):
+    G = K // 128
+    pairs = np.full((G, L, 64, 2), 0xFF, np.uint8)
+    for g in range(G):
+        for l in range(L):
+            for s in range(60):
+                pairs[g, l, s] = (2 * s + l % 2, 2 * s + 1 + l % 2) if 2 * s + 1 + l % 2 < 128 else (0xFF, 0xFF)
+    return pairs, np.zeros((G, L, 64), np.float32), np.zeros(K, np.float32)
+
+
+@pytest.mark.parametrize("bad", ["i_ge_j", "range", "reuse", "half_empty"])
+def test_givens_rejects_bad_pair_tables(bad):
+    pairs, theta, beta = _givens_tables()
+    if bad == "i_ge_j":
+        pairs[0, 0, 0] = (5, 5)
+    elif bad == "range":
+        pairs[1, 1, 3] = (3, 200)
+    elif bad == "reuse":
+        pairs[0, 1, 0] = (1, 9)
+        pairs[0, 1, 1] = (9, 11)
+    else:
+        pairs[0, 0, 2] = (0xFF, 7)
+    h = ctypes.c_void_p()
+    st = lib.rw4_transform_givens(256, 2, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data,
+                                  None, ctypes.byref(h))
+    assert st == ARG and not h.value
+
+
+def test_givens_shape_and_null_checks():
+    pairs, theta, beta = _givens_tables()
+    h = ctypes.c_void_p()
+    assert lib.rw4_transform_givens(250, 2, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, None, ctypes.byref(h)) == SHAPE
+    assert lib.rw4_transform_givens(256, 0, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, None, ctypes.byref(h)) == SHAPE
+    assert lib.rw4_transform_givens(256, 2, None, theta.ctypes.data, beta.ctypes.data, None, ctypes.byref(h)) == ARG
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device error path")
+def test_givens_without_device_reports_hip_error():
+    pairs, theta, beta = _givens_tables()
+    h = ctypes.c_void_p()
+    st = lib.rw4_transform_givens(256, 2, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data,
+                                  None, ctypes.byref(h))
+    assert st in (HIP, NOMEM) and not h.value
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails validation first
+
+
+def test_quantize_act_validation():
+    st, t = _had(4096, 128)
+    assert st == OK
+    q = lib.rw4_quantize_act
+    # null transform, bad mode, bad dtype
+    assert q(None, 0, FAKE, 1, 4, 4096, FAKE, FAKE, None, None) == ARG
+    assert q(t, 7, FAKE, 1, 4, 4096, FAKE, FAKE, None, None) == ARG
+    assert q(t, 0, FAKE, 9, 4, 4096, FAKE, FAKE, None, None) == ARG
+    # M == 0 is a no-op even with null buffers; negative M is a shape error
+    assert q(t, 0, None, 1, 0, 4096, None, None, None, None) == OK
+    assert q(t, 0, FAKE, 1, -1, 4096, FAKE, FAKE, None, None) == SHAPE
+    # null buffers, ld too small, misaligned pointers and pitch
+    assert q(t, 0, None, 1, 4, 4096, FAKE, FAKE, None, None) == ARG
+    assert q(t, 0, FAKE, 1, 4, 4095, FAKE, FAKE, None, None) == ARG
+    assert q(t, 0, FAKE + 2, 1, 4, 4096, FAKE, FAKE, None, None) == ARG
+    assert q(t, 0, FAKE, 1, 4, 4100, FAKE, FAKE, None, None) == ARG  # 8200-byte pitch
+    assert q(t, 0, FAKE, 1, 4, 4096, FAKE + 4, FAKE, None, None) == ARG
+    # RRS needs a workspace, and is unsupported for K outside the row-kernel set
+    assert q(t, 1, FAKE, 1, 4, 4096, FAKE, FAKE, None, None) == ARG
+    lib.rw4_transform_destroy(t)
+    st, t2 = _had(14336, 128)
+    assert q(t2, 1, FAKE, 1, 4, 14336, FAKE, FAKE, FAKE, None) == UNSUP
+    lib.rw4_transform_destroy(t2)
+
+
+def test_pack_weight_validation():
+    st, t = _had(1024, 128)
+    p = lib.rw4_pack_weight
+    assert p(None, FAKE, 0, 8, 8, 1, FAKE, FAKE, None) == ARG
+    assert p(t, FAKE, 3, 8, 8, 1, FAKE, FAKE, None) == ARG
+    assert p(t, None, 0, 0, 8, 1, None, None, None) == OK
+    assert p(t, FAKE, 0, -2, 8, 1, FAKE, FAKE, None) == SHAPE
+    assert p(t, FAKE, 0, 8, 0, 1, FAKE, FAKE, None) == ARG
+    assert p(t, FAKE + 2, 0, 8, 8, 1, FAKE, FAKE, None) == ARG
+    assert p(t, FAKE, 0, 8, 8, 1, FAKE + 1, FAKE, None) == ARG
+    lib.rw4_transform_destroy(t)
+
+
+def test_gemm_validation():
+    g = lib.rw4_w4a4_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 0, 4, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 0, FAKE, 0, 4, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 4, 128, FAKE, 0, 4, None) == SHAPE
+    assert g(None, None, None, None, 0, 4, 128, None, 0, 4, None) == OK
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 5, 4, None) == ARG
+    assert g(None, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 0, 4, None) == ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 8, 128, FAKE, 0, 4, None) == ARG
+    assert g(FAKE, FAKE, FAKE + 8, FAKE, 4, 4, 128, FAKE, 0, 4, None) == ARG

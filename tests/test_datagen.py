@@ -10,6 +10,11 @@ def test_round_to_bf16_exact_and_idempotent():
     r = datagen.round_to_bf16(x)
     assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0 + 2 ** -7
     assert np.array_equal(datagen.round_to_bf16(r), r)
+    # below 2^-126 the bf16 grid is 2^-133 (subnormals)
+    sub = datagen.round_to_bf16(np.array([1e-39, 3e-40, -2.0 ** -140]))
+    assert np.allclose(sub / 2.0 ** -133, np.rint(sub / 2.0 ** -133), atol=0)
+    assert sub[0] == 11 * 2.0 ** -133 and sub[2] == 0.0
+    datagen.bf16_bits(sub)
     bits = datagen.bf16_bits(r)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     assert np.array_equal(back.astype(np.float64), r)
