@@ -31,8 +31,26 @@ namespace rw4 {
 // ---------------------------------------------------------------------------
 // quant_h128
 // ---------------------------------------------------------------------------
-// Each wave processes quads of 4 consecutive (row, group) units per
-// iteration; UNITS_PER_ITER quads are loaded before any is transformed.
+// Each wave processes quads of 4 consecutive (row, group) units per step,
+// UNROLL quads per loop iteration, in a grid-stride loop; the loads of the
+// next iteration are issued before the current one is transformed, so every
+// wave keeps 2 * UNROLL KB of input in flight.
+template <class Src, int UNROLL>
+__device__ __forceinline__ void h128_load(const Src& src, int64_t quad0, int64_t n_quads, int64_t n_units,
+                                          int64_t G, int seg, int sub, float (&v)[UNROLL][8]) {
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t unit = (quad0 + u) * 4 + seg;
+    if (quad0 + u < n_quads && unit < n_units) {
+      const int64_t row = unit / G, grp = unit - row * G;
+      src.load8(row, grp * kGroup + sub * 8, v[u]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+    }
+  }
+}
+
 template <class Src, int UNROLL>
 __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t n_units, int64_t G,
                                                          uint8_t* __restrict__ q, float* __restrict__ s,
@@ -43,21 +61,18 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t n_unit
   const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
   const int64_t n_quads = (n_units + 3) >> 2;
+  const int64_t stride = n_waves * UNROLL;
 
-  for (int64_t quad0 = wave * UNROLL; quad0 < n_quads; quad0 += n_waves * UNROLL) {
+  float nxt[UNROLL][8];
+  int64_t quad0 = wave * UNROLL;
+  if (quad0 < n_quads) h128_load<Src, UNROLL>(src, quad0, n_quads, n_units, G, seg, sub, nxt);
+  for (; quad0 < n_quads; quad0 += stride) {
     float v[UNROLL][8];
-    int64_t unit[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      unit[u] = (quad0 + u) * 4 + seg;
-      if (quad0 + u < n_quads && unit[u] < n_units) {
-        const int64_t row = unit[u] / G, grp = unit[u] - row * G;
-        src.load8(row, grp * kGroup + sub * 8, v[u]);
-      } else {
+    for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
-      }
-    }
+      for (int e = 0; e < 8; ++e) v[u][e] = nxt[u][e];
+    if (quad0 + stride < n_quads) h128_load<Src, UNROLL>(src, quad0 + stride, n_quads, n_units, G, seg, sub, nxt);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       fwht8(v[u]);
@@ -80,8 +95,9 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t n_unit
       uint32_t b[8];
       encode<8>(v[u], m, b);
       const uint32_t packed = pack8_bits(b);
-      if (quad0 + u < n_quads && unit[u] < n_units) {
-        const int64_t row = unit[u] / G, grp = unit[u] - row * G;
+      const int64_t unit = (quad0 + u) * 4 + seg;
+      if (quad0 + u < n_quads && unit < n_units) {
+        const int64_t row = unit / G, grp = unit - row * G;
         reinterpret_cast<uint32_t*>(q + row * (G * 64) + grp * 64)[sub] = packed;
         if (sub == 0) s[row * G + grp] = m * post_scale;
       }
@@ -349,7 +365,9 @@ hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, floa
   constexpr int UNROLL = 2;
   const int64_t n_units = rows * G;
   const int64_t n_quads = (n_units + 3) / 4;
-  const int grid = grid_for_waves((n_quads + UNROLL - 1) / UNROLL, 256 * 32);
+  // one loop iteration per wave for all but the largest inputs: the
+  // dispatcher keeps every SIMD full and streams new waves as others retire
+  const int grid = grid_for_waves((n_quads + UNROLL - 1) / UNROLL, 65535);
   hipLaunchKernelGGL((quant_h128_kernel<Src, UNROLL>), dim3(grid), dim3(256), 0, st, src, n_units, G,
                      q, s, post);
   return hipGetLastError();
