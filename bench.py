@@ -3,7 +3,7 @@
 
 One step = one pass of the whole online path over one batch: quantize_act
 (load bf16 activations, block Walsh-Hadamard, group-128 absmax, INT4 RNE,
-pack) followed by w4a4_gemm (i8 MFMA, int32 per 128-group, fp32 epilogue,
+pack) followed by w4a4_gemm (FP8 MFMA on the exact codes, per-128-group rescale, fp32 epilogue,
 bf16 output).  Weights are transformed and packed once before timing, as in
 deployment (the offline step).  Default workload: LLaMA-3-8B q_proj prefill,
 X 2048x4096 bf16 with channel outliers and spikes, W 4096x4096.
@@ -15,7 +15,7 @@ cannot serve them.
 
 Prints one JSON line (stdout).  Per-kernel times come from HIP events
 recorded on the stream the library launches on; the GEMM is the dominant
-kernel and its int8-MFMA roofline is reported, the quantize kernel's HBM
+kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported, the quantize kernel's HBM
 roofline beside it.  The CPU oracle is timed on a bounded sample of the same
 workload as a reported baseline (not a target).
 """
@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "W4A4 layer TOPS + quantize GB/s (% roofline) at LLaMA-3-8B q_proj shapes"
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
-PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_I8_TOPS = 5000.0        # MI355X dense FP8 / int8 MFMA (the GEMM runs on the FP8 units)
 MALL_FLUSH_BYTES = 512 << 20
 
 
@@ -60,7 +60,7 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "gemm_dl_kernel": ["gemm.hip", "rw4_device.h"],
+    "gemm_f8_kernel": ["gemm.hip", "rw4_device.h"],
     "gemm_small_kernel": ["gemm.hip", "rw4_device.h"],
     "quant_h128_kernel": ["quant.hip", "rw4_device.h"],
     "quant_rowh_kernel": ["quant.hip", "rw4_device.h"],
@@ -249,7 +249,7 @@ def main():
     log(f"back-to-back: quantize {q_b2b:.2f} us, gemm {g_b2b:.2f} us")
 
     decode = M <= 16
-    gemm_kernel = "gemm_small_kernel" if decode else "gemm_dl_kernel"
+    gemm_kernel = "gemm_small_kernel" if decode else "gemm_f8_kernel"
     traffic = measured_traffic(gemm_kernel, args.workload)
     if decode:
         # the small-M GEMM streams the packed weights: HBM-bound
@@ -262,7 +262,7 @@ def main():
                 "frac": gemm_tops / PEAK_I8_TOPS, "traffic": traffic,
                 "kernel": gemm_kernel, "ops_per_launch": ops, "avg_launch_us": g_us,
                 "algorithmic_bytes_per_launch": gbytes,
-                "note": "integer ops (2 per int8 MAC) against the dense int8 MFMA peak; traffic in bytes"}
+                "note": "ops = 2 M N K (2 per MAC of INT4 codes, computed exactly on the FP8 MFMA) against the dense FP8/int8 MFMA peak; traffic in bytes"}
     quant_kernel = {"hadamard": "quant_h128_kernel" if wl.transform[1] == 128 and wl.mode == "group128"
                     else "quant_rowh_kernel", "givens": "quant_givens_kernel"}[wl.transform[0]]
     out = {
@@ -276,7 +276,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on i8 MFMA, int32 accumulate, fp32 transform and epilogue",
+        "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue",
         "data": "synthetic",
         "config": {"workload": f"{wl.name} M={M} K={K} N={N}", "M": M, "K": K, "N": N,
                    "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,
@@ -289,7 +289,7 @@ def main():
                      "back_to_back_frac_hbm": qbytes / (q_b2b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(quant_kernel, args.workload)},
         "gemm": {"kernel": gemm_kernel, "avg_launch_us": g_us, "tops": gemm_tops,
-                 "frac_i8_mfma": gemm_tops / PEAK_I8_TOPS, "gbps": gemm_gbps,
+                 "frac_mfma": gemm_tops / PEAK_I8_TOPS, "gbps": gemm_gbps,
                  "back_to_back_us": g_b2b, "back_to_back_tops": ops / (g_b2b * 1e-6) / 1e12},
         "layer_us": ms_per_step * 1e3,
     }

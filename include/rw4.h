@@ -34,8 +34,14 @@
  *     (stride_k, stride_n), so both [K, N] and [N, K] (nn.Linear) layouts
  *     work; output Y [M, N] row-major with leading dimension ldy.
  *     K must be a multiple of 128; G = K / 128 is the number of groups.
- *   - Packed INT4: byte b of a row holds code 2b in its low nibble and code
- *     2b+1 in its high nibble, two's complement, codes in [-8, 7].
+ *   - Packed INT4 (this library's layout; the pages fix none): codes lie in
+ *     [-7, 7] (the symmetric scale max/7 never leaves it).  Every 32-bit
+ *     little-endian word (bytes 4w..4w+3 of a row) holds codes c_0..c_7 of
+ *     that word as sign-magnitude nibbles: nibble e (byte e/2, low nibble
+ *     for even e) = |c_e| in bits 0-2 plus the sign (1 = negative) of
+ *     c_((e-1) mod 8) in bit 3; zero has sign 0.  Masking a word with
+ *     0x87878787, and its rotation right by 4 bits likewise, gives the even
+ *     and the odd codes as sign-magnitude bytes.
  *     qa is [M, K/2] bytes, qw is [N, K/2] bytes, rows contiguous.
  *   - Scales: fp32, row-major, sa [M, G], sw [N, G].
  *   - stream is a hipStream_t (NULL = the null stream).  Every call checks
@@ -137,10 +143,13 @@ rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dt
                            void* stream);
 
 /* w4a4_gemm: Y = sum over groups of sa * sw * (qa . qw^T restricted to the
- * group), int32 accumulation inside each 128-wide group on the i8 matrix
- * cores, fp32 epilogue, output rounded once to y_dtype (F32, or BF16 with
- * round-to-nearest-even).  Any M >= 0, N >= 0; K % 128 == 0.
- *   y [M, N] with leading dimension ldy >= N elements. */
+ * group).  Each group's integer dot products are exact (FP8 matrix cores on
+ * the codes as exact small values, fp32 accumulation of integers below
+ * 2^24); the per-group rescale and the sum over groups are fp32, the output
+ * is rounded once to y_dtype (F32, or BF16 with round-to-nearest-even).
+ * Any M >= 0, N >= 0; K % 128 == 0 and K <= 2^24 (RW4_ERR_SHAPE otherwise).
+ *   y [M, N] with leading dimension ldy >= N elements (16-byte aligned
+ *   pointer; rows whose byte stride is a multiple of 16 get wide stores). */
 rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype,
                          int64_t ldy, void* stream);

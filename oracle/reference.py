@@ -32,7 +32,7 @@ Sources (web pages; a reader has the pages, cited by title and section):
 Readings where the pages are silent or garbled (each is listed with its
 reason in the design notes):
   * rounding is round-half-to-even (numpy ``rint``);
-  * codes are clamped to [-8, 7]; the symmetric scale never produces -8;
+  * codes are clamped to [-7, 7] (the symmetric scale never leaves it);
   * an all-zero group gets scale 0 and codes 0 (no epsilon);
   * Hadamard in Sylvester order, (H)_ij = (-1)^popcount(i AND j), 1/sqrt(b)
     per side;
@@ -42,8 +42,11 @@ reason in the design notes):
     over all tokens of the call (group = 128 contiguous channels = the GEMM
     K-block), then per-token symmetric INT4; the stored activation scale of
     (token t, group g) is a_t * s_g;
-  * packed INT4: byte b of a row holds code 2b in its low nibble and code
-    2b+1 in its high nibble, two's complement.
+  * the symmetric quantizer's codes lie in [-7, 7] (scale = max / 7), the
+    range the packed form holds;
+  * packed INT4 (the pages fix no layout): sign-magnitude nibbles, 8 codes
+    per little-endian 32-bit word; nibble e (byte e // 2, low nibble for
+    even e) holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 8) in bit 3.
 
 Shapes: X [M, K] (tokens x input channels), W [K, N], Y = X W [M, N];
 group size g = 128, G = K / g.
@@ -56,7 +59,7 @@ import numpy as np
 
 GROUP = 128
 QMAX = 7      # 2^(4-1) - 1
-QMIN = -8
+QMIN = -QMAX  # symmetric: max / 7 never gives -8
 
 __all__ = [
     "GROUP", "QMAX", "QMIN",
@@ -193,7 +196,7 @@ def transform_weight(W: np.ndarray, spec: dict) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def _rtn(v: np.ndarray) -> np.ndarray:
-    """Round half to even, clamp to the INT4 range [-8, 7]."""
+    """Round half to even, clamp to the symmetric range [-7, 7] (a no-op for |v| <= 7)."""
     return np.clip(np.rint(v), QMIN, QMAX)
 
 
@@ -235,7 +238,7 @@ def quantize_rrs(xt: np.ndarray, g: int = GROUP, quantizer=None):
       s_g    = max over all tokens t and channels j in g of |xt[t, j]|
       z      = xt / s_g(j)                (0 where s_g = 0)
       a_t    = max_j |z[t, j]| / 7
-      q      = clamp(rne(z / a_t), -8, 7) (0 where a_t = 0)
+      q      = clamp(rne(z / a_t), -7, 7) (0 where a_t = 0)
       sa[t, g] = a_t * s_g
 
     ``quantizer`` replaces the INT4 rounding when given (a test hook: the
@@ -262,26 +265,43 @@ def quantize_rrs(xt: np.ndarray, g: int = GROUP, quantizer=None):
 # --------------------------------------------------------------------------
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """[R, K] codes in [-8, 7] -> [R, K/2] bytes: code 2b low nibble, code 2b+1 high nibble."""
+    """[R, K] codes in [-7, 7] -> [R, K/2] bytes, K a multiple of 8.
+
+    Sign-magnitude nibbles, 8 codes c_0..c_7 per little-endian 32-bit word
+    (bytes 4w..4w+3 of the row): nibble e of the word (byte e // 2, low
+    nibble for even e) holds |c_e| in its bits 0-2, and its bit 3 holds the
+    sign (1 = negative) of the code before it, c_((e-1) mod 8).  Zero is
+    always stored with sign 0.  (No page fixes a packed layout; this one
+    lets a reader split a word into two 4-byte groups of sign-magnitude
+    bytes with one mask and one rotate + mask.)
+    """
     c = np.asarray(codes)
-    if c.shape[-1] % 2:
-        raise ValueError("row length must be even")
+    if c.shape[-1] % 8:
+        raise ValueError("row length must be a multiple of 8")
     if c.min(initial=0) < QMIN or c.max(initial=0) > QMAX:
-        raise ValueError("code out of INT4 range")
-    u = (c.astype(np.int64) & 0xF).astype(np.uint8)
-    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+        raise ValueError("code out of the symmetric INT4 range [-7, 7]")
+    c = c.astype(np.int64)
+    words = c.reshape(c.shape[:-1] + (c.shape[-1] // 8, 8))
+    mag = np.abs(words)
+    neg = (words < 0).astype(np.int64)
+    nib = mag | (np.roll(neg, 1, axis=-1) << 3)   # nibble e gets the sign of code e-1
+    nib = nib.reshape(c.shape)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
-    """Inverse of pack_int4: sign-extend each nibble."""
+    """Inverse of pack_int4: int8 codes [R, 2 * bytes]."""
     p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
-    lo, hi = p & 0xF, (p >> 4) & 0xF
-    lo = np.where(lo >= 8, lo - 16, lo)
-    hi = np.where(hi >= 8, hi - 16, hi)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int8)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    return out
+    if p.shape[-1] % 4:
+        raise ValueError("packed row length must be a multiple of 4 bytes")
+    nib = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int64)
+    nib[..., 0::2] = p & 0xF
+    nib[..., 1::2] = p >> 4
+    words = nib.reshape(nib.shape[:-1] + (nib.shape[-1] // 8, 8))
+    mag = words & 7
+    neg = np.roll(words >> 3, -1, axis=-1)          # sign of code e sits in nibble e+1
+    codes = np.where(neg == 1, -mag, mag)
+    return codes.reshape(nib.shape).astype(np.int8)
 
 
 # --------------------------------------------------------------------------

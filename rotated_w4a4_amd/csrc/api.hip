@@ -200,7 +200,7 @@ rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, 
                          int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype, int64_t ldy,
                          void* stream) {
   if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
-  if (M < 0 || N < 0 || K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
   if (M == 0 || N == 0) return RW4_OK;
   if (!qa || !sa || !qw || !sw || !y) return RW4_ERR_ARG;
   if (ldy < N) return RW4_ERR_ARG;

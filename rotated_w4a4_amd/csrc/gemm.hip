@@ -1,43 +1,61 @@
-// W4A4 GEMM on the gfx950 i8 matrix cores.
+// W4A4 GEMM on the gfx950 FP8 matrix cores.
 //
 //   Y[m, n] = sum over 128-wide groups g of sa[m, g] * sw[n, g] * acc[m, n, g]
-//   acc[m, n, g] = sum over k in g of qa[m, k] * qw[n, k]     (exact int32)
+//   acc[m, n, g] = sum over k in g of qa[m, k] * qw[n, k]     (exact)
 //
 // (the Rotated Runtime Smooth page, main equation and Figure 4 (3): the
 // GEMM block equals the quantization group and the scale multiplies the
 // block's partial result; the QuIP#/QTIP page, section 4.2, folds the
 // rotation into the weights so the GEMM itself is a plain product.)
 //
-// INT4 -> int8 unpack: for a packed dword d holding codes k0..k7 (code 2b
-// in the low nibble of byte b), d & 0xF0F0F0F0 gives the odd codes and
-// (d << 4) & 0xF0F0F0F0 the even codes, each byte equal to 16 * code, a
-// valid int8.  Both operands use the same unpack, so the int32 result is
-// 256 * acc exactly (|256 acc| <= 2^21); the 2^-8 is folded into the
-// activation scale.  The unpack permutes codes inside each 8-code block,
-// identically for A and B, which leaves the dot product unchanged.
+// Operands.  A 32-bit word of the stored form holds 8 sign-magnitude codes
+// (nibble e = |c_e| | sign(c_{e-1 mod 8}) << 3).  w & 0x87878787 gives the
+// even codes and rotr(w, 4) & 0x87878787 the odd codes, each as a byte
+// sign << 7 | |c|: an FP8 E4M3 subnormal of value c * 2^-9.  The scaled FP8
+// MFMA with E8M0 operand scale 2^9 on both sides therefore returns acc
+// itself, exactly (integer products, partial sums below 128 * 49 < 2^24).
+// Both operands use the same unpack, so the permutation of codes inside a
+// word is the same on both sides and the dot product over the group is
+// unchanged.
 //
-// Two kernels:
-//   gemm_dl_kernel     M > 16: 128 x 128 block tiles, 4 waves of 64 x 64,
-//                      v_mfma_i32_32x32x32_i8 (4 per group per 32 x 32 tile);
-//                      the scale products sa * sw of a 32 x 32 tile come from
-//                      one v_mfma_f32_32x32x16_bf16 on a 3-way bf16 split of
-//                      each scale, so the VALU only converts and accumulates.
+// Kernels:
+//   gemm_f8_kernel     M > 16: 128 x 128 block tiles, 4 waves of 64 x 64,
+//                      v_mfma_scale_f32_32x32x64_f8f6f4 (2 per group per
+//                      32 x 32 tile); the scale products sa * sw of a tile
+//                      come from one v_mfma_f32_32x32x16_bf16 on a 3-way
+//                      bf16 split of each scale, split once per block and
+//                      group into LDS; the VALU unpacks and accumulates.
 //   gemm_small_kernel  M <= 16 (decode): 16 output channels per block, the
-//                      four waves split the groups, v_mfma_i32_16x16x64_i8
-//                      with fragments loaded straight from global memory.
-// MFMA layouts: lane l supplies row (l % T) of the A tile and row (l % T) of
-// B^T (T = 32 or 16), 16 int8 values; lane l receives, for 32 x 32,
-// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15, and for 16 x 16,
+//                      four waves split the groups, one
+//                      v_mfma_scale_f32_16x16x128_f8f6f4 per group with
+//                      fragments loaded straight from global memory.
+// MFMA result layouts: for 32 x 32, lane l holds
+// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15; for 16 x 16,
 // D[4 (l / 16) + r][l % 16], r = 0..3.
+#include <type_traits>
+
 #include "rw4_device.h"
 #include "rw4_internal.h"
 
 namespace rw4 {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t unpack_lo(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t unpack_hi(uint32_t d) { return d & 0xF0F0F0F0u; }
+constexpr int kE8Scale = 127 + 9;  // E8M0 encoding of 2^9
+
+__device__ __forceinline__ uint32_t f8_even(uint32_t w) { return w & 0x87878787u; }
+__device__ __forceinline__ uint32_t f8_odd(uint32_t w) {
+  return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;
+}
+// 4 stored words (32 codes) -> the 8-dword FP8 operand
+__device__ __forceinline__ v8i f8_operand(v4u w) {
+  return v8i{int(f8_even(w[0])), int(f8_odd(w[0])), int(f8_even(w[1])), int(f8_odd(w[1])),
+             int(f8_even(w[2])), int(f8_odd(w[2])), int(f8_even(w[3])), int(f8_odd(w[3]))};
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,10 +72,6 @@ __device__ __forceinline__ void store_y(void* y, int64_t ldy, int64_t m, int64_t
   }
 }
 
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
 // bf16 truncations with a + b + c == x exactly (8 + 8 + 8 significant bits).
 __device__ __forceinline__ void split3(float x, uint32_t& a, uint32_t& b, uint32_t& c) {
   const uint32_t xa = __float_as_uint(x) & 0xFFFF0000u;
@@ -68,27 +82,46 @@ __device__ __forceinline__ void split3(float x, uint32_t& a, uint32_t& b, uint32
   b = xb >> 16;
   c = __float_as_uint(r2) >> 16;
 }
+// bf16 MFMA operands whose product over K slots 0..5 is
+// a1 b1 + a1 b2 + a2 b1 + a1 b3 + a2 b2 + a3 b1 = x y up to ~2^-24 relative:
+// rows get [a1 a1 a2 a1 a2 a3 0 0], columns [b1 b2 b1 b3 b2 b1 0 0].  From
+// P = x1 | x2 << 16 and Q = x3 | x1 << 16 each operand dword is one byte
+// permute with a selector fixed per wave (rows or columns).
+struct SplitSel {
+  uint32_t s0, s1, s2;
+};
+__device__ __forceinline__ SplitSel split_selectors(bool rows) {
+  // v_perm_b32(P, Q, sel): selector byte values 0-3 pick bytes of Q, 4-7 of P
+  // halves: x1 = P.lo (5,4), x2 = P.hi (7,6), x3 = Q.lo (1,0), x1' = Q.hi (3,2)
+  return rows ? SplitSel{0x05040504u, 0x05040706u, 0x01000706u}   // (x1,x1) (x2,x1) (x2,x3)
+              : SplitSel{0x07060504u, 0x01000504u, 0x05040706u};  // (x1,x2) (x1,x3) (x2,x1)
+}
+__device__ __forceinline__ uint4 split_operand(float x, const SplitSel& sel) {
+  uint32_t a1, a2, a3;
+  split3(x, a1, a2, a3);
+  const uint32_t P = a1 | (a2 << 16), Q = a3 | (a1 << 16);
+  return make_uint4(__builtin_amdgcn_perm(P, Q, sel.s0), __builtin_amdgcn_perm(P, Q, sel.s1),
+                    __builtin_amdgcn_perm(P, Q, sel.s2), 0u);
+}
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS prefill kernel.  Packed INT4 tiles go from global memory
-// straight into LDS (global_load_lds_dwordx4: no VGPR round trip, no VALU)
-// through an S-stage ring, one 128-wide group per stage, with S - 1 groups
-// in flight.  Each wave waits only for the oldest stage (vmcnt) before the
-// block barrier.  LDS rows hold 64 packed bytes as four 16-byte slots, slot
-// index XOR-swizzled by (row >> 2) & 3 so that 16 lanes reading 16 rows hit
-// 16 distinct 4-bank groups.  Lane l of a 32 x 32 tile reads the 32 packed
-// bytes [32 h, 32 h + 32) of its row (h = l / 32) and unpacks k-step ks from
-// bytes 32 h + 8 ks .. + 8; A and B use the same order, so the dot product
-// over the group is unchanged.
+// Direct-to-LDS staging.  Packed tiles go from global memory straight into
+// LDS (global_load_lds_dwordx4: no VGPR round trip, no VALU) through a
+// 3-stage ring, one 128-wide group per stage, two groups in flight.  LDS
+// rows hold 64 packed bytes as four 16-byte slots, the slot index
+// XOR-swizzled by (row >> 2) & 3 so that 16 lanes reading 16 rows hit 16
+// distinct 4-bank groups.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+// Buffer resource over [base, base + bytes) (bytes < 2^31, checked on the
+// host): raw (stride 0) access; out-of-range lanes read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+// 16 bytes per lane from rsrc + voffset + soffset into LDS at lds_base + 16 lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, int(voff), int(soff), 0, 0);
 }
 // Wait until at most n vector-memory instructions of this wave are in flight
 // and all its LDS instructions are done, then a block barrier.  The asm
@@ -101,272 +134,299 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
-// Eight 16-byte LDS reads and four 4-byte LDS reads in one block that waits
-// for all of them before returning (the results are complete on exit).  The
-// data was produced by DMA that the caller has already waited for; keeping
-// these reads out of the compiler's sight stops it from adding a wait for
-// every DMA still in flight.
-__device__ __forceinline__ void lds_read_8x16_4x4(v4u (&v)[8], uint32_t (&w)[4], const uint32_t (&a)[8],
-                                                  const uint32_t (&b)[4]) {
+
+// Shared memory of one block: two stages of two groups each (packed A and
+// B tiles of 128 rows x 64 bytes per group), and the split scale operands
+// of the same four groups.  One object, so every group buffer is a fixed
+// immediate offset from a per-lane base address.  After the main loop the
+// tile area stages the output tile for wide stores.
+constexpr int kTileBytes = 128 * 64;               // one operand of one group
+constexpr int kGroupBytes = 2 * kTileBytes;        // A and B
+constexpr int kStageBytes = 2 * kGroupBytes;       // two groups
+constexpr int kSplitGroupBytes = 256 * 16;         // 128 row + 128 column operands
+struct alignas(16) GemmSmem {
+  uint8_t tile[2 * kStageBytes];
+  uint8_t split[4 * kSplitGroupBytes];
+};
+static_assert(2 * kStageBytes <= 65536 && 4 * kSplitGroupBytes <= 65536, "ds offsets are 16-bit");
+// group buffer q (0..3: stage q / 2, slot q % 2)
+constexpr int tile_off(int q) { return q * kGroupBytes; }
+constexpr int split_off(int q) { return q * kSplitGroupBytes; }
+
+// LDS reads of one group for a wave, in two batches that each wait for
+// their own results (the compiler cannot see these reads, so it adds no
+// wait for the DMA stages still in flight).  Batch 1: the fragments of
+// K-half 0 (A tiles 0/1, B tiles 0/1; tile 1 lies 32 rows = 2048 bytes
+// further; B lies kTileBytes after A).  Batch 2, issued while the first
+// half's MFMAs run: the fragments of K-half 1 and the 4 split-scale
+// operands (tile 1 lies 32 entries = 512 bytes further; columns 2048 bytes
+// after rows).  OT/OS: immediate byte offsets of the group's buffers.
+template <int OT>
+__device__ __forceinline__ void lds_read_half0(v4u (&f)[4], uint32_t a, uint32_t b) {
   asm volatile(
-      "ds_read_b128 %0, %12\n"
-      "ds_read_b128 %1, %13\n"
-      "ds_read_b128 %2, %14\n"
-      "ds_read_b128 %3, %15\n"
-      "ds_read_b128 %4, %16\n"
-      "ds_read_b128 %5, %17\n"
-      "ds_read_b128 %6, %18\n"
-      "ds_read_b128 %7, %19\n"
-      "ds_read_b32 %8, %20\n"
-      "ds_read_b32 %9, %21\n"
-      "ds_read_b32 %10, %22\n"
-      "ds_read_b32 %11, %23\n"
+      "ds_read_b128 %0, %4 offset:%6\n"
+      "ds_read_b128 %1, %4 offset:%7\n"
+      "ds_read_b128 %2, %5 offset:%8\n"
+      "ds_read_b128 %3, %5 offset:%9\n"
       "s_waitcnt lgkmcnt(0)\n"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7]), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3])
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+      : "v"(a), "v"(b), "i"(OT), "i"(OT + 2048), "i"(OT + kTileBytes), "i"(OT + kTileBytes + 2048)
       : "memory");
 }
+template <int OT, int OS>
+__device__ __forceinline__ void lds_read_half1(v4u (&f)[4], v4u (&p)[4], uint32_t a, uint32_t b, uint32_t sa,
+                                               uint32_t sb) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n"
+      "ds_read_b128 %1, %8 offset:%13\n"
+      "ds_read_b128 %2, %9 offset:%14\n"
+      "ds_read_b128 %3, %9 offset:%15\n"
+      "ds_read_b128 %4, %10 offset:%16\n"
+      "ds_read_b128 %5, %10 offset:%17\n"
+      "ds_read_b128 %6, %11 offset:%18\n"
+      "ds_read_b128 %7, %11 offset:%19\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3])
+      : "v"(a), "v"(b), "v"(sa), "v"(sb), "i"(OT), "i"(OT + 2048), "i"(OT + kTileBytes),
+        "i"(OT + kTileBytes + 2048), "i"(OS), "i"(OS + 512), "i"(OS + 2048), "i"(OS + 2048 + 512)
+      : "memory");
+}
+template <int OS>
+__device__ __forceinline__ void lds_write_split(uint32_t addr, v4u v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OS) : "memory");
+}
 
-template <int BM, int BN>
-struct alignas(16) DlStage {
-  uint8_t a[BM * 64];
-  uint8_t b[BN * 64];
-  float sc[BM + BN + 64];  // sa rows, then sw rows, then a landing area for padding loads
-};
-
-template <int BM, int BN, int WM, int WN, int S, bool BF16>
-__global__ __launch_bounds__(256) void gemm_dl_kernel(const uint8_t* __restrict__ qa,
-                                                      const float* __restrict__ sa,
-                                                      const uint8_t* __restrict__ qw,
-                                                      const float* __restrict__ sw, int64_t M,
-                                                      int64_t N, int64_t K, void* __restrict__ y,
-                                                      int64_t ldy) {
-  constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * WAVES_N == 4, "4 waves");
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int IA = BM / 64, IB = BN / 64;          // 1 KB DMA instructions per wave
-  constexpr int SC_BLOCKS = (BM + BN) / 64;          // 64-scale blocks per stage
-  constexpr int SCI = (SC_BLOCKS + 3) / 4;           // scale DMA instructions per wave
-  constexpr int LPW = IA + IB + SCI;                 // vector-memory instructions per wave per stage
-  static_assert(S >= 2 && S <= 4, "stages");
-  static_assert((S - 2) * LPW < 64, "vmcnt");
-
-  __shared__ DlStage<BM, BN> st0;
-  __shared__ DlStage<BM, BN> st1;
-  __shared__ DlStage<BM, BN> st2;
-  __shared__ DlStage<BM, BN> st3;
-  auto stage = [&](int i) -> DlStage<BM, BN>& {
-    return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
-  };
+template <bool BF16>
+__global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restrict__ qa,
+                                                         const float* __restrict__ sa,
+                                                         const uint8_t* __restrict__ qw,
+                                                         const float* __restrict__ sw, int64_t M,
+                                                         int64_t N, int64_t K, void* __restrict__ y,
+                                                         int64_t ldy, int64_t tiles_m) {
+  __shared__ GemmSmem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;
   const int64_t G = K / kGroup;
   const int64_t rowbytes = K / 2;
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t m0 = (blockIdx.x % tiles_m) * BM;
-  const int64_t n0 = (blockIdx.x / tiles_m) * BN;
+  const int64_t m0 = (blockIdx.x % tiles_m) * 128, n0 = (blockIdx.x / tiles_m) * 128;
 
-  // per-lane DMA source offsets (rows clamped into range: every wave issues
-  // the same instructions; data of clamped rows is never stored)
-  const int srow = lane >> 2;                                   // row within a 16-row block
-  const int schunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;     // swizzled source chunk
-  int64_t a_off[IA], b_off[IB];
+  // DMA sources: wave w fills rows [32 w, 32 w + 32) of the A and B tiles,
+  // 16 rows per instruction; rows are clamped into range (every wave issues
+  // the same instructions; data of clamped rows is never stored).  Buffer
+  // ranges cover only the block's rows (<= 128 rows * K / 2 bytes).
+  const int srow = lane >> 2;
+  const int schunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+  const int64_t rows_a = M - m0 < 128 ? M - m0 : 128, rows_b = N - n0 < 128 ? N - n0 : 128;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa + m0 * rowbytes, rows_a * rowbytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + n0 * rowbytes, rows_b * rowbytes);
+  uint32_t a_src[2], b_src[2];
 #pragma unroll
-  for (int i = 0; i < IA; ++i) {
-    const int64_t m = m0 + (wave * IA + i) * 16 + srow;
-    a_off[i] = (m < M ? m : M - 1) * rowbytes + schunk;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t r = (wave * 2 + i) * 16 + srow;
+    a_src[i] = uint32_t((r < rows_a ? r : rows_a - 1) * rowbytes + schunk);
+    b_src[i] = uint32_t((r < rows_b ? r : rows_b - 1) * rowbytes + schunk);
   }
+  auto issue = [&](int q, int64_t g) {  // group g into group buffer q
+    const uint32_t so = uint32_t((g < G ? g : G - 1) * 64);
+    uint8_t* t = sm.tile + tile_off(q);
 #pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int64_t n = n0 + (wave * IB + i) * 16 + srow;
-    b_off[i] = (n < N ? n : N - 1) * rowbytes + schunk;
-  }
-  // scale block q of a stage: sa rows [64q, 64q + 64) for q < BM / 64, then
-  // sw rows; blocks past SC_BLOCKS are padding loads (uniform instruction
-  // count per wave) that land in the spare area and are never read
-  const float* sc_src[SCI];
-  int64_t sc_step[SCI];
-  int sc_dst[SCI];
+    for (int i = 0; i < 2; ++i) dma16(ra, a_src[i], so, t + (wave * 2 + i) * 1024);
 #pragma unroll
-  for (int j = 0; j < SCI; ++j) {
-    const int q = wave * SCI + j;
-    if (q < BM / 64) {
-      const int64_t m = m0 + q * 64 + lane;
-      sc_src[j] = sa + (m < M ? m : M - 1) * G;
-      sc_step[j] = 1;
-      sc_dst[j] = q * 64;
-    } else if (q < SC_BLOCKS) {
-      const int64_t n = n0 + (q - BM / 64) * 64 + lane;
-      sc_src[j] = sw + (n < N ? n : N - 1) * G;
-      sc_step[j] = 1;
-      sc_dst[j] = q * 64;
-    } else {
-      sc_src[j] = sa;
-      sc_step[j] = 0;
-      sc_dst[j] = BM + BN;
-    }
-  }
-
-  auto issue = [&](DlStage<BM, BN>& stg, int64_t g) {
-#pragma unroll
-    for (int i = 0; i < IA; ++i) dma16(qa + a_off[i] + g * 64, stg.a + (wave * IA + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < IB; ++i) dma16(qw + b_off[i] + g * 64, stg.b + (wave * IB + i) * 1024);
-#pragma unroll
-    for (int j = 0; j < SCI; ++j) dma4(sc_src[j] + sc_step[j] * g, stg.sc + sc_dst[j]);
+    for (int i = 0; i < 2; ++i) dma16(rb, b_src[i], so, t + kTileBytes + (wave * 2 + i) * 1024);
   };
 
-  float yacc[TM][TN][16];
+  // this thread splits one scale per group: sa of tile row tid (tid < 128)
+  // or sw of tile column tid - 128 (waves 0-1 rows, waves 2-3 columns)
+  const bool row_scale = wave < 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      row_scale ? make_rsrc(sa + m0 * G, rows_a * G * 4) : make_rsrc(sw + n0 * G, rows_b * G * 4);
+  uint32_t sc_off;  // byte offset of this thread's scale row
+  {
+    const int64_t r = row_scale ? tid : tid - 128;
+    const int64_t lim = row_scale ? rows_a : rows_b;
+    sc_off = uint32_t((r < lim ? r : lim - 1) * G * 4);
+  }
+  auto sc_load = [&](int64_t g) {
+    return __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rs, int(sc_off), int((g < G ? g : G - 1) * 4), 0));
+  };
+  const SplitSel sel = split_selectors(row_scale);
+  const uint32_t sp_addr = lds_off(sm.split + tid * 16);
+  // written with an LDS store the compiler does not see (it would otherwise
+  // wait for the DMA stages in flight, which never target the split
+  // buffers); the next wait_vm_barrier completes it before any wave reads it
+  auto put_split = [&](auto q_const, float x) {
+    constexpr int q = decltype(q_const)::value;
+    const uint4 o = split_operand(x, sel);
+    lds_write_split<split_off(q)>(sp_addr, v4u{o.x, o.y, o.z, o.w});
+  };
+
+  // per-lane LDS read bases (group buffer 0).  Lanes 32..63 supply K slots
+  // 8..15 of the bf16 scale-product MFMA: their row operands are zeroed in
+  // registers, their column operands are finite values that multiply zero.
+  const int frow = lane & 31, h = lane >> 5;
+  uint32_t ba0, ba1, bb0, bb1, bsa, bsb;
+  {
+    const uint32_t t0 = lds_off(sm.tile), s0 = lds_off(sm.split);
+    const int ra_ = wm * 64 + frow, rb_ = wn * 64 + frow;
+    const int xa = (ra_ >> 2) & 3, xb = (rb_ >> 2) & 3;
+    ba0 = t0 + ra_ * 64 + (((2 * h) ^ xa) * 16);
+    ba1 = t0 + ra_ * 64 + (((2 * h + 1) ^ xa) * 16);
+    bb0 = t0 + rb_ * 64 + (((2 * h) ^ xb) * 16);
+    bb1 = t0 + rb_ * 64 + (((2 * h + 1) ^ xb) * 16);
+    bsa = s0 + (wm * 64 + frow) * 16;
+    bsb = s0 + (wn * 64 + frow) * 16;  // + 2048 (column operands) in the read offsets
+  }
+  const uint32_t keep = h ? 0u : 0xFFFFFFFFu;
+
+  float yacc[2][2][16];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
 
-  const int frow = lane & 31, h = lane >> 5;
-  auto compute = [&](DlStage<BM, BN>& stg) {
-    // packed fragments: 8 dwords per tile row/column, plus the scales this
-    // lane needs (one per tile row/column)
-    static_assert(TM == 2 && TN == 2, "batched LDS read assumes a 2 x 2 tile grid per wave");
-    uint32_t pa[TM][8], pb[TN][8];
-    uint32_t addr[8], saddr[4];
+  auto compute = [&](auto q_const) {
+    constexpr int q = decltype(q_const)::value;
+    v4u fr[4], ps[4];
+    v16f acc[2][2];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * WM + i * 32 + frow;
-      const int f = (r >> 2) & 3;
-      addr[2 * i] = lds_off(stg.a + r * 64 + (((2 * h) ^ f) * 16));
-      addr[2 * i + 1] = lds_off(stg.a + r * 64 + (((2 * h + 1) ^ f) * 16));
-      saddr[i] = lds_off(stg.sc + wm * WM + i * 32 + frow);
-    }
+    for (int ks = 0; ks < 2; ++ks) {
+      // fr: A tile 0, A tile 1, B tile 0, B tile 1 of this K-half
+      if (ks == 0)
+        lds_read_half0<tile_off(q)>(fr, ba0, bb0);
+      else
+        lds_read_half1<tile_off(q), split_off(q)>(fr, ps, ba1, bb1, bsa, bsb);
+      v8i oa[2], ob[2];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * WN + j * 32 + frow;
-      const int f = (r >> 2) & 3;
-      addr[4 + 2 * j] = lds_off(stg.b + r * 64 + (((2 * h) ^ f) * 16));
-      addr[4 + 2 * j + 1] = lds_off(stg.b + r * 64 + (((2 * h + 1) ^ f) * 16));
-      saddr[2 + j] = lds_off(stg.sc + BM + wn * WN + j * 32 + frow);
-    }
-    v4u rv[8];
-    uint32_t rs[4];
-    lds_read_8x16_4x4(rv, rs, addr, saddr);
+      for (int i = 0; i < 2; ++i) oa[i] = f8_operand(fr[i]);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int j = 0; j < 2; ++j) ob[j] = f8_operand(fr[2 + j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pa[i][e] = rv[2 * i][e];
-        pa[i][4 + e] = rv[2 * i + 1][e];
-      }
-    }
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[j][e] = rv[4 + 2 * j][e];
-        pb[j][4 + e] = rv[4 + 2 * j + 1][e];
-      }
-    }
-    v16i acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      v4i fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = v4i{int(unpack_lo(pa[i][2 * ks])), int(unpack_hi(pa[i][2 * ks])),
-                    int(unpack_lo(pa[i][2 * ks + 1])), int(unpack_hi(pa[i][2 * ks + 1]))};
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = v4i{int(unpack_lo(pb[j][2 * ks])), int(unpack_hi(pb[j][2 * ks])),
-                    int(unpack_lo(pb[j][2 * ks + 1])), int(unpack_hi(pb[j][2 * ks + 1]))};
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    {
-      v8bf va[TM], vb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (h == 0) {
-          uint32_t a1, a2, a3;
-          split3(__uint_as_float(rs[i]) * (1.0f / 256.0f), a1, a2, a3);
-          u = make_uint4(a1 | (a1 << 16), a2 | (a1 << 16), a2 | (a3 << 16), 0u);
+        for (int j = 0; j < 2; ++j) {
+          const v16f c = ks == 0 ? v16f{} : acc[i][j];
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], c, 0, 0, 0, kE8Scale,
+                                                                     0, kE8Scale);
         }
-        va[i] = __builtin_bit_cast(v8bf, u);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (h == 0) {
-          uint32_t b1, b2, b3;
-          split3(__uint_as_float(rs[2 + j]), b1, b2, b3);
-          u = make_uint4(b1 | (b2 << 16), b1 | (b3 << 16), b2 | (b1 << 16), 0u);
-        }
-        vb[j] = __builtin_bit_cast(v8bf, u);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          v16f p = {};
-          p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], vb[j], p, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) yacc[i][j][r] = fmaf(float(acc[i][j][r]), p[r], yacc[i][j][r]);
-        }
-      }
+      // keep each half's unpack and MFMAs together (bounds register use)
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
+    // scale products, tile by tile, one tile ahead of the accumulation (the
+    // scheduling barriers keep at most two product tiles live)
+    auto prod = [&](int t) {
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ps[t >> 1]),
+                                                     __builtin_bit_cast(v8bf, ps[2 + (t & 1)]), v16f{}, 0,
+                                                     0, 0);
+    };
+    auto accum = [&](int t, const v16f& p) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        yacc[t >> 1][t & 1][r] = fmaf(acc[t >> 1][t & 1][r], p[r], yacc[t >> 1][t & 1][r]);
+    };
+    v16f p0 = prod(0);
+    v16f p1 = prod(1);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(0, p0);
+    p0 = prod(2);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(1, p1);
+    p1 = prod(3);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(2, p0);
+    accum(3, p1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: groups 0 .. S-2 in flight.  Every iteration issues exactly one
-  // stage (past the last group it reloads group G-1 into a stage that is
-  // never read again), so the in-flight count is the same static number
-  // everywhere and the compiler can track which stage each DMA writes.
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(stage(s), s < G ? s : G - 1);
-
-  for (int64_t g0 = 0; g0 < G; g0 += S) {
-#pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int64_t g = g0 + u;
-      if (g >= G) break;
-      // group g has landed for every wave after the barrier; stage u-1
-      // (read in the previous iteration) is free for reuse
-      wait_vm_barrier<(S - 2) * LPW>();
-      const int64_t gn = g + S - 1;
-      issue(stage((u + S - 1) % S), gn < G ? gn : G - 1);
-      compute(stage(u));
-    }
+  // Stage s holds groups 2s and 2s + 1 in group buffers 2 (s % 2) and
+  // 2 (s % 2) + 1.  Iteration s: wait for stage s (everything this wave has
+  // in flight) and a block barrier; issue the scale loads and DMA of stage
+  // s + 1 into the other buffers (all waves finished reading them before
+  // the barrier); compute the two groups; split the scales of stage s + 1.
+  // Past the last group the loads are clamped to group G - 1 and never read.
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  put_split(Q0{}, sc_load(0));
+  put_split(Q1{}, sc_load(1));
+  issue(0, 0);
+  issue(1, 1);
+  const int64_t S = (G + 1) / 2;
+  auto stage = [&](auto q0, auto q1, auto n0_, auto n1_, int64_t s) {
+    wait_vm_barrier<0>();
+    const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
+    issue(decltype(n0_)::value, 2 * s + 2);
+    issue(decltype(n1_)::value, 2 * s + 3);
+    compute(q0);
+    if (2 * s + 1 < G) compute(q1);
+    put_split(n0_, x0);
+    put_split(n1_, x1);
+  };
+  for (int64_t s = 0; s < S; s += 2) {
+    stage(Q0{}, Q1{}, Q2{}, Q3{}, s);
+    if (s + 1 >= S) break;
+    stage(Q2{}, Q3{}, Q0{}, Q1{}, s + 1);
   }
-  // drain the trailing loads: no DMA may outlive the block's LDS allocation
+  // drain the trailing loads: no DMA may outlive the block's LDS allocation,
+  // and the tile area is reused below
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
 
+  // Output: each wave stages its 64 x 64 tile in LDS (row-major), then
+  // writes whole 16-byte chunks of rows; chunks that cross the right edge,
+  // or a leading dimension that breaks 16-byte alignment, use element
+  // stores.
+  constexpr int E = BF16 ? 2 : 4;           // bytes per element
+  constexpr int RB = 64 * E;                // bytes per staged row
+  uint8_t* ot = sm.tile + wave * 64 * RB;   // 8 or 16 KB per wave
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t n = n0 + wn * WN + j * 32 + frow;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (m < M && n < N) store_y<BF16>(y, ldy, m, n, yacc[i][j][r]);
+        const int row = i * 32 + (r >> 2) * 8 + h * 4 + (r & 3), col = j * 32 + frow;
+        if constexpr (BF16)
+          *reinterpret_cast<uint16_t*>(ot + row * RB + col * 2) = f32_to_bf16_rne(yacc[i][j][r]);
+        else
+          *reinterpret_cast<float*>(ot + row * RB + col * 4) = yacc[i][j][r];
+      }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x0 << 8) | 0xF | (3 << 14));  // lgkmcnt(0)
+  const int64_t wr0 = m0 + wm * 64, wc0 = n0 + wn * 64;
+  constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  const bool aligned = ((ldy * E) % 16 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+#pragma unroll
+  for (int it = 0; it < CPR; ++it) {
+    const int idx = it * 64 + lane;
+    const int row = idx / CPR, ch = idx % CPR;
+    const int64_t m = wr0 + row, n = wc0 + ch * (16 / E);
+    if (m >= M) continue;
+    const v4u v = *reinterpret_cast<const v4u*>(ot + row * RB + ch * 16);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(y) + (m * ldy + n) * E;
+    if (aligned && n + 16 / E <= N) {
+      *reinterpret_cast<v4u*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16 / E; ++e) {
+        if (n + e < N) {
+          if constexpr (BF16)
+            reinterpret_cast<uint16_t*>(dst)[e] = uint16_t(v[e / 2] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(dst)[e] = v[e];
+        }
       }
     }
   }
@@ -374,9 +434,11 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Small-M kernel (decode, M <= 16): one block per 16 output channels; the
-// 4 waves split the groups; A and B fragments come straight from global
-// memory (16 bytes per lane per group, no reuse to stage); the partial
-// results are summed across waves in LDS.
+// 4 waves split the groups; lane l supplies row l % 16 and codes
+// [32 (l / 16), 32 (l / 16) + 32) of the group for both operands, so one
+// 16 x 16 x 128 MFMA covers a whole group.  Fragments come straight from
+// global memory (no reuse to stage); the partial results are summed across
+// waves in LDS.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __global__ __launch_bounds__(256) void gemm_small_kernel(const uint8_t* __restrict__ qa,
@@ -399,33 +461,28 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint8_t* __restri
 
   float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t gb = wave; gb < G; gb += 4 * NB) {
-    uint4 pa[NB], pb[NB];
+    v4u pa[NB], pb[NB];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + 4 * t;
       const bool in = g < G;
-      pa[t] = (in && a_ok) ? *reinterpret_cast<const uint4*>(qa + am * rowbytes + g * 64 + part * 16)
-                           : make_uint4(0, 0, 0, 0);
-      pb[t] = (in && b_ok) ? *reinterpret_cast<const uint4*>(qw + bn * rowbytes + g * 64 + part * 16)
-                           : make_uint4(0, 0, 0, 0);
+      pa[t] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + g * 64 + part * 16)
+                           : v4u{0u, 0u, 0u, 0u};
+      pb[t] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + g * 64 + part * 16)
+                           : v4u{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + 4 * t;
       if (g >= G) break;
-      const v4i a0 = {int(unpack_lo(pa[t].x)), int(unpack_hi(pa[t].x)), int(unpack_lo(pa[t].y)), int(unpack_hi(pa[t].y))};
-      const v4i a1 = {int(unpack_lo(pa[t].z)), int(unpack_hi(pa[t].z)), int(unpack_lo(pa[t].w)), int(unpack_hi(pa[t].w))};
-      const v4i b0 = {int(unpack_lo(pb[t].x)), int(unpack_hi(pb[t].x)), int(unpack_lo(pb[t].y)), int(unpack_hi(pb[t].y))};
-      const v4i b1 = {int(unpack_lo(pb[t].z)), int(unpack_hi(pb[t].z)), int(unpack_lo(pb[t].w)), int(unpack_hi(pb[t].w))};
-      v4i acc = {0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
-      const float swv = b_ok ? sw[bn * G + g] * (1.0f / 256.0f) : 0.0f;
+      const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          f8_operand(pa[t]), f8_operand(pb[t]), v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+      const float swv = b_ok ? sw[bn * G + g] : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = (lane >> 4) * 4 + r;
         const float sav = (m < M) ? sa[m * G + g] : 0.0f;
-        yv[r] = fmaf(float(acc[r]), sav * swv, yv[r]);
+        yv[r] = fmaf(acc[r], sav * swv, yv[r]);
       }
     }
   }
@@ -443,20 +500,6 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint8_t* __restri
   }
 }
 
-template <int BM, int BN, int WM, int WN, int S>
-static hipError_t launch_dl(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                            int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
-                            hipStream_t st) {
-  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (y_bf16)
-    hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WM, WN, S, true>), dim3(blocks), dim3(256), 0, st,
-                       qa, sa, qw, sw, M, N, K, y, ldy);
-  else
-    hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WM, WN, S, false>), dim3(blocks), dim3(256), 0, st,
-                       qa, sa, qw, sw, M, N, K, y, ldy);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                        hipStream_t st) {
@@ -470,7 +513,18 @@ hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, co
                          N, K, y, ldy);
     return hipGetLastError();
   }
-  return launch_dl<128, 128, 64, 64, 2>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  // per-block buffer ranges: 128 rows of K / 2 bytes, 128 rows of K / 128 scales
+  if (K > (int64_t(1) << 24)) return hipErrorInvalidValue;
+  const int64_t tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (y_bf16)
+    hipLaunchKernelGGL((gemm_f8_kernel<true>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N, K,
+                       y, ldy, tiles_m);
+  else
+    hipLaunchKernelGGL((gemm_f8_kernel<false>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
+                       K, y, ldy, tiles_m);
+  return hipGetLastError();
 }
 
 }  // namespace rw4

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
     float xv[2] = {x0, x1};
     uint32_t b[2];
     encode<2>(xv, m, b);
-    const uint32_t byte = pack2_bits(b[0], b[1]);
+    const uint32_t byte = pack2_bits_quad(b[0], b[1]);
     const int64_t row = row0 + r;
     q[row * (G * 64) + grp * 64 + lane] = uint8_t(byte);
     if (lane == 0) s[row * G + grp] = m * (1.0f / 7.0f);

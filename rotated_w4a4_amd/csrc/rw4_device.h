@@ -1,7 +1,7 @@
 // Device-side building blocks of the rotated W4A4 kernels (gfx950, wave64).
 //
 // Element sources, cross-lane exchanges for the Walsh-Hadamard butterflies,
-// the round-to-nearest-even INT4 encoder and the nibble packer.
+// the round-to-nearest-even INT4 encoder and the packer of the stored form.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -141,11 +141,11 @@ __device__ __forceinline__ uint32_t rne_code_bits(float v, float inv) {
   return __float_as_uint(fmaf(v, inv, kRoundMagic));
 }
 
-// Pack 8 codes (given as magic-rounded float bit patterns, code e at nibble
-// e) into one dword: Horner sum of the raw patterns, then subtract the
-// magic constant from every nibble while adding 8 (offset binary, no
-// borrows), then flip the nibble sign bits back to two's complement.
-__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8]) {
+// Two's-complement nibbles from 8 magic-rounded float bit patterns (code e
+// at nibble e): Horner sum of the raw patterns, then subtract the magic
+// constant from every nibble while adding 8 (offset binary, no borrows),
+// then flip the nibble sign bits.
+__device__ __forceinline__ uint32_t pack8_twos(const uint32_t b[8]) {
   uint32_t acc = b[7];
 #pragma unroll
   for (int e = 6; e >= 0; --e) acc = (acc << 4) + b[e];
@@ -154,11 +154,33 @@ __device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8]) {
   return (acc + kFix) ^ 0x88888888u;
 }
 
-// Two codes into one byte (low nibble = first).
-__device__ __forceinline__ uint32_t pack2_bits(uint32_t b0, uint32_t b1) {
-  const uint32_t acc = (b1 << 4) + b0;
+// Stored form of 8 codes (one 32-bit word): sign-magnitude nibbles, nibble e
+// = |c_e| in bits 0-2 and the sign of c_{(e-1) mod 8} in bit 3.  From the
+// two's-complement nibbles t: s = the nibble sign bits; |c| per nibble is
+// (t XOR 0xF) + 1 where negative, done for all nibbles at once (|c| <= 7, so
+// nothing carries); the signs then move up one nibble, the top one wrapping
+// to nibble 0.  Zero is stored with sign 0.
+__device__ __forceinline__ uint32_t twos_to_stored(uint32_t t) {
+  const uint32_t s = t & 0x88888888u;
+  const uint32_t one = s >> 3;
+  const uint32_t mag = (t ^ ((one << 4) - one)) + one;
+  return mag | __builtin_amdgcn_alignbit(s, s, 28);  // rotate left by 4
+}
+
+__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8]) { return twos_to_stored(pack8_twos(b)); }
+
+// One byte of the stored form for codes 2l, 2l+1 of a word, held by lane l of
+// a quad (lanes 4w..4w+3 hold word w): the low nibble takes the sign of code
+// 2l-1, i.e. of the high code of the previous lane of the quad (cyclically).
+__device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1) {
   constexpr uint32_t kFix2 = (8u - kRoundMagicBits) * 0x11u;
-  return ((acc + kFix2) ^ 0x88u) & 0xFFu;
+  const uint32_t t = ((((b1 << 4) + b0) + kFix2) ^ 0x88u) & 0xFFu;  // two's complement byte
+  const uint32_t s = t & 0x88u;
+  const uint32_t one = s >> 3;
+  const uint32_t mag = (t ^ ((one << 4) - one)) + one;
+  // lane i of each quad reads lane (i + 3) % 4: quad_perm [3, 0, 1, 2]
+  const uint32_t prev = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x93, 0xF, 0xF, false));
+  return (mag | ((s & 0x08u) << 4) | ((prev >> 4) & 0x08u)) & 0xFFu;
 }
 
 __device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f ? num / m : 0.0f; }

@@ -165,6 +165,8 @@ def test_gemm_validation():
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 0, 4, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 0, FAKE, 0, 4, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, -1, 4, 128, FAKE, 0, 4, None) == SHAPE
+    # K above 2^24 (the per-block buffer ranges) is a shape error
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, (1 << 24) + 128, FAKE, 0, 4, None) == SHAPE
     assert g(None, None, None, None, 0, 4, 128, None, 0, 4, None) == OK
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 5, 4, None) == ARG
     assert g(None, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 0, 4, None) == ARG

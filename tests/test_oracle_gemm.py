@@ -19,16 +19,18 @@ def _brute_acc(qa, qw, g=128):
 
 def test_group_accumulators_match_python_ints():
     rng = np.random.default_rng(20)
-    qa = rng.integers(-8, 8, size=(3, 256)).astype(np.int8)
-    qw = rng.integers(-8, 8, size=(4, 256)).astype(np.int8)
+    qa = rng.integers(-7, 8, size=(3, 256)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(4, 256)).astype(np.int8)
     assert np.array_equal(oracle.group_accumulators(qa, qw), _brute_acc(qa, qw))
 
 
 def test_group_accumulator_bound():
-    qa = np.full((1, 128), -8, dtype=np.int8)
-    qw = np.full((1, 128), -8, dtype=np.int8)
+    qa = np.full((1, 128), -7, dtype=np.int8)
+    qw = np.full((1, 128), -7, dtype=np.int8)
     acc = oracle.group_accumulators(qa, qw)
-    assert acc[0, 0, 0] == 128 * 64 == 8192
+    assert acc[0, 0, 0] == 128 * 49 == 6272
+    qw[0] = 7
+    assert oracle.group_accumulators(qa, qw)[0, 0, 0] == -6272
 
 
 def test_dequant_gemm_matches_brute_force():

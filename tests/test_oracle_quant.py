@@ -22,7 +22,7 @@ def test_group_quant_golden(golden_dir):
     assert codes[0, :10].tolist() == g["expected_codes_group0_first10"]
     assert not codes[0, 10:].any()
     packed = oracle.pack_int4(codes)
-    assert packed[0, :5].tolist() == g["expected_first_bytes"]
+    assert packed[0, :8].tolist() == g["expected_first_bytes"]
     # the whole all-zero second group packs to zero bytes
     assert not packed[0, 64:].any()
     # the same row scaled by a power of two: identical codes, scaled scale
@@ -36,9 +36,8 @@ def test_quant_properties_random():
     x = rng.standard_normal((64, 512)) * rng.uniform(0.01, 100, size=(64, 1))
     x[3, 200] = 5e4  # spike
     codes, scales, ratio = oracle.quantize_groups(x)
-    assert codes.min() >= -8 and codes.max() <= 7
-    # the symmetric scale never reaches -8
-    assert codes.min() >= -7
+    # the symmetric scale keeps codes in [-7, 7]
+    assert codes.min() >= -7 and codes.max() <= 7
     xg = x.reshape(64, 4, 128)
     cg = codes.reshape(64, 4, 128).astype(float)
     # the group maximum maps to +-7
@@ -73,18 +72,54 @@ def test_quant_rounds_half_to_even():
 
 def test_pack_unpack_roundtrip_and_order():
     rng = np.random.default_rng(8)
-    c = rng.integers(-8, 8, size=(5, 256)).astype(np.int8)
+    c = rng.integers(-7, 8, size=(5, 256)).astype(np.int8)
     p = oracle.pack_int4(c)
     assert p.shape == (5, 128) and p.dtype == np.uint8
     assert np.array_equal(oracle.unpack_int4(p), c)
-    # low nibble = even index
-    one = np.zeros((1, 2), dtype=np.int8)
-    one[0] = [-1, 0]
-    assert oracle.pack_int4(one)[0, 0] == 0x0F
-    one[0] = [0, -8]
-    assert oracle.pack_int4(one)[0, 0] == 0x80
+    # magnitude in bits 0-2 of nibble e (low nibble = even e); the sign of
+    # code e in bit 3 of nibble e+1, the last code's sign in nibble 0
+    word = np.zeros((1, 8), dtype=np.int8)
+    word[0, 0] = -1
+    assert oracle.pack_int4(word)[0].tolist() == [0x81, 0, 0, 0]
+    word[0] = [0, -7, 0, 0, 0, 0, 0, 0]
+    assert oracle.pack_int4(word)[0].tolist() == [0x70, 0x08, 0, 0]
+    word[0] = [0, 0, 0, 0, 0, 0, 0, -3]
+    assert oracle.pack_int4(word)[0].tolist() == [0x08, 0, 0, 0x30]
+    word[0] = [7, 0, 0, 0, 0, 0, 0, 0]
+    assert oracle.pack_int4(word)[0].tolist() == [0x07, 0, 0, 0]
+    # words are independent: the sign bit never crosses a 4-byte boundary
+    two = np.zeros((1, 16), dtype=np.int8)
+    two[0, 7] = -2
+    assert oracle.pack_int4(two)[0].tolist() == [0x08, 0, 0, 0x20, 0, 0, 0, 0]
+    # a negative zero (sign bit set, magnitude 0) decodes to 0
+    assert oracle.unpack_int4(np.array([[0x08, 0, 0, 0]], dtype=np.uint8)).tolist() == [[0] * 8]
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.array([[8, 0]]))
+        oracle.pack_int4(np.array([[8, 0, 0, 0, 0, 0, 0, 0]]))
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.array([[-8, 0, 0, 0, 0, 0, 0, 0]]))
+
+
+def test_packed_word_splits_into_sign_magnitude_bytes():
+    """A word w of the packed form gives the even codes as the bytes of
+    w & 0x87878787 and the odd codes as the bytes of rotr(w, 4) & 0x87878787,
+    each byte = sign << 7 | magnitude (brute force over random words)."""
+    rng = np.random.default_rng(9)
+    c = rng.integers(-7, 8, size=(64, 8)).astype(np.int8)
+    p = oracle.pack_int4(c).astype(np.uint32)
+    w = p[:, 0] | (p[:, 1] << 8) | (p[:, 2] << 16) | (p[:, 3] << 24)
+    def decode(u):
+        out = []
+        for k in range(4):
+            b = (int(u) >> (8 * k)) & 0xFF
+            out.append(-(b & 7) if b & 0x80 else (b & 7))
+        return out
+    for row in range(64):
+        wi = int(w[row])
+        even = decode(wi & 0x87878787)
+        rot = ((wi >> 4) | (wi << 28)) & 0xFFFFFFFF
+        odd = decode(rot & 0x87878787)
+        assert even == c[row, 0::2].tolist()
+        assert odd == c[row, 1::2].tolist()
 
 
 def test_rrs_golden(golden_dir):

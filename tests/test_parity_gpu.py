@@ -163,10 +163,12 @@ def test_group_isolation_int32_exact(shape):
     M, K, N = shape
     G = K // 128
     rng = np.random.default_rng(M + N)
-    ca = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
-    cw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
-    ca[0, :128] = -8
-    cw[0, :128] = -8   # the extreme accumulator 8192
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[0, :128] = -7
+    cw[0, :128] = -7   # the extreme accumulator 128 * 49
+    if N > 1:
+        cw[1, :128] = 7  # and its negative
     qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
     qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
     sa = torch.ones((M, G), dtype=torch.float32, device=gu.DEV)
@@ -181,7 +183,9 @@ def test_group_isolation_int32_exact(shape):
         assert np.array_equal(y[rows].astype(np.int64), acc), f"group {g}"
         assert np.array_equal(y[rows], acc.astype(np.float64))
         if g == 0:
-            assert y[0, 0] == 8192.0
+            assert y[0, 0] == 6272.0
+            if N > 1:
+                assert y[0, 1] == -6272.0
 
 
 # ----------------------------------------------------------------------------
