@@ -3,8 +3,8 @@
 
 One step = one pass of the whole online path over one batch: quantize_act
 (load bf16 activations, block Walsh-Hadamard, group-128 absmax, INT4 RNE,
-pack) followed by w4a4_gemm (FP8 MFMA on the exact codes, per-128-group rescale, fp32 epilogue,
-bf16 output).  Weights are transformed and packed once before timing, as in
+pack) followed by w4a4_gemm (FP8 MFMA on the exact codes, per-128-group
+rescale, fp32 epilogue, bf16 output).  Weights are transformed and packed once before timing, as in
 deployment (the offline step).  Default workload: LLaMA-3-8B q_proj prefill,
 X 2048x4096 bf16 with channel outliers and spikes, W 4096x4096.
 
@@ -14,14 +14,16 @@ Inputs are resident in HBM before the timed region.  Independent buffer sets
 cannot serve them.
 
 Prints one JSON line (stdout).  Per-kernel times come from HIP events
-recorded on the stream the library launches on; the GEMM is the dominant
-kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported, the quantize kernel's HBM
-roofline beside it.  The CPU oracle is timed on a bounded sample of the same
+(created without the system-scope fence, so recording them flushes no
+caches) recorded on the stream the library launches on; the GEMM is the
+dominant kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported,
+the quantize kernel's HBM roofline beside it.  The CPU oracle is timed on a bounded sample of the same
 workload as a reported baseline (not a target).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -43,6 +45,53 @@ MALL_FLUSH_BYTES = 512 << 20
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvent:
+    """A timing event of the HIP runtime that torch itself uses, created with
+    hipEventDisableSystemFence: recording it does not write back and invalidate
+    the caches (torch's default events do), so timing events inside the timed
+    region do not slow the kernels they bracket."""
+
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            import torch
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        rc = self._hip().hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        """stream: the hipStream_t handle (torch's current_stream().cuda_stream)."""
+        rc = self._hip().hipEventRecord(self.h, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, end):
+        self._hip().hipEventSynchronize(end.h)
+        f = ctypes.c_float()
+        rc = self._hip().hipEventElapsedTime(ctypes.byref(f), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def __del__(self):
+        if self._lib is not None and self.h:
+            self._lib.hipEventDestroy(self.h)
 
 
 def parse():
@@ -191,31 +240,33 @@ def main():
     torch.cuda.synchronize()
     log(f"{nsets} rotating buffer sets of {set_bytes / 2**20:.1f} MiB")
 
+    stream = torch.cuda.current_stream(dev).cuda_stream  # the stream the kernels run on
+
     def step(i, ev=None):
         s = sets[i % nsets]
         if ev is not None:
-            ev[0].record()
+            ev[0].record(stream)
         rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"])
         if ev is not None:
-            ev[1].record()
+            ev[1].record(stream)
         rw4.w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"])
         if ev is not None:
-            ev[2].record()
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, events on the launch stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_ms = [e[0].elapsed_time(e[1]) for e in events]
-    g_ms = [e[1].elapsed_time(e[2]) for e in events]
+    q_ms = [e[0].elapsed_ms(e[1]) for e in events]
+    g_ms = [e[1].elapsed_ms(e[2]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * M * N * K
     q_us, g_us = 1e3 * float(np.mean(q_ms)), 1e3 * float(np.mean(g_ms))
@@ -228,14 +279,14 @@ def main():
 
     # each kernel alone, launched back to back (no event between launches)
     def back_to_back(fn, reps=20):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(), HipEvent()
         torch.cuda.synchronize()
-        e0.record()
+        e0.record(stream)
         for i in range(reps):
             fn(i)
-        e1.record()
+        e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        return e0.elapsed_ms(e1) * 1e3 / reps
 
     def q_only(i):
         st = sets[i % nsets]

@@ -199,6 +199,25 @@ __device__ __forceinline__ void lds_write_split(uint32_t addr, v4u v) {
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OS) : "memory");
 }
 
+// Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b % 8),
+// each with its own L2.  Renumber so that every XCD gets one contiguous
+// range of logical tiles, and walk the tiles in bands of 8 tile rows,
+// column by column, so the tiles resident on one XCD share A row panels
+// and B column panels.
+__device__ __forceinline__ void tile_of_block(int64_t b, int64_t nb, int64_t tiles_m, int64_t& mt,
+                                              int64_t& nt) {
+  const int64_t x = b & 7, i = b >> 3, q = nb >> 3, r = nb & 7;
+  const int64_t l = x * q + (x < r ? x : r) + i;
+  const int64_t tiles_n = nb / tiles_m;
+  constexpr int64_t kBand = 8;
+  const int64_t band = l / (kBand * tiles_n);
+  const int64_t m_first = band * kBand;
+  const int64_t gm = tiles_m - m_first < kBand ? tiles_m - m_first : kBand;
+  const int64_t li = l - band * kBand * tiles_n;
+  mt = m_first + li % gm;
+  nt = li / gm;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restrict__ qa,
                                                          const float* __restrict__ sa,
@@ -214,7 +233,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t G = K / kGroup;
   const int64_t rowbytes = K / 2;
-  const int64_t m0 = (blockIdx.x % tiles_m) * 128, n0 = (blockIdx.x / tiles_m) * 128;
+  int64_t mt, nt;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, mt, nt);
+  const int64_t m0 = mt * 128, n0 = nt * 128;
 
   // DMA sources: wave w fills rows [32 w, 32 w + 32) of the A and B tiles,
   // 16 rows per instruction; rows are clamped into range (every wave issues

@@ -10,7 +10,8 @@
 // Kernel families:
 //   quant_h128      block-128 Hadamard, group-128 scales.  16 lanes own one
 //                   (row, group); each lane holds 8 consecutive channels:
-//                   3 butterfly stages in registers + 4 across lanes.
+//                   3 butterfly stages in registers + 4 across lanes
+//                   (DPP for lane distances 1, 2, 8; ds_swizzle for 4).
 //   quant_rowh      one wave per row for Hadamard blocks up to the whole row
 //                   (K = 512 * E / 8): lane i holds channels 512c + 8i + e,
 //                   so bits 0-2 and 9+ are register stages and bits 3-8 are
@@ -31,76 +32,66 @@ namespace rw4 {
 // ---------------------------------------------------------------------------
 // quant_h128
 // ---------------------------------------------------------------------------
-// Each wave processes quads of 4 consecutive (row, group) units per step,
-// UNROLL quads per loop iteration, in a grid-stride loop; the loads of the
-// next iteration are issued before the current one is transformed, so every
-// wave keeps 2 * UNROLL KB of input in flight.
-template <class Src, int UNROLL>
-__device__ __forceinline__ void h128_load(const Src& src, int64_t quad0, int64_t n_quads, int64_t n_units,
-                                          int64_t G, int seg, int sub, float (&v)[UNROLL][8]) {
+// A block covers 16 U consecutive groups of one row: wave w of the block
+// takes groups [4 (U w + u), 4 (U w + u) + 4) for u < U, 16 lanes per
+// group, 8 channels per lane (one 16-byte load for bf16).  Blocks run over
+// rows and their group ranges in a flat 1-D grid; the row and range come
+// from the block index (uniform), so the lanes do no index division.
+template <class Src, int U>
+__global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int64_t blocks_per_row,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s,
+                                                         float post_scale) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int seg = lane >> 4;   // which group of the quad
+  const int sub = lane & 15;   // 8-channel slice of the group
+  const int64_t row = int64_t(blockIdx.x) / blocks_per_row;
+  const int64_t g_blk = (int64_t(blockIdx.x) - row * blocks_per_row) * (16 * U);
+
+  float v[U][8];
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u) {
-    const int64_t unit = (quad0 + u) * 4 + seg;
-    if (quad0 + u < n_quads && unit < n_units) {
-      const int64_t row = unit / G, grp = unit - row * G;
+  for (int u = 0; u < U; ++u) {
+    const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
+    if (grp < G) {
       src.load8(row, grp * kGroup + sub * 8, v[u]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
     }
   }
-}
-
-template <class Src, int UNROLL>
-__global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t n_units, int64_t G,
-                                                         uint8_t* __restrict__ q, float* __restrict__ s,
-                                                         float post_scale) {
-  const int lane = threadIdx.x & 63;
-  const int seg = lane >> 4;   // which unit of the quad
-  const int sub = lane & 15;   // 8-channel slice of the group
-  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
-  const int64_t n_quads = (n_units + 3) >> 2;
-  const int64_t stride = n_waves * UNROLL;
-
-  float nxt[UNROLL][8];
-  int64_t quad0 = wave * UNROLL;
-  if (quad0 < n_quads) h128_load<Src, UNROLL>(src, quad0, n_quads, n_units, G, seg, sub, nxt);
-  for (; quad0 < n_quads; quad0 += stride) {
-    float v[UNROLL][8];
+  uint8_t* qrow = q + row * (G * 64);
+  float* srow = s + row * G;
+  // lane stages in the negating form: the values of this lane end up
+  // multiplied by flip = (-1)^popcount(lane & 15), undone in the encoder
+  const float c1 = (lane & 1) ? -1.0f : 1.0f, c2 = (lane & 2) ? -1.0f : 1.0f;
+  const float c4 = (lane & 4) ? -1.0f : 1.0f, c8 = (lane & 8) ? -1.0f : 1.0f;
+  const float flip = (__builtin_popcount(lane & 15) & 1) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
+  for (int u = 0; u < U; ++u) {
+    fwht8(v[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[u][e] = nxt[u][e];
-    if (quad0 + stride < n_quads) h128_load<Src, UNROLL>(src, quad0 + stride, n_quads, n_units, G, seg, sub, nxt);
+    for (int e = 0; e < 8; ++e) {
+      float x = v[u][e];
+      x = butterfly_neg_x<1>(x, c1);
+      x = butterfly_neg_x<2>(x, c2);
+      x = butterfly_neg_x<4>(x, c4);
+      x = butterfly_neg_x<8>(x, c8);
+      v[u][e] = x;
+    }
+    float m = 0.0f;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      fwht8(v[u]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = v[u][e];
-        x = butterfly_x<1>(x, lane);
-        x = butterfly_x<2>(x, lane);
-        x = butterfly_x<4>(x, lane);
-        x = butterfly_x<8>(x, lane);
-        v[u][e] = x;
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
-      m = max_x<1>(m);
-      m = max_x<2>(m);
-      m = max_x<4>(m);
-      m = max_x<8>(m);
-      uint32_t b[8];
-      encode<8>(v[u], m, b);
-      const uint32_t packed = pack8_bits(b);
-      const int64_t unit = (quad0 + u) * 4 + seg;
-      if (quad0 + u < n_quads && unit < n_units) {
-        const int64_t row = unit / G, grp = unit - row * G;
-        reinterpret_cast<uint32_t*>(q + row * (G * 64) + grp * 64)[sub] = packed;
-        if (sub == 0) s[row * G + grp] = m * post_scale;
-      }
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+    m = max_x<1>(m);
+    m = max_x<2>(m);
+    m = max_x<4>(m);
+    m = max_x<8>(m);
+    uint32_t b[8];
+    encode<8>(v[u], m, b, flip);
+    const uint32_t packed = pack8_bits(b);
+    const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
+    if (grp < G) {
+      reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
+      if (sub == 0) srow[grp] = m * post_scale;
     }
   }
 }
@@ -362,14 +353,11 @@ int grid_for_waves(int64_t waves_needed, int64_t cap_blocks) {
 template <class Src>
 hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, float* s, float post,
                        hipStream_t st) {
-  constexpr int UNROLL = 2;
-  const int64_t n_units = rows * G;
-  const int64_t n_quads = (n_units + 3) / 4;
-  // one loop iteration per wave for all but the largest inputs: the
-  // dispatcher keeps every SIMD full and streams new waves as others retire
-  const int grid = grid_for_waves((n_quads + UNROLL - 1) / UNROLL, 65535);
-  hipLaunchKernelGGL((quant_h128_kernel<Src, UNROLL>), dim3(grid), dim3(256), 0, st, src, n_units, G,
-                     q, s, post);
+  // 16 groups per block, one quad of groups per wave: measured faster than
+  // two quads per wave at both the 4096- and the 14336-channel shapes
+  const int64_t bpr = (G + 15) / 16, blocks = rows * bpr;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_h128_kernel<Src, 1>), dim3(blocks), dim3(256), 0, st, src, G, bpr, q, s, post);
   return hipGetLastError();
 }
 

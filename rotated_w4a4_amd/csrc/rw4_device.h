@@ -77,17 +77,22 @@ struct StridedSrc {
 };
 
 // ---------------------------------------------------------------------------
-// Cross-lane exchange: value of lane (lane ^ M).  DPP quad permutes for
-// M = 1, 2; ds_swizzle (bit-mask mode, within 32 lanes) for 4, 8, 16;
-// ds_bpermute for 32.
+// Cross-lane exchange: value of lane (lane ^ M); every DPP source lane
+// exists (bound_ctrl set only lets the compiler fuse the move into the
+// consumer).  DPP quad permutes for
+// M = 1, 2; DPP row rotate by 8 for M = 8 (inside a 16-lane row, lane i and
+// i ^ 8 are 8 apart either way); ds_swizzle (bit-mask mode, within 32
+// lanes) for 4 and 16; ds_bpermute for 32.
 // ---------------------------------------------------------------------------
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
   int x = __float_as_int(v);
   if constexpr (M == 1) {
-    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
   } else if constexpr (M == 2) {
-    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 8) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);  // row_ror:8 (lane ^ 8 in a row of 16)
   } else if constexpr (M < 32) {
     x = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
   } else {
@@ -105,6 +110,17 @@ __device__ __forceinline__ float butterfly_x(float v, int lane) {
   const float o = lane_xor<M>(v);
   const float sgn = (lane & M) ? -1.0f : 1.0f;
   return fmaf(sgn, v, o);
+}
+
+// The same stage in a cheaper form: x + c * partner with c = +1 on the low
+// lane and -1 on the high lane, one fused multiply-add whose multiplicand
+// comes straight from the cross-lane move.  The high lane gets the negated
+// butterfly output; after stages on a set of lane bits, every value is off
+// by (-1)^(number of those bits set in the lane index), which the caller
+// folds into the quantizer (the absolute maximum does not change).
+template <int M>
+__device__ __forceinline__ float butterfly_neg_x(float v, float c) {
+  return fmaf(lane_xor<M>(v), c, v);
 }
 
 // Butterfly stages on the low 3 index bits held in one lane's 8 registers.
@@ -191,14 +207,17 @@ __device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f 
 constexpr float kTinyMax = 0x1p-100f;
 constexpr float kTinyLift = 0x1p64f;
 
+// sign = -1 encodes the negated values (for inputs that carry a known sign
+// flip); rounding to nearest even is symmetric, so the codes are exactly
+// the negated codes.
 template <int N>
-__device__ __forceinline__ void encode(float v[N], float m, uint32_t b[N]) {
+__device__ __forceinline__ void encode(float v[N], float m, uint32_t b[N], float sign = 1.0f) {
   if (m > 0.0f && m < kTinyMax) {
 #pragma unroll
     for (int e = 0; e < N; ++e) v[e] *= kTinyLift;
     m *= kTinyLift;
   }
-  const float inv = safe_inv(m, 7.0f);
+  const float inv = safe_inv(m, 7.0f) * sign;
 #pragma unroll
   for (int e = 0; e < N; ++e) b[e] = rne_code_bits(v[e], inv);
 }
