@@ -26,7 +26,7 @@
 //                      bf16 split of each scale, split once per block and
 //                      group into LDS; the VALU unpacks and accumulates.
 //   gemm_small_kernel  M <= 16 (decode): 16 output channels per block, the
-//                      four waves split the groups, one
+//                      eight waves split the groups, one
 //                      v_mfma_scale_f32_16x16x128_f8f6f4 per group with
 //                      fragments loaded straight from global memory.
 // MFMA result layouts: for 32 x 32, lane l holds
@@ -454,21 +454,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel (decode, M <= 16): one block per 16 output channels; the
-// 4 waves split the groups; lane l supplies row l % 16 and codes
-// [32 (l / 16), 32 (l / 16) + 32) of the group for both operands, so one
-// 16 x 16 x 128 MFMA covers a whole group.  Fragments come straight from
-// global memory (no reuse to stage); the partial results are summed across
-// waves in LDS.
+// Small-M kernel (decode, M <= 16): one block of 8 waves per 16 output
+// channels; the waves split the groups (4 groups in flight per wave, with
+// their scales); lane l supplies row l % 16 and codes [32 (l / 16),
+// 32 (l / 16) + 32) of the group for both operands, so one 16 x 16 x 128
+// MFMA covers a whole group.  Fragments come straight from global memory
+// (no reuse to stage); the partial results are summed across waves in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kSmallWaves = 8;
 template <bool BF16>
-__global__ __launch_bounds__(256) void gemm_small_kernel(const uint8_t* __restrict__ qa,
-                                                         const float* __restrict__ sa,
-                                                         const uint8_t* __restrict__ qw,
-                                                         const float* __restrict__ sw, int64_t M,
-                                                         int64_t N, int64_t K, void* __restrict__ y,
-                                                         int64_t ldy) {
-  constexpr int NB = 8;  // groups in flight per wave
+__global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint8_t* __restrict__ qa,
+                                                                      const float* __restrict__ sa,
+                                                                      const uint8_t* __restrict__ qw,
+                                                                      const float* __restrict__ sw, int64_t M,
+                                                                      int64_t N, int64_t K, void* __restrict__ y,
+                                                                      int64_t ldy) {
+  constexpr int NB = 4;  // groups in flight per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -481,41 +482,45 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint8_t* __restri
   const bool a_ok = am < M, b_ok = bn < N;
 
   float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t gb = wave; gb < G; gb += 4 * NB) {
+  for (int64_t gb = wave; gb < G; gb += kSmallWaves * NB) {
     v4u pa[NB], pb[NB];
+    float swv[NB], sav[NB][4];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
-      const int64_t g = gb + 4 * t;
+      const int64_t g = gb + kSmallWaves * t;
       const bool in = g < G;
       pa[t] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + g * 64 + part * 16)
                            : v4u{0u, 0u, 0u, 0u};
       pb[t] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + g * 64 + part * 16)
                            : v4u{0u, 0u, 0u, 0u};
+      swv[t] = (in && b_ok) ? sw[bn * G + g] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = part * 4 + r;
+        sav[t][r] = (in && m < M) ? sa[m * G + g] : 0.0f;
+      }
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
-      const int64_t g = gb + 4 * t;
+      const int64_t g = gb + kSmallWaves * t;
       if (g >= G) break;
       const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           f8_operand(pa[t]), f8_operand(pb[t]), v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
-      const float swv = b_ok ? sw[bn * G + g] : 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = (lane >> 4) * 4 + r;
-        const float sav = (m < M) ? sa[m * G + g] : 0.0f;
-        yv[r] = fmaf(acc[r], sav * swv, yv[r]);
-      }
+      for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][r] * swv[t], yv[r]);
     }
   }
-  __shared__ float red[4][64][4];
+  __shared__ float red[kSmallWaves][64][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][lane][r] = yv[r];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float v = red[0][lane][r] + red[1][lane][r] + red[2][lane][r] + red[3][lane][r];
-      const int64_t m = (lane >> 4) * 4 + r;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) v += red[w][lane][r];
+      const int64_t m = part * 4 + r;
       if (m < M && b_ok) store_y<BF16>(y, ldy, m, bn, v);
     }
   }
@@ -527,11 +532,11 @@ hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, co
   if (M <= 16) {
     const int64_t blocks = (N + 15) / 16;
     if (y_bf16)
-      hipLaunchKernelGGL((gemm_small_kernel<true>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M,
-                         N, K, y, ldy);
+      hipLaunchKernelGGL((gemm_small_kernel<true>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa, sa,
+                         qw, sw, M, N, K, y, ldy);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<false>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M,
-                         N, K, y, ldy);
+      hipLaunchKernelGGL((gemm_small_kernel<false>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+                         sa, qw, sw, M, N, K, y, ldy);
     return hipGetLastError();
   }
   // per-block buffer ranges: 128 rows of K / 2 bytes, 128 rows of K / 128 scales

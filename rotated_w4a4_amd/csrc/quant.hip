@@ -296,6 +296,8 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
   const int64_t row0 = (blockIdx.x / G) * ROWS;
   const int nrows = int(M - row0 < ROWS ? M - row0 : ROWS);
 
+  const float sc0 = chan_scale[grp * kGroup + 2 * lane];
+  const float sc1 = chan_scale[grp * kGroup + 2 * lane + 1];
   for (int r = 0; r < nrows; ++r) {
     float v[2];
     src.load2(row0 + r, grp * kGroup + 2 * lane, v);
@@ -305,19 +307,30 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
   __syncthreads();
   const uint16_t* idx = lut_idx + grp * L * 64;
   const float2* cs = lut_cs + grp * L * 64;
-  for (int l = 0; l < L; ++l) {
-    const uint16_t pr = idx[l * 64 + lane];
-    const float2 t = cs[l * 64 + lane];
-    const int i = pr & 0xFF, j = pr >> 8;
-    for (int r = 0; r < nrows; ++r) {
-      const float a = buf[r][i], b = buf[r][j];
-      buf[r][i] = fmaf(t.x, a, t.y * b);
-      buf[r][j] = fmaf(t.x, b, -t.y * a);
+  // the table entries of 8 layers are loaded together (one memory latency
+  // per 8 layers instead of one per layer), then applied in order
+  constexpr int LB = 8;
+  for (int l0 = 0; l0 < L; l0 += LB) {
+    uint32_t pr[LB];
+    float2 t[LB];
+#pragma unroll
+    for (int k = 0; k < LB; ++k) {
+      const bool in = l0 + k < L;
+      pr[k] = in ? idx[(l0 + k) * 64 + lane] : 0u;
+      t[k] = in ? cs[(l0 + k) * 64 + lane] : make_float2(1.0f, 0.0f);
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < LB; ++k) {
+      if (l0 + k >= L) break;
+      const int i = pr[k] & 0xFF, j = pr[k] >> 8;
+      for (int r = 0; r < nrows; ++r) {
+        const float a = buf[r][i], b = buf[r][j];
+        buf[r][i] = fmaf(t[k].x, a, t[k].y * b);
+        buf[r][j] = fmaf(t[k].x, b, -t[k].y * a);
+      }
+      __syncthreads();
+    }
   }
-  const float sc0 = chan_scale[grp * kGroup + 2 * lane];
-  const float sc1 = chan_scale[grp * kGroup + 2 * lane + 1];
   for (int r = 0; r < nrows; ++r) {
     const float x0 = buf[r][2 * lane] * sc0;
     const float x1 = buf[r][2 * lane + 1] * sc1;
@@ -395,10 +408,18 @@ hipError_t dispatch_rowh(const Src& src, int64_t K, int64_t rows, int log2b, boo
 template <class Src>
 hipError_t launch_givens(const Src& src, int64_t rows, int64_t G, int L, const uint16_t* idx,
                          const float2* cs, const float* scale, uint8_t* q, float* s, hipStream_t st) {
-  constexpr int ROWS = 4;
-  const int64_t blocks = G * ((rows + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((quant_givens_kernel<Src, ROWS>), dim3(blocks), dim3(64), 0, st, src,
-                     rows, G, L, idx, cs, scale, q, s);
+  // few rows (decode): one row per wave, so the 8-layer dependency chain is
+  // short and more waves run in parallel; many rows: 4 rows per wave
+  if (rows <= 256) {
+    const int64_t blocks = G * rows;
+    hipLaunchKernelGGL((quant_givens_kernel<Src, 1>), dim3(blocks), dim3(64), 0, st, src, rows, G, L, idx,
+                       cs, scale, q, s);
+  } else {
+    constexpr int ROWS = 4;
+    const int64_t blocks = G * ((rows + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((quant_givens_kernel<Src, ROWS>), dim3(blocks), dim3(64), 0, st, src, rows, G, L,
+                       idx, cs, scale, q, s);
+  }
   return hipGetLastError();
 }
 
