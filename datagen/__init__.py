@@ -26,6 +26,13 @@ Workloads (all seeded with numpy's PCG64 ``default_rng``):
 * ``rrs``       Rotated Runtime Smooth: X 8192x4096 with the q_proj outlier
                 recipe; W 4096x11008; full 4096-point Hadamard, runtime
                 group-max smoothing, per-token INT4; bf16 output.
+* ``kv``        INT4 KV cache: K/V rows of 4096 tokens x 8 heads x 128
+                (head dimension = group), the q_proj outlier recipe, a
+                block-128 Hadamard per head; quantize and dequantize only
+                (no weights).
+
+``random_signs(seed, K)`` draws the +-1 diagonal of a randomized Hadamard
+transform from its own stream ``default_rng([seed, 0x5167])``.
 
 The pages measure on trained LLaMA/Qwen weights and WikiText-2/C4 text; the
 synthetic tensors stand in for those, shaped like the projections the pages
@@ -57,6 +64,7 @@ __all__ = [
     "greedy_pair_plan",
     "givens_plan",
     "outlier_activations",
+    "random_signs",
 ]
 
 
@@ -156,6 +164,12 @@ def givens_plan(seed: int, K: int, layers: int = 8, per_layer: int = 64,
     return pairs, theta, beta
 
 
+def random_signs(seed: int, K: int) -> np.ndarray:
+    """K independent signs, +1 or -1 with probability 1/2 (int8)."""
+    rng = np.random.default_rng([seed, 0x5167])
+    return np.where(rng.random(K) < 0.5, -1, 1).astype(np.int8)
+
+
 @dataclass
 class Workload:
     """One seeded synthetic workload.
@@ -178,6 +192,7 @@ class Workload:
     pairs: Optional[np.ndarray] = None
     theta: Optional[np.ndarray] = None
     beta: Optional[np.ndarray] = None
+    signs: Optional[np.ndarray] = None   # randomized Hadamard diagonal (int8 +-1)
     meta: dict = field(default_factory=dict)
 
     def x_storage(self) -> np.ndarray:
@@ -237,17 +252,34 @@ def _rrs(seed: int, **kw) -> Workload:
     return Workload("rrs", M, K, N, x, "bf16", w, ("hadamard", K), "rrs", "bf16")
 
 
+def _kv(seed: int, **kw) -> Workload:
+    rng = np.random.default_rng(seed)
+    M, K = kw.get("M", 4096), kw.get("K", 1024)
+    x = round_to_bf16(outlier_activations(rng, M, K))
+    w = np.zeros((K, 0), dtype=np.float32)
+    return Workload("kv", M, K, 0, x, "bf16", w, ("hadamard", 128), "group128", "bf16")
+
+
 WORKLOADS = {
     "tiny": _tiny,
     "q_proj": _q_proj,
     "decode": _decode,
     "down_proj": _down_proj,
     "rrs": _rrs,
+    "kv": _kv,
 }
 
 
-def make(name: str, seed: int = 0, **overrides) -> Workload:
-    """Build workload ``name`` with ``seed``; overrides (M, K, N, layers) shrink it for tests."""
+def make(name: str, seed: int = 0, signed: bool = False, **overrides) -> Workload:
+    """Build workload ``name`` with ``seed``; overrides (M, K, N, layers) shrink it for tests.
+
+    ``signed`` turns a Hadamard workload into its randomized form (a +-1
+    diagonal from ``random_signs(seed, K)`` before each block)."""
     if name not in WORKLOADS:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
-    return WORKLOADS[name](seed, **overrides)
+    wl = WORKLOADS[name](seed, **overrides)
+    if signed:
+        if wl.transform[0] != "hadamard":
+            raise ValueError("signs apply to Hadamard transforms only")
+        wl.signs = random_signs(seed, wl.K)
+    return wl

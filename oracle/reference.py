@@ -70,7 +70,7 @@ __all__ = [
     "quantize_groups", "quantize_rrs",
     "pack_int4", "unpack_int4",
     "group_accumulators", "dequant_gemm",
-    "round_bf16", "round_output",
+    "round_bf16", "round_output", "dequantize", "round_dequant_output",
     "quantize_act", "pack_weight", "w4a4_gemm", "layer_forward",
 ]
 
@@ -132,15 +132,30 @@ def givens_group_rotation(pairs_g: np.ndarray, theta_g: np.ndarray, g: int = GRO
 
 
 def _rotation_blocks(spec: dict, K: int):
-    """Yield (k0, k1, R_block, d) with d the per-channel scale alpha (ones for Hadamard)."""
+    """Yield (k0, k1, R_block, d) with d the per-channel scale alpha (ones for Hadamard).
+
+    A Hadamard spec may carry "signs" (K values of +-1): the randomized
+    Hadamard transform R = diag(signs) H_b / sqrt(b) per block, the random
+    sign diagonal the QuIP#/QTIP page pairs with the Hadamard matrix
+    (section 6.1 block form; a +-1 diagonal keeps R R^T = I).
+    """
     kind = spec["kind"]
     if kind == "hadamard":
         b = int(spec["block"])
         if K % b:
             raise ValueError("block must divide K")
         R = hadamard_block(b)
+        signs = spec.get("signs")
+        if signs is not None:
+            signs = np.asarray(signs, dtype=np.float64)
+            if signs.shape != (K,) or not np.all(np.abs(signs) == 1.0):
+                raise ValueError("signs must be K values of +1 or -1")
         for k0 in range(0, K, b):
-            yield k0, k0 + b, R, np.ones(b)
+            if signs is None:
+                yield k0, k0 + b, R, np.ones(b)
+            else:
+                # randomized Hadamard: R = diag(signs) H_b / sqrt(b), still orthogonal
+                yield k0, k0 + b, signs[k0:k0 + b, None] * R, np.ones(b)
     elif kind == "givens":
         pairs, theta, beta = spec["pairs"], spec["theta"], spec["beta"]
         for gi in range(K // GROUP):
@@ -361,6 +376,28 @@ def round_output(y: np.ndarray, dtype: str) -> np.ndarray:
         return round_bf16(y)
     if dtype == "f64":
         return y
+    raise ValueError(dtype)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, g: int = GROUP) -> np.ndarray:
+    """x_hat[r, k] = codes[r, k] * scales[r, k // g] (float64), the inverse of
+    the quantizer up to rounding: Q(x) = Delta * round(x / Delta) ([Cplx]
+    section 2.1), in the transformed domain (for RRS the stored scale a_t * s_g
+    already carries the smoothing factor)."""
+    c = np.asarray(codes, dtype=np.float64)
+    s = np.asarray(scales, dtype=np.float64)
+    return c * np.repeat(s, g, axis=1)
+
+
+def round_dequant_output(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Output rounding of the library's dequantize: the code * scale product is
+    rounded to fp32 (it needs up to 27 significant bits), then, for bf16,
+    rounded again to the nearest bf16 (ties to even)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return x32
+    if dtype == "bf16":
+        return round_bf16(x32)
     raise ValueError(dtype)
 
 

@@ -10,7 +10,10 @@ def spec_of(wl):
     """Oracle transform spec for a datagen.Workload."""
     kind = wl.transform[0]
     if kind == "hadamard":
-        return {"kind": "hadamard", "block": int(wl.transform[1])}
+        spec = {"kind": "hadamard", "block": int(wl.transform[1])}
+        if wl.signs is not None:
+            spec["signs"] = wl.signs
+        return spec
     return {"kind": "givens", "pairs": wl.pairs, "theta": wl.theta, "beta": wl.beta}
 
 
