@@ -97,6 +97,17 @@ typedef struct rw4_transform rw4_transform; /* opaque */
  * Allocates nothing on the device.  *out receives the new transform. */
 rw4_status rw4_transform_hadamard(int64_t K, int32_t block, void* stream, rw4_transform** out);
 
+/* Randomized block Hadamard transform R = blockdiag(diag(d) H_b / sqrt(b)),
+ * d a +-1 diagonal (the random sign diagonal the QuIP#/QTIP page pairs with
+ * the Hadamard matrix; R stays orthogonal).  Activations x~ = x R (channel k
+ * negated where d_k = -1, then the block transform); weights W~ = R^T W =
+ * blockdiag(H_b / sqrt(b)) diag(d) W.
+ *   signs_host [K] int8, every entry +1 or -1 (ARG otherwise); copied to a
+ *   device table of K 32-bit words; the upload is synchronous with respect
+ *   to `stream`.  block as for rw4_transform_hadamard. */
+rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t* signs_host,
+                                        void* stream, rw4_transform** out);
+
 /* ParoQuant-style independent rotation: for each 128-channel group g,
  * R_g = G_1 G_2 ... G_L, where layer l rotates up to 64 disjoint channel
  * pairs (i, j), i < j < 128, by angle theta: (xG)_i = c x_i + s x_j,
@@ -141,6 +152,18 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
 rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
                            int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
                            void* stream);
+
+/* dequantize: x_hat[r, k] = code(q[r], k) * s[r, k / 128], the stored codes
+ * times their group scale, in the transformed domain (for RRS the stored
+ * scale already carries the smoothing factor); the complex-domain
+ * quantization page, section 2.1: Q(x) = Delta * round(x / Delta).  Reads
+ * back an INT4 KV cache written by quantize_act.  The product is rounded
+ * to fp32, then (out_dtype BF16) to the nearest bf16, ties to even.
+ *   q [M, K/2] packed codes, s [M, K/128] fp32 scales (as quantize_act
+ *   writes them); out [M, K] row-major with leading dimension ldo >= K
+ *   elements, 16-byte aligned rows.  K % 128 == 0. */
+rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+                          rw4_dtype out_dtype, int64_t ldo, void* stream);
 
 /* w4a4_gemm: Y = sum over groups of sa * sw * (qa . qw^T restricted to the
  * group).  Each group's integer dot products are exact (FP8 matrix cores on

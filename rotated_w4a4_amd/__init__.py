@@ -7,7 +7,7 @@ HIP stream, allocates the outputs with torch and turns a non-OK status into
 kernels; there is no fallback.  Importing fails loudly when the library has
 not been built (``python -m rotated_w4a4_amd._build``).
 
-    t = Transform.hadamard(K, block=128)             # or Transform.givens(...)
+    t = Transform.hadamard(K, block=128)             # or .hadamard(K, 128, signs), Transform.givens(...)
     qw, sw = pack_weight(t, w)                       # w: [K, N] (offline)
     qa, sa = quantize_act(t, x)                      # x: [M, K] bf16 / fp32
     y = w4a4_gemm(qa, sa, qw, sw, torch.bfloat16)    # [M, N]
@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
-    "status_str", "version", "EXPORTED_SYMBOLS",
+    "dequantize", "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librw4.so")
@@ -31,8 +31,9 @@ RW4_F32, RW4_BF16 = 0, 1
 MODES = {"group128": 0, "rrs": 1}
 
 EXPORTED_SYMBOLS = (
-    "rw4_transform_hadamard", "rw4_transform_givens", "rw4_transform_destroy", "rw4_transform_k",
-    "rw4_quantize_act", "rw4_pack_weight", "rw4_w4a4_gemm", "rw4_status_str", "rw4_version",
+    "rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
+    "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
+    "rw4_dequantize", "rw4_w4a4_gemm", "rw4_status_str", "rw4_version",
 )
 
 
@@ -58,6 +59,7 @@ lib.rw4_status_str.restype = ctypes.c_char_p
 lib.rw4_status_str.argtypes = [ctypes.c_int]
 lib.rw4_version.restype = ctypes.c_char_p
 lib.rw4_transform_hadamard.argtypes = [_i64, _i32, _p, ctypes.POINTER(_p)]
+lib.rw4_transform_hadamard_signed.argtypes = [_i64, _i32, _p, _p, ctypes.POINTER(_p)]
 lib.rw4_transform_givens.argtypes = [_i64, _i32, _p, _p, _p, _p, ctypes.POINTER(_p)]
 lib.rw4_transform_destroy.argtypes = [_p]
 lib.rw4_transform_k.argtypes = [_p]
@@ -65,8 +67,10 @@ lib.rw4_transform_k.restype = _i64
 lib.rw4_quantize_act.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
 lib.rw4_pack_weight.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_w4a4_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int, _i64, _p]
-for _name in ("rw4_transform_hadamard", "rw4_transform_givens", "rw4_transform_destroy",
-              "rw4_quantize_act", "rw4_pack_weight", "rw4_w4a4_gemm"):
+lib.rw4_dequantize.argtypes = [_p, _p, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+for _name in ("rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
+              "rw4_transform_destroy", "rw4_quantize_act", "rw4_pack_weight", "rw4_dequantize",
+              "rw4_w4a4_gemm"):
     getattr(lib, _name).restype = ctypes.c_int
 
 
@@ -125,11 +129,20 @@ class Transform:
         return self._h
 
     @classmethod
-    def hadamard(cls, K: int, block: int = 128, stream=None) -> "Transform":
+    def hadamard(cls, K: int, block: int = 128, signs=None, stream=None) -> "Transform":
+        """Block Hadamard; with ``signs`` (K values of +1/-1) the randomized form."""
         h = ctypes.c_void_p()
-        _check(lib.rw4_transform_hadamard(int(K), int(block), stream, ctypes.byref(h)),
-               "rw4_transform_hadamard")
-        return cls(h, int(K), f"hadamard{block}")
+        if signs is None:
+            _check(lib.rw4_transform_hadamard(int(K), int(block), stream, ctypes.byref(h)),
+                   "rw4_transform_hadamard")
+            return cls(h, int(K), f"hadamard{block}")
+        signs = np.ascontiguousarray(signs, dtype=np.int8)
+        if signs.shape != (int(K),):
+            raise ValueError("signs must have K entries")
+        _check(lib.rw4_transform_hadamard_signed(int(K), int(block), signs.ctypes.data, stream,
+                                                 ctypes.byref(h)),
+               "rw4_transform_hadamard_signed")
+        return cls(h, int(K), f"hadamard{block}_signed")
 
     @classmethod
     def givens(cls, K: int, pairs, theta, beta, stream=None) -> "Transform":
@@ -206,6 +219,27 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None):
                                _stream(w.device)),
            "rw4_pack_weight")
     return qw, sw
+
+
+def dequantize(q, s, out_dtype=None, out=None):
+    """x_hat [M, K] = codes * group scale (transformed domain), fp32 or bf16."""
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    M, Kh = q.shape
+    K = Kh * 2
+    if s.shape != (M, K // 128):
+        raise ValueError("scale shape does not match the codes")
+    if not (q.is_contiguous() and s.is_contiguous()):
+        raise ValueError("q and s must be contiguous")
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=q.device)
+    if out.stride(1) != 1:
+        raise ValueError("out must have unit stride along K")
+    _check(lib.rw4_dequantize(_ptr(q), _ptr(s), M, K, _ptr(out), _dtype_code(out), out.stride(0),
+                              _stream(q.device)),
+           "rw4_dequantize")
+    return out
 
 
 def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):

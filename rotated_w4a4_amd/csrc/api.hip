@@ -59,8 +59,41 @@ rw4_status rw4_transform_hadamard(int64_t K, int32_t block, void* stream, rw4_tr
   if (block > 128 && !rw4::rowh_supported(K)) return RW4_ERR_UNSUPPORTED;
   auto* t = new (std::nothrow) rw4_transform();
   if (!t) return RW4_ERR_NOMEM;
-  t->dev = rw4::TransformDev{rw4::TransformKind::Hadamard, K, block, 0, nullptr, nullptr, nullptr, nullptr};
+  t->dev = rw4::TransformDev{rw4::TransformKind::Hadamard, K, block, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (hipGetDevice(&t->device) != hipSuccess) t->device = -1;
+  *out = t;
+  return RW4_OK;
+}
+
+rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t* signs_host,
+                                        void* stream, rw4_transform** out) {
+  if (!out) return RW4_ERR_ARG;
+  *out = nullptr;
+  if (!signs_host) return RW4_ERR_ARG;
+  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (!pow2(block) || block < 128 || block > K || K % block) return RW4_ERR_SHAPE;
+  if (block > 128 && !rw4::rowh_supported(K)) return RW4_ERR_UNSUPPORTED;
+  std::vector<uint32_t> mask(K);
+  for (int64_t k = 0; k < K; ++k) {
+    if (signs_host[k] != 1 && signs_host[k] != -1) return RW4_ERR_ARG;
+    mask[k] = signs_host[k] < 0 ? 0x80000000u : 0u;
+  }
+  auto* t = new (std::nothrow) rw4_transform();
+  if (!t) return RW4_ERR_NOMEM;
+  t->dev = rw4::TransformDev{rw4::TransformKind::Hadamard, K, block, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (hipGetDevice(&t->device) != hipSuccess) {
+    delete t;
+    return RW4_ERR_HIP;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMalloc(&t->dev.sign_mask, K * sizeof(uint32_t));
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(t->dev.sign_mask, mask.data(), K * sizeof(uint32_t), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host table dies on return
+  if (e != hipSuccess) {
+    rw4_transform_destroy(t);
+    return from_hip(e);
+  }
   *out = t;
   return RW4_OK;
 }
@@ -121,7 +154,7 @@ rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_
 
   auto* t = new (std::nothrow) rw4_transform();
   if (!t) return RW4_ERR_NOMEM;
-  t->dev = rw4::TransformDev{rw4::TransformKind::Givens, K, 0, layers, nullptr, nullptr, nullptr, nullptr};
+  t->dev = rw4::TransformDev{rw4::TransformKind::Givens, K, 0, layers, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (hipGetDevice(&t->device) != hipSuccess) {
     delete t;
     return RW4_ERR_HIP;
@@ -147,7 +180,8 @@ rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_
 rw4_status rw4_transform_destroy(rw4_transform* t) {
   if (!t) return RW4_OK;
   hipError_t e = hipSuccess;
-  for (void* p : {(void*)t->dev.lut_idx, (void*)t->dev.lut_cs, (void*)t->dev.alpha, (void*)t->dev.alpha_inv}) {
+  for (void* p : {(void*)t->dev.lut_idx, (void*)t->dev.lut_cs, (void*)t->dev.alpha, (void*)t->dev.alpha_inv,
+                  (void*)t->dev.sign_mask}) {
     if (p) {
       const hipError_t f = hipFree(p);
       if (e == hipSuccess) e = f;
@@ -194,6 +228,19 @@ rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dt
   hipStream_t st = static_cast<hipStream_t>(stream);
   return from_hip(rw4::launch_pack_weight(t->dev, w, w_dtype == RW4_BF16, N, stride_k, stride_n, qw,
                                           sw, st));
+}
+
+rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+                          rw4_dtype out_dtype, int64_t ldo, void* stream) {
+  if (out_dtype != RW4_F32 && out_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (M == 0) return RW4_OK;
+  if (!q || !s || !out) return RW4_ERR_ARG;
+  if (ldo < K) return RW4_ERR_ARG;
+  const int64_t esz = out_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(out) || (ldo * esz) % 16) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_dequantize(q, s, M, K, out, out_dtype == RW4_BF16, ldo, st));
 }
 
 rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,

@@ -437,12 +437,16 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
     const float post = (rrs ? 1.0f : 1.0f / 7.0f) / sqrtf(float(t.block));
     int log2b = 0;
     while ((int64_t(1) << log2b) < t.block) ++log2b;
-    if (t.block == 128 && !rrs) {
-      if (bf16) return launch_h128(RowSrc<true>{x, ldx}, M, G, q, s, post, st);
-      return launch_h128(RowSrc<false>{x, ldx}, M, G, q, s, post, st);
+    auto run = [&](const auto& src) {
+      if (t.block == 128 && !rrs) return launch_h128(src, M, G, q, s, post, st);
+      return dispatch_rowh(src, K, M, log2b, rrs, q, s, smooth, post, st);
+    };
+    if (t.sign_mask) {
+      if (bf16) return run(SignedSrc<RowSrc<true>>{{x, ldx}, t.sign_mask});
+      return run(SignedSrc<RowSrc<false>>{{x, ldx}, t.sign_mask});
     }
-    if (bf16) return dispatch_rowh(RowSrc<true>{x, ldx}, K, M, log2b, rrs, q, s, smooth, post, st);
-    return dispatch_rowh(RowSrc<false>{x, ldx}, K, M, log2b, rrs, q, s, smooth, post, st);
+    if (bf16) return run(RowSrc<true>{x, ldx});
+    return run(RowSrc<false>{x, ldx});
   }
   // Givens
   if (bf16)
@@ -460,13 +464,18 @@ hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, i
     const float post = (1.0f / 7.0f) / sqrtf(float(t.block));
     int log2b = 0;
     while ((int64_t(1) << log2b) < t.block) ++log2b;
-    if (t.block == 128) {
-      if (bf16) return launch_h128(StridedSrc<true>{w, sk, sn}, N, G, q, s, post, st);
-      return launch_h128(StridedSrc<false>{w, sk, sn}, N, G, q, s, post, st);
+    // W_tilde = R^T W with R = diag(signs) H / sqrt(b): H / sqrt(b) applied
+    // to the rows of diag(signs) W, so the same sign flip on channel k
+    auto run = [&](const auto& src) {
+      if (t.block == 128) return launch_h128(src, N, G, q, s, post, st);
+      return dispatch_rowh(src, K, N, log2b, false, q, s, nullptr, post, st);
+    };
+    if (t.sign_mask) {
+      if (bf16) return run(SignedSrc<StridedSrc<true>>{{w, sk, sn}, t.sign_mask});
+      return run(SignedSrc<StridedSrc<false>>{{w, sk, sn}, t.sign_mask});
     }
-    if (bf16)
-      return dispatch_rowh(StridedSrc<true>{w, sk, sn}, K, N, log2b, false, q, s, nullptr, post, st);
-    return dispatch_rowh(StridedSrc<false>{w, sk, sn}, K, N, log2b, false, q, s, nullptr, post, st);
+    if (bf16) return run(StridedSrc<true>{w, sk, sn});
+    return run(StridedSrc<false>{w, sk, sn});
   }
   if (bf16)
     return launch_givens<StridedSrc<true>>(StridedSrc<true>{w, sk, sn}, N, G, t.layers,

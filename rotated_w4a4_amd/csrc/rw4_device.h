@@ -76,6 +76,30 @@ struct StridedSrc {
   }
 };
 
+// Randomized Hadamard: the inner source with the sign of channel k flipped
+// where mask[k] = 0x80000000 (the +-1 diagonal applied before the block
+// transform, to activations and to weight rows alike).  k0 is a multiple
+// of 8 for load8 and of 2 for load2.
+template <class Inner>
+struct SignedSrc {
+  Inner in;
+  const uint32_t* mask;
+  __device__ __forceinline__ void load8(int64_t row, int64_t k0, float v[8]) const {
+    in.load8(row, k0, v);
+    const uint4 a = *reinterpret_cast<const uint4*>(mask + k0);
+    const uint4 b = *reinterpret_cast<const uint4*>(mask + k0 + 4);
+    const uint32_t m[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ m[e]);
+  }
+  __device__ __forceinline__ void load2(int64_t row, int64_t k0, float v[2]) const {
+    in.load2(row, k0, v);
+    const uint2 a = *reinterpret_cast<const uint2*>(mask + k0);
+    v[0] = __uint_as_float(__float_as_uint(v[0]) ^ a.x);
+    v[1] = __uint_as_float(__float_as_uint(v[1]) ^ a.y);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Cross-lane exchange: value of lane (lane ^ M); every DPP source lane
 // exists (bound_ctrl set only lets the compiler fuse the move into the

@@ -20,6 +20,7 @@ struct TransformDev {
   float2* lut_cs;       // [G][layers][64]
   float* alpha;         // [K] exp(beta)
   float* alpha_inv;     // [K] exp(-beta)
+  uint32_t* sign_mask;  // Hadamard with random signs: [K], 0 or 0x80000000 (else null)
 };
 
 bool rowh_supported(int64_t K);
@@ -29,6 +30,9 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
 
 hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
                               int64_t sn, uint8_t* q, float* s, hipStream_t st);
+
+hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+                             bool out_bf16, int64_t ldo, hipStream_t st);
 
 hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                        int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,

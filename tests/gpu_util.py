@@ -19,7 +19,7 @@ def x_to_device(x64: np.ndarray, dtype: str):
 
 def transform_for(wl):
     if wl.transform[0] == "hadamard":
-        return rw4.Transform.hadamard(wl.K, int(wl.transform[1]))
+        return rw4.Transform.hadamard(wl.K, int(wl.transform[1]), signs=wl.signs)
     return rw4.Transform.givens(wl.K, wl.pairs, wl.theta, wl.beta)
 
 

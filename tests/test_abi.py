@@ -172,3 +172,30 @@ def test_gemm_validation():
     assert g(None, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 0, 4, None) == ARG
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 8, 128, FAKE, 0, 4, None) == ARG
     assert g(FAKE, FAKE, FAKE + 8, FAKE, 4, 4, 128, FAKE, 0, 4, None) == ARG
+
+
+def test_signed_hadamard_validation():
+    import numpy as np
+    h = ctypes.c_void_p()
+    f = lib.rw4_transform_hadamard_signed
+    good = np.ones(256, dtype=np.int8)
+    bad = good.copy()
+    bad[7] = 0
+    assert f(256, 128, None, None, ctypes.byref(h)) == ARG
+    assert f(256, 128, good.ctypes.data, None, None) == ARG
+    assert f(256, 128, bad.ctypes.data, None, ctypes.byref(h)) == ARG
+    assert f(100, 128, good.ctypes.data, None, ctypes.byref(h)) == SHAPE
+    assert f(256, 96, good.ctypes.data, None, ctypes.byref(h)) == SHAPE
+
+
+def test_dequantize_validation():
+    d = lib.rw4_dequantize
+    assert d(FAKE, FAKE, 4, 100, FAKE, 0, 100, None) == SHAPE
+    assert d(FAKE, FAKE, -1, 128, FAKE, 0, 128, None) == SHAPE
+    assert d(None, None, 0, 128, None, 0, 128, None) == OK
+    assert d(FAKE, FAKE, 4, 128, FAKE, 7, 128, None) == ARG
+    assert d(None, FAKE, 4, 128, FAKE, 0, 128, None) == ARG
+    assert d(FAKE, FAKE, 4, 128, FAKE, 0, 64, None) == ARG
+    assert d(FAKE, FAKE, 4, 128, FAKE + 4, 0, 128, None) == ARG
+    assert d(FAKE, FAKE, 4, 128, FAKE, 1, 132, None) == ARG   # bf16 rows of 264 bytes: not 16-aligned
+

@@ -1,0 +1,117 @@
+"""GPU parity of the transform / quantizer variants: randomized (signed)
+Hadamard transforms and dequantization (the INT4 KV-cache read-back),
+through the C ABI against the CPU oracle."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import datagen  # noqa: E402
+import oracle  # noqa: E402
+from tests.helpers import compare_codes, rel_fro, spec_of  # noqa: E402
+
+if torch.cuda.is_available():
+    import rotated_w4a4_amd as rw4  # noqa: E402
+    from tests import gpu_util as gu  # noqa: E402
+    from tests import test_parity_gpu as tp  # noqa: E402
+
+
+SIGNED = [
+    # name, M, K, N, block, mode, x dtype
+    ("signed_h128", 300, 384, 200, 128, "group128", "bf16"),
+    ("signed_h128_f32", 45, 1024, 64, 128, "group128", "f32"),
+    ("signed_h512", 70, 1024, 96, 512, "group128", "bf16"),
+    ("signed_h4096_rrs", 33, 4096, 80, 4096, "rrs", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SIGNED, ids=[c[0] for c in SIGNED])
+def test_signed_hadamard(case):
+    name, M, K, N, b, mode, xdt = case
+    rng = np.random.default_rng(abs(hash(name)) % 2 ** 31)
+    x = datagen.outlier_activations(rng, M, K)
+    x = datagen.round_to_bf16(x) if xdt == "bf16" else x.astype(np.float32).astype(np.float64)
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    wl = datagen.Workload(name, M, K, N, x, xdt, w, ("hadamard", b), mode, "f32",
+                          signs=datagen.random_signs(11, K))
+    t, xd, qa, sa, aref = tp._quant_parity(wl)
+    qw, sw, wref = tp._weight_parity(wl, t)
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+def test_signs_change_codes_and_match_plain_when_all_positive():
+    K, M = 256, 16
+    rng = np.random.default_rng(12)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(gu.DEV)
+    plain = rw4.Transform.hadamard(K, 128)
+    ones = rw4.Transform.hadamard(K, 128, signs=np.ones(K, dtype=np.int8))
+    signed = rw4.Transform.hadamard(K, 128, signs=datagen.random_signs(1, K))
+    q0, s0 = rw4.quantize_act(plain, x)
+    q1, s1 = rw4.quantize_act(ones, x)
+    q2, _ = rw4.quantize_act(signed, x)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1) and torch.equal(s0, s1)
+    assert not torch.equal(q0, q2)
+
+
+@pytest.mark.parametrize("shape", [(1, 128), (37, 384), (300, 1024)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_dequantize_exact(shape, out):
+    """dequantize of random stored codes and scales equals the oracle's product,
+    rounded once to fp32 (then to bf16), bit for bit."""
+    M, K = shape
+    rng = np.random.default_rng(M * 7 + K)
+    codes = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    scales = rng.uniform(1e-3, 10.0, size=(M, K // 128)).astype(np.float32)
+    scales[0, 0] = 0.0
+    q = torch.from_numpy(oracle.pack_int4(codes)).to(gu.DEV)
+    s = torch.from_numpy(scales).to(gu.DEV)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = gu.to_np(rw4.dequantize(q, s, dt))
+    ref = oracle.round_dequant_output(oracle.dequantize(codes, scales), out)
+    assert np.array_equal(y, ref)
+
+
+def test_dequantize_strided_output():
+    M, K = 20, 256
+    rng = np.random.default_rng(3)
+    codes = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    scales = rng.uniform(0.1, 1.0, size=(M, 2)).astype(np.float32)
+    q = torch.from_numpy(oracle.pack_int4(codes)).to(gu.DEV)
+    s = torch.from_numpy(scales).to(gu.DEV)
+    big = torch.full((M, K + 64), 7.0, dtype=torch.float32, device=gu.DEV)
+    rw4.dequantize(q, s, out=big[:, :K])
+    y = gu.to_np(big)
+    assert np.array_equal(y[:, :K], oracle.round_dequant_output(oracle.dequantize(codes, scales), "f32"))
+    assert np.all(y[:, K:] == 7.0)   # the padding beyond K is untouched
+
+
+def test_kv_cache_roundtrip_full_size():
+    """The INT4 KV-cache workload at its full size (4096 tokens x 8 heads x 128):
+    quantize (block-128 Hadamard per head, group-128 INT4) and dequantize."""
+    wl = datagen.make("kv")
+    t, xd, qa, sa, aref = tp._quant_parity(wl)
+    y = gu.to_np(rw4.dequantize(qa, sa, torch.bfloat16))
+    # exact given the GPU's own codes and scales
+    ref = oracle.round_dequant_output(oracle.dequantize(tp._unpack(qa), gu.to_np(sa)), "bf16")
+    assert np.array_equal(y, ref)
+    # and close to the transformed activations: RTN error within half a step
+    xt = oracle.transform_act(wl.x, spec_of(wl))
+    step = np.repeat(aref["sa"], 128, axis=1)
+    assert np.all(np.abs(y - xt) <= step / 2 * (1 + 1e-2) + np.abs(xt) * 2 ** -8)
+    print(f"kv: rel-Frobenius reconstruction error {rel_fro(y, xt):.3e}", flush=True)
+
+
+def test_signed_weight_layouts_agree():
+    rng = np.random.default_rng(8)
+    K, N = 1024, 72
+    w = torch.from_numpy(rng.normal(0, 0.02, size=(K, N)).astype(np.float32)).to(gu.DEV)
+    sg = datagen.random_signs(4, K)
+    for b in (128, 1024):
+        t = rw4.Transform.hadamard(K, b, signs=sg)
+        qw1, sw1 = rw4.pack_weight(t, w, "kn")
+        qw2, sw2 = rw4.pack_weight(t, w.t().contiguous(), "nk")
+        torch.cuda.synchronize()
+        assert torch.equal(qw1, qw2) and torch.equal(sw1, sw2)
