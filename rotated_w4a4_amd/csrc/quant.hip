@@ -8,10 +8,13 @@
 // pack the weights offline.
 //
 // Kernel families:
-//   quant_h128      block-128 Hadamard, group-128 scales.  16 lanes own one
-//                   (row, group); each lane holds 8 consecutive channels:
-//                   3 butterfly stages in registers + 4 across lanes
-//                   (DPP for lane distances 1, 2, 8; ds_swizzle for 4).
+//   quant_h128_act  block-128 Hadamard, group-128 scales, row-major
+//                   activations: 16 lanes own one (row, group), each lane
+//                   8 consecutive channels; 3 butterfly stages in registers
+//                   + 4 across lanes as DPP-fused multiply-adds; persistent
+//                   waves that prefetch their next row.
+//   quant_h128      the same transform for the offline weight pack (any
+//                   strides; lane distance 4 through ds_swizzle).
 //   quant_rowh      one wave per row for Hadamard blocks up to the whole row
 //                   (K = 512 * E / 8): lane i holds channels 512c + 8i + e,
 //                   so bits 0-2 and 9+ are register stages and bits 3-8 are
@@ -28,6 +31,8 @@
 #include "rw4_internal.h"
 
 namespace rw4 {
+
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // quant_h128
@@ -92,6 +97,193 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     if (grp < G) {
       reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
       if (sub == 0) srow[grp] = m * post_scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quant_h128_act: the activation form of quant_h128 (row-major X) as a
+// persistent loop.  Wave w keeps one quad of groups (quad w % Q of Q per
+// row) and walks the rows w / Q, w / Q + R, ...; the load of the next row
+// is issued before the current one is transformed (D rows ahead), so the
+// memory system has work queued while the wave computes.  Every pass issues
+// the same memory operations (rows past the end use empty buffer ranges),
+// which keeps the compiler's counted waits exact across the loop.
+//
+// The four lane stages run along lane masks 1, 2, 7 and 8, each one DPP
+// move (quad_perm, row_half_mirror, row_ror:8) fused into a v_fmac_f32:
+// x += c_k * x[lane ^ m_k] with c_k = (-1)^parity(lane & t_k) for the dual
+// functionals t = (5, 6, 4, 8) (parity(m_j & t_k) = [j == k]).  The product
+// of these stages is the Walsh-Hadamard transform of the 16-lane index up
+// to a signed permutation: lane l ends with (-1)^popcount(l) times the
+// outputs of Sylvester lane f(l), where f is GF(2)-linear with f(1) = 5,
+// f(2) = 6, f(4) = 7, f(8) = 8.  The sign is undone in the encoder (the
+// absolute maximum is unchanged) and the packed word is stored at word f(l)
+// of the group.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int h128_lane_word(int l) {
+  return ((l & 1) ? 5 : 0) ^ ((l & 2) ? 6 : 0) ^ ((l & 4) ? 7 : 0) ^ (l & 8);
+}
+__device__ __forceinline__ float parity_sign(int x) { return (__builtin_popcount(x) & 1) ? -1.0f : 1.0f; }
+
+// The four lane stages on 8 values (asm: the compiler does not fuse the DPP
+// move into the multiply-add).  Each DPP read follows the write of its
+// register by at least 2 wait states: s_nop 1 at entry, then 8 independent
+// instructions between the stages of one value.
+__device__ __forceinline__ void lane_stages_dpp(float (&v)[8], float c1, float c2, float c7, float c8) {
+#define RW4_STAGE(CTRL, C)                                            \
+  "v_fmac_f32_dpp %0, %0, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %1, %1, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %2, %2, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %3, %3, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %4, %4, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %5, %5, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %6, %6, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %7, %7, " C " " CTRL " row_mask:0xf bank_mask:0xf\n"
+  asm volatile("s_nop 1\n"
+               RW4_STAGE("quad_perm:[1,0,3,2]", "%8")
+               RW4_STAGE("quad_perm:[2,3,0,1]", "%9")
+               RW4_STAGE("row_half_mirror", "%10")
+               RW4_STAGE("row_ror:8", "%11")
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7])
+               : "v"(c1), "v"(c2), "v"(c7), "v"(c8));
+#undef RW4_STAGE
+}
+// Maximum over the 16 lanes of a DPP row (lane masks 1, 2, 7, 8 span them).
+__device__ __forceinline__ float row16_max_dpp(float m) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      : "+v"(m));
+  return m;
+}
+
+// Buffer resource over [base, base + bytes), bytes < 2^31 (checked on the
+// host); raw access: a lane whose offset lies outside reads zeros and its
+// store is dropped, and a resource of 0 bytes touches no memory at all.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <bool BF16>
+struct RawRow {
+  v4u32 w[BF16 ? 1 : 2];
+};
+
+template <bool BF16, bool SIGNED, int D>
+__global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restrict__ x, int64_t ldx,
+                                                             int64_t rows, int64_t G, int64_t Q, int64_t R,
+                                                             const uint32_t* __restrict__ sign_mask,
+                                                             uint8_t* __restrict__ q, float* __restrict__ s,
+                                                             float post_scale) {
+  constexpr int ES = BF16 ? 2 : 4;  // bytes per input element
+  const int lane = threadIdx.x & 63;
+  // wave index, Q and R below 2^31 (checked on the host): 32-bit division
+  const uint32_t w = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (w >= uint32_t(Q * R)) return;
+  const int64_t quad = w % uint32_t(Q), r0 = w / uint32_t(Q);
+  const int sub = lane & 15;
+  const int64_t grp = quad * 4 + (lane >> 4);
+  const int64_t K = G * kGroup;
+  // byte offsets inside one row; lanes of groups past the end fall outside
+  // the row's buffer range (their loads read zeros, their stores vanish)
+  const uint32_t x_off = uint32_t((grp * kGroup + sub * 8) * ES);
+  const uint32_t q_off = uint32_t(grp * 64 + h128_lane_word(sub) * 4);
+  const uint32_t s_off = sub == 0 ? uint32_t(grp * 4) : kOutOfRange;
+
+  uint32_t smask[8];
+  if constexpr (SIGNED) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) smask[e] = grp < G ? sign_mask[grp * kGroup + sub * 8 + e] : 0u;
+  }
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  const float flip = parity_sign(lane & 15);
+
+  // rows at or past the end get an empty range: the prefetch past the last
+  // row is issued like any other (so every path has the same memory
+  // operations in flight) but reads nothing
+  auto load = [&](int64_t row) {
+    RawRow<BF16> raw;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + row * ldx * ES,
+                                              row < rows ? K * ES : 0);
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 1 : 2); ++i)
+      raw.w[i] = __builtin_amdgcn_raw_buffer_load_b128(r, int(x_off + 16 * i), 0, 0);
+    return raw;
+  };
+
+  // issue order fixed (slot 0 first) and kept in the loop below, so the
+  // counted wait before each slot's use leaves the later loads in flight
+  RawRow<BF16> raw[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    raw[d] = load(r0 + d * R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  for (int64_t row0 = r0; row0 < rows; row0 += D * R) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // a row past the end (the last pass of a wave whose row count is not
+      // a multiple of D) is computed on zeros and stored into empty ranges
+      const int64_t row = row0 + d * R;
+      const bool live = row < rows;
+      float v[8];
+      if constexpr (BF16) {
+        const v4u32 u = raw[d].w[0];
+        v[0] = bf16_lo(u[0]); v[1] = bf16_hi(u[0]);
+        v[2] = bf16_lo(u[1]); v[3] = bf16_hi(u[1]);
+        v[4] = bf16_lo(u[2]); v[5] = bf16_hi(u[2]);
+        v[6] = bf16_lo(u[3]); v[7] = bf16_hi(u[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(raw[d].w[e >> 2][e & 3]);
+      }
+      if constexpr (SIGNED) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ smask[e]);
+      }
+      raw[d] = load(row + D * R);
+      fwht8(v);
+      lane_stages_dpp(v, c1, c2, c7, c8);
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+      m = row16_max_dpp(m);
+      // groups whose maximum is below 2^-100 are lifted by 2^64 (exact) so
+      // that 7 / m stays finite; rare, so the whole wave branches around it
+      float mm = m;
+      if (__builtin_amdgcn_ballot_w64(m > 0.0f && m < kTinyMax) != 0) {
+        if (m > 0.0f && m < kTinyMax) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
+          mm = m * kTinyLift;
+        }
+      }
+      // 7 / m as the hardware reciprocal of m / 7: a few ulp from the rounded
+      // quotient, which moves v * 7 / m by ~1e-6 of a code step at most.
+      // (The reciprocal flushes subnormal results, so it is taken of m / 7,
+      // whose reciprocal is normal for every finite m >= 2^-100; 1 / m is
+      // not, for m above 2^126.)
+      const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 7.0f)) : 0.0f;
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
+      const uint32_t packed = pack8_bits(b);
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, live ? G * 4 : 0);
+      __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * post_scale), rs, int(s_off), 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -363,6 +555,33 @@ int grid_for_waves(int64_t waves_needed, int64_t cap_blocks) {
   return int(blocks);
 }
 
+// Row-major activations.  One row per wave while all (row, quad) items fit
+// in one generation of resident waves (32 per CU), else about three rows per
+// wave: measured best at 2048 x 4096 and 4096 x 14336 (more rows per wave
+// leave the memory system less work in flight, fewer cost more setup; a
+// deeper prefetch only added work at the end of each wave).
+hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t* sign_mask, int64_t rows,
+                           int64_t G, uint8_t* q, float* s, float post, hipStream_t st) {
+  constexpr int D = 1;
+  constexpr int64_t kResidentWaves = 256 * 32;
+  constexpr int64_t kRowsPerWave = 3;
+  const int64_t Q = (G + 3) / 4;
+  int64_t R = Q * rows <= kResidentWaves ? rows : (rows + kRowsPerWave - 1) / kRowsPerWave;
+  if (R < 1) R = 1;
+  const int64_t blocks = (Q * R + 3) / 4;
+  if (Q * R > 0x7FFFFFFF - 3 || G * 64 * (bf16 ? 4 : 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+#define RW4_H128_ACT(B, S)                                                                              \
+  hipLaunchKernelGGL((quant_h128_act_kernel<B, S, D>), dim3(blocks), dim3(256), 0, st, x, ldx, rows, G, Q, R, \
+                     sign_mask, q, s, post)
+  if (bf16) {
+    if (sign_mask) RW4_H128_ACT(true, true); else RW4_H128_ACT(true, false);
+  } else {
+    if (sign_mask) RW4_H128_ACT(false, true); else RW4_H128_ACT(false, false);
+  }
+#undef RW4_H128_ACT
+  return hipGetLastError();
+}
+
 template <class Src>
 hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, float* s, float post,
                        hipStream_t st) {
@@ -437,10 +656,8 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
     const float post = (rrs ? 1.0f : 1.0f / 7.0f) / sqrtf(float(t.block));
     int log2b = 0;
     while ((int64_t(1) << log2b) < t.block) ++log2b;
-    auto run = [&](const auto& src) {
-      if (t.block == 128 && !rrs) return launch_h128(src, M, G, q, s, post, st);
-      return dispatch_rowh(src, K, M, log2b, rrs, q, s, smooth, post, st);
-    };
+    if (t.block == 128 && !rrs) return launch_h128_act(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+    auto run = [&](const auto& src) { return dispatch_rowh(src, K, M, log2b, rrs, q, s, smooth, post, st); };
     if (t.sign_mask) {
       if (bf16) return run(SignedSrc<RowSrc<true>>{{x, ldx}, t.sign_mask});
       return run(SignedSrc<RowSrc<false>>{{x, ldx}, t.sign_mask});
