@@ -464,6 +464,236 @@ __global__ __launch_bounds__(256) void rrs_colmax_kernel(Src src, int64_t M, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rotated Runtime Smooth with the Hadamard block equal to the whole row,
+// K = 512 NC (NC >= 4 chunks of 8 channels per lane).  Lane l, chunk c,
+// register e hold channel 512 c + 8 l + e after the load.  Stages:
+//   bits 0-2      in registers (fwht8),
+//   bits 9..      in registers, across chunks,
+//   bits 3-6      lane bits 0-3 by the fused DPP stages of quant_h128_act,
+//   bits 7, 8     lane bits 4, 5: v_permlane16_swap / v_permlane32_swap
+//                 trade them for chunk bits 0, 1 (a 2 x 2 transpose of a
+//                 register pair and a lane bit), then an in-register
+//                 butterfly.
+// Afterwards lane bits 0-3 hold f(l) (bits 3-6, see h128_lane_word), lane
+// bits 4, 5 hold bits 9, 10, chunk bits 0, 1 hold bits 7, 8 and chunk bits
+// 2.. hold bits 11..; the values of lane l carry the sign (-1)^popcount(l &
+// 15).  A 128-channel group (bits 7.. fixed) is one chunk of one 16-lane
+// DPP row.
+// ---------------------------------------------------------------------------
+template <int NC>
+__device__ __forceinline__ int64_t rrs_word(int l, int c) {  // index of the 8-channel word
+  return h128_lane_word(l & 15) | ((c & 3) << 4) | (((l >> 4) & 3) << 6) | (int64_t(c >> 2) << 8);
+}
+__device__ __forceinline__ int rrs_group(int l, int c) {  // 128-channel group
+  return (c & 3) | (((l >> 4) & 3) << 2) | ((c >> 2) << 4);
+}
+
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+template <int NC>
+__device__ __forceinline__ void fwht_row_full(float (&v)[NC][8], float c1, float c2, float c7, float c8) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) fwht8(v[c]);
+#pragma unroll
+  for (int hc = 1; hc < NC; hc <<= 1) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c & hc) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = v[c][e], b = v[c | hc][e];
+        v[c][e] = a + b;
+        v[c | hc][e] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) lane_stages_dpp(v[c], c1, c2, c7, c8);
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      swap16(v[c][e], v[c + 1][e]);
+      const float a = v[c][e], b = v[c + 1][e];
+      v[c][e] = a + b;
+      v[c + 1][e] = a - b;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c & 2) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      swap32(v[c][e], v[c + 2][e]);
+      const float a = v[c][e], b = v[c + 2][e];
+      v[c][e] = a + b;
+      v[c + 2][e] = a - b;
+    }
+  }
+}
+
+template <int NC, bool BF16>
+struct RawFullRow {
+  v4u32 w[NC * (BF16 ? 1 : 2)];
+};
+template <int NC, bool BF16>
+__device__ __forceinline__ RawFullRow<NC, BF16> load_full_row(const void* x, int64_t ldx, int64_t rows,
+                                                              int64_t row, int lane) {
+  constexpr int ES = BF16 ? 2 : 4;
+  RawFullRow<NC, BF16> raw;
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + row * ldx * ES,
+                                            row < rows ? int64_t(NC) * 512 * ES : 0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 1 : 2); ++i)
+      raw.w[c * (BF16 ? 1 : 2) + i] =
+          __builtin_amdgcn_raw_buffer_load_b128(r, (512 * c + 8 * lane) * ES + 16 * i, 0, 0);
+  return raw;
+}
+template <int NC, bool BF16>
+__device__ __forceinline__ void unpack_full_row(const RawFullRow<NC, BF16>& raw, float (&v)[NC][8]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if constexpr (BF16) {
+      const v4u32 u = raw.w[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[c][2 * i] = bf16_lo(u[i]);
+        v[c][2 * i + 1] = bf16_hi(u[i]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = __uint_as_float(raw.w[2 * c + (e >> 2)][e & 3]);
+    }
+  }
+}
+
+// First pass: per 128-channel group, the maximum of |H x| over all rows.
+// smooth[] is zero on entry; waves reduce in registers, then per block in
+// LDS, then one atomic maximum per group and block.
+template <int NC, bool BF16>
+__global__ __launch_bounds__(256) void rrs_colmax_full_kernel(const void* __restrict__ x, int64_t ldx,
+                                                              int64_t rows, float* __restrict__ smooth) {
+  constexpr int G = 4 * NC;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  // wave-uniform (the buffer descriptors built from it must be scalar)
+  const int64_t w = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int64_t W = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  float gmax[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) gmax[c] = 0.0f;
+  RawFullRow<NC, BF16> raw = load_full_row<NC, BF16>(x, ldx, rows, w, lane);
+  for (int64_t row = w; row < rows; row += W) {
+    float v[NC][8];
+    unpack_full_row<NC, BF16>(raw, v);
+    raw = load_full_row<NC, BF16>(x, ldx, rows, row + W, lane);
+    fwht_row_full<NC>(v, c1, c2, c7, c8);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gmax[c] = fmaxf(gmax[c], fabsf(v[c][e]));
+  }
+  __shared__ float red[4][G];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float m = row16_max_dpp(gmax[c]);
+    if ((lane & 15) == 0) red[wv][rrs_group(lane, c)] = m;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const float m = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+    if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(smooth) + g, __float_as_uint(m));
+  }
+}
+
+// Second pass: z = (H x) / s_g (as a multiplication by 1 / s_g), per-token
+// scale a_t = max |z| / 7, codes rne(z / a_t), stored scale a_t * s_g
+// (times post_scale).
+template <int NC, bool BF16>
+__global__ __launch_bounds__(256) void quant_rrs_full_kernel(const void* __restrict__ x, int64_t ldx,
+                                                             int64_t rows, const float* __restrict__ smooth,
+                                                             uint8_t* __restrict__ q, float* __restrict__ s,
+                                                             float post_scale) {
+  constexpr int G = 4 * NC;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (the buffer descriptors built from it must be scalar)
+  const int64_t w = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int64_t W = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  const float flip = parity_sign(lane & 15);
+  float inv_s[NC], sg[NC];
+  uint32_t q_off[NC], s_off[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int g = rrs_group(lane, c);
+    sg[c] = smooth[g];
+    inv_s[c] = safe_inv(sg[c], 1.0f);
+    q_off[c] = uint32_t(rrs_word<NC>(lane, c) * 4);
+    s_off[c] = (lane & 15) == 0 ? uint32_t(g * 4) : kOutOfRange;
+  }
+  RawFullRow<NC, BF16> raw = load_full_row<NC, BF16>(x, ldx, rows, w, lane);
+  for (int64_t row = w; row < rows; row += W) {
+    float v[NC][8];
+    unpack_full_row<NC, BF16>(raw, v);
+    raw = load_full_row<NC, BF16>(x, ldx, rows, row + W, lane);
+    fwht_row_full<NC>(v, c1, c2, c7, c8);
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[c][e] *= inv_s[c];
+        m = fmaxf(m, fabsf(v[c][e]));
+      }
+    m = row16_max_dpp(m);
+    {
+      float t = m;
+      swap16(m, t);
+      m = fmaxf(m, t);
+      t = m;
+      swap32(m, t);
+      m = fmaxf(m, t);
+    }
+    // rows whose maximum |z| is below 2^-100 are lifted by 2^64 (exact) so
+    // that 7 / m stays finite (m is uniform over the wave)
+    float mm = m;
+    if (__builtin_amdgcn_ballot_w64(m > 0.0f && m < kTinyMax) != 0) {
+      mm = m * kTinyLift;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] *= kTinyLift;
+    }
+    const float k = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 7.0f)) : 0.0f;
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), G * 64);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, G * 4);
+    const float a_t = m * (1.0f / 7.0f);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[c][e], k);
+      __builtin_amdgcn_raw_buffer_store_b32(pack8_bits(b), rq, int(q_off[c]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a_t * (sg[c] * post_scale)), rs, int(s_off[c]), 0, 0);
+    }
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float value) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = value;
@@ -582,6 +812,27 @@ hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t
   return hipGetLastError();
 }
 
+// Rotated Runtime Smooth over whole rows of K = 512 NC channels.
+template <int NC>
+hipError_t launch_rrs_full(const void* x, bool bf16, int64_t ldx, int64_t rows, uint8_t* q, float* s,
+                           float* smooth, float post, hipStream_t st) {
+  constexpr int64_t G = 4 * NC;
+  constexpr int64_t kWaves = 256 * 12;
+  const int64_t waves = rows < kWaves ? rows : kWaves;
+  const int grid = int((waves + 3) / 4 > 0 ? (waves + 3) / 4 : 1);
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, smooth, G, 0.0f);
+  if (bf16) {
+    hipLaunchKernelGGL((rrs_colmax_full_kernel<NC, true>), dim3(grid), dim3(256), 0, st, x, ldx, rows, smooth);
+    hipLaunchKernelGGL((quant_rrs_full_kernel<NC, true>), dim3(grid), dim3(256), 0, st, x, ldx, rows,
+                       (const float*)smooth, q, s, post);
+  } else {
+    hipLaunchKernelGGL((rrs_colmax_full_kernel<NC, false>), dim3(grid), dim3(256), 0, st, x, ldx, rows, smooth);
+    hipLaunchKernelGGL((quant_rrs_full_kernel<NC, false>), dim3(grid), dim3(256), 0, st, x, ldx, rows,
+                       (const float*)smooth, q, s, post);
+  }
+  return hipGetLastError();
+}
+
 template <class Src>
 hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, float* s, float post,
                        hipStream_t st) {
@@ -657,6 +908,11 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
     int log2b = 0;
     while ((int64_t(1) << log2b) < t.block) ++log2b;
     if (t.block == 128 && !rrs) return launch_h128_act(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+    if (rrs && t.block == K && !t.sign_mask) {
+      if (K == 2048) return launch_rrs_full<4>(x, bf16, ldx, M, q, s, smooth, post, st);
+      if (K == 4096) return launch_rrs_full<8>(x, bf16, ldx, M, q, s, smooth, post, st);
+      if (K == 8192) return launch_rrs_full<16>(x, bf16, ldx, M, q, s, smooth, post, st);
+    }
     auto run = [&](const auto& src) { return dispatch_rowh(src, K, M, log2b, rrs, q, s, smooth, post, st); };
     if (t.sign_mask) {
       if (bf16) return run(SignedSrc<RowSrc<true>>{{x, ldx}, t.sign_mask});

@@ -201,6 +201,9 @@ RAGGED = [
     ("h1024_rrs", 97, 1024, 144, ("hadamard", 1024), "rrs", "bf16"),
     ("h128_rrs", 50, 512, 16, ("hadamard", 128), "rrs", "f32"),
     ("h8192_rrs", 20, 8192, 32, ("hadamard", 8192), "rrs", "bf16"),
+    ("h2048_rrs_f32", 37, 2048, 40, ("hadamard", 2048), "rrs", "f32"),
+    ("h4096_rrs_ragged", 130, 4096, 24, ("hadamard", 4096), "rrs", "bf16"),
+    ("h4096_rrs_f32", 9, 4096, 16, ("hadamard", 4096), "rrs", "f32"),
     ("givens_prefill", 70, 512, 96, ("givens", 3), "group128", "bf16"),
     ("givens_f32", 5, 256, 17, ("givens", 8), "group128", "f32"),
 ]
