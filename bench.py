@@ -111,7 +111,9 @@ def parse():
 KERNEL_SOURCES = {
     "gemm_f8_kernel": ["gemm.hip", "rw4_device.h"],
     "gemm_small_kernel": ["gemm.hip", "rw4_device.h"],
+    "quant_h128_act_kernel": ["quant.hip", "rw4_device.h"],
     "quant_h128_kernel": ["quant.hip", "rw4_device.h"],
+    "quant_rrs_full_kernel": ["quant.hip", "rw4_device.h"],
     "quant_rowh_kernel": ["quant.hip", "rw4_device.h"],
     "quant_givens_kernel": ["quant.hip", "rw4_device.h"],
 }
@@ -314,8 +316,14 @@ def main():
                 "kernel": gemm_kernel, "ops_per_launch": ops, "avg_launch_us": g_us,
                 "algorithmic_bytes_per_launch": gbytes,
                 "note": "ops = 2 M N K (2 per MAC of INT4 codes, computed exactly on the FP8 MFMA) against the dense FP8/int8 MFMA peak; traffic in bytes"}
-    quant_kernel = {"hadamard": "quant_h128_kernel" if wl.transform[1] == 128 and wl.mode == "group128"
-                    else "quant_rowh_kernel", "givens": "quant_givens_kernel"}[wl.transform[0]]
+    if wl.transform[0] == "givens":
+        quant_kernel = "quant_givens_kernel"
+    elif wl.transform[1] == 128 and wl.mode == "group128":
+        quant_kernel = "quant_h128_act_kernel"
+    elif wl.mode == "rrs" and wl.transform[1] == K and K in (2048, 4096, 8192) and wl.signs is None:
+        quant_kernel = "quant_rrs_full_kernel"  # after rrs_colmax_full_kernel, in the same call
+    else:
+        quant_kernel = "quant_rowh_kernel"
     out = {
         "metric": METRIC,
         "value": layer_tops,

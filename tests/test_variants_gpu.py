@@ -115,3 +115,19 @@ def test_signed_weight_layouts_agree():
         qw2, sw2 = rw4.pack_weight(t, w.t().contiguous(), "nk")
         torch.cuda.synchronize()
         assert torch.equal(qw1, qw2) and torch.equal(sw1, sw2)
+
+
+@pytest.mark.parametrize("layers", [4, 12, 16])
+def test_givens_layer_counts(layers):
+    """ParoQuant-style plans with other numbers of rotation layers (the plan is
+    an input; the kernel batches its table loads 8 layers at a time)."""
+    M, K, N = 6, 512, 40
+    rng = np.random.default_rng(100 + layers)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    plan = dict(zip(("pairs", "theta", "beta"), datagen.givens_plan(9, K, layers=layers)))
+    wl = datagen.Workload(f"givens_L{layers}", M, K, N, x, "bf16", w, ("givens", layers), "group128", "f32",
+                          **plan)
+    t, xd, qa, sa, aref = tp._quant_parity(wl)
+    qw, sw, wref = tp._weight_parity(wl, t)
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
