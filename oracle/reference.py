@@ -405,37 +405,43 @@ def round_dequant_output(x: np.ndarray, dtype: str) -> np.ndarray:
 # The three library calls, as plain definitions
 # --------------------------------------------------------------------------
 
-def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128"):
-    """Oracle of quantize_act: transform, then group-128 or RRS per-token INT4.
+def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GROUP):
+    """Oracle of quantize_act: transform, then per-group or RRS per-token INT4.
 
-    Returns dict(qa=packed uint8 [M, K/2], sa=float64 [M, G], codes, ratio,
-    xt=transformed activations, s=RRS group scales or None).
+    ``g`` is the quantization group ([Paro] section 2.3 uses 128; other
+    group sizes are a knob of the same quantizer).  Returns dict(qa=packed
+    uint8 [M, K/2], sa=float64 [M, K/g], codes, ratio, xt=transformed
+    activations, s=RRS group scales or None).
     """
     xt = transform_act(X, spec)
     if mode == "group128":
-        codes, sa, ratio = quantize_groups(xt)
+        codes, sa, ratio = quantize_groups(xt, g)
         s = None
     elif mode == "rrs":
-        codes, sa, s, ratio = quantize_rrs(xt)
+        codes, sa, s, ratio = quantize_rrs(xt, g)
     else:
         raise ValueError(mode)
     return {"qa": pack_int4(codes), "sa": sa, "codes": codes, "ratio": ratio, "xt": xt, "s": s}
 
 
-def pack_weight(W: np.ndarray, spec: dict):
+def pack_weight(W: np.ndarray, spec: dict, g: int = GROUP):
     """Oracle of pack_weight: W_tilde = T_w W, per-(output channel, group) INT4.
 
-    W is [K, N].  Returns dict(qw=packed uint8 [N, K/2], sw=float64 [N, G],
+    W is [K, N].  Returns dict(qw=packed uint8 [N, K/2], sw=float64 [N, K/g],
     codes [N, K], ratio [N, K], wt=W_tilde [K, N]).
     """
     wt = transform_weight(W, spec)
-    codes, sw, ratio = quantize_groups(wt.T)
+    codes, sw, ratio = quantize_groups(wt.T, g)
     return {"qw": pack_int4(codes), "sw": sw, "codes": codes, "ratio": ratio, "wt": wt}
 
 
 def w4a4_gemm(qa_packed, sa, qw_packed, sw, out_dtype: str = "f32") -> np.ndarray:
-    """Oracle of w4a4_gemm: unpack, exact grouped integer products, float64 epilogue, output rounding."""
-    Y = dequant_gemm(unpack_int4(qa_packed), sa, unpack_int4(qw_packed), sw)
+    """Oracle of w4a4_gemm: unpack, exact grouped integer products, float64 epilogue, output rounding.
+
+    The group size is K divided by the number of scale columns."""
+    qa = unpack_int4(qa_packed)
+    g = qa.shape[1] // np.asarray(sa).shape[1]
+    Y = dequant_gemm(qa, sa, unpack_int4(qw_packed), sw, g)
     return round_output(Y, out_dtype)
 
 

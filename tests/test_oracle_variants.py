@@ -89,3 +89,93 @@ def test_dequant_output_rounding():
     assert rb[0, 0] == 7.0  # nearest bf16 of 7.0000008
     with pytest.raises(ValueError):
         oracle.round_dequant_output(x, "f16")
+
+
+# ---------------------------------------------------------------------------
+# Group size as a knob of the same quantizer ([Paro] section 2.3 groups
+# channels by 128; 64 and 256 are the neighbouring choices).  Pins: the
+# group maximum nests (a 256-group's scale is the larger of its two
+# 128-groups', and so on), codes keep the per-group quantizer properties,
+# and the grouped integer products add up across group sizes exactly.
+# ---------------------------------------------------------------------------
+
+def _outlier_rows(seed, R, K):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, K))
+    x[:, rng.choice(K, 5, replace=False)] *= 80.0
+    return x
+
+
+@pytest.mark.parametrize("small,big", [(64, 128), (128, 256), (64, 256)])
+def test_group_scales_nest(small, big):
+    x = _outlier_rows(4, 9, 1024)
+    _, s_small, _ = oracle.quantize_groups(x, small)
+    _, s_big, _ = oracle.quantize_groups(x, big)
+    r = big // small
+    assert s_small.shape == (9, 1024 // small) and s_big.shape == (9, 1024 // big)
+    assert np.array_equal(s_big, s_small.reshape(9, -1, r).max(axis=2))
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_quantizer_properties_at_other_group_sizes(g):
+    x = _outlier_rows(5, 6, 1024)
+    x[2, :g] = 0.0                                   # one all-zero group
+    codes, s, ratio = oracle.quantize_groups(x, g)
+    assert codes.min() >= -7 and codes.max() <= 7
+    xg = x.reshape(6, -1, g)
+    cg = codes.reshape(6, -1, g)
+    for r in range(6):
+        for j in range(xg.shape[1]):
+            if s[r, j] == 0:
+                assert not cg[r, j].any() and not xg[r, j].any()
+                continue
+            i = np.argmax(np.abs(xg[r, j]))
+            assert abs(cg[r, j, i]) == 7                               # the maximum maps to +-7
+            assert np.all(np.abs(xg[r, j] - s[r, j] * cg[r, j]) <= s[r, j] / 2 * (1 + 1e-12))
+    assert s[2, 0] == 0
+
+
+def test_group_accumulators_add_up_across_group_sizes():
+    rng = np.random.default_rng(6)
+    qa = rng.integers(-7, 8, size=(5, 512))
+    qw = rng.integers(-7, 8, size=(3, 512))
+    a64 = oracle.group_accumulators(qa, qw, 64)
+    a128 = oracle.group_accumulators(qa, qw, 128)
+    a256 = oracle.group_accumulators(qa, qw, 256)
+    assert np.array_equal(a128, a64[:, :, 0::2] + a64[:, :, 1::2])
+    assert np.array_equal(a256, a128[:, :, 0::2] + a128[:, :, 1::2])
+    # brute force in Python integers at g = 256
+    for m in range(5):
+        for n in range(3):
+            for j in range(2):
+                ref = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(256 * j, 256 * j + 256))
+                assert a256[m, n, j] == ref
+
+
+def test_gemm_at_g256_equals_g128_with_shared_scales():
+    rng = np.random.default_rng(7)
+    M, N, K = 4, 6, 1024
+    qa = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    sa = rng.uniform(0.1, 2.0, size=(M, K // 256))
+    sw = rng.uniform(0.1, 2.0, size=(N, K // 256))
+    y256 = oracle.dequant_gemm(qa, sa, qw, sw, 256)
+    y128 = oracle.dequant_gemm(qa, np.repeat(sa, 2, axis=1), qw, np.repeat(sw, 2, axis=1), 128)
+    assert np.allclose(y256, y128, rtol=1e-13, atol=0)
+    # the packed entry point takes the group size from the scale shapes
+    y = oracle.w4a4_gemm(oracle.pack_int4(qa), sa, oracle.pack_int4(qw), sw, "f64")
+    assert np.array_equal(y, y256)
+
+
+def test_quantize_act_group_size_follows_the_transform():
+    X = _outlier_rows(8, 7, 512)
+    spec = {"kind": "hadamard", "block": 128}
+    a128 = oracle.quantize_act(X, spec, "group128", 128)
+    a256 = oracle.quantize_act(X, spec, "group128", 256)
+    a64 = oracle.quantize_act(X, spec, "group128", 64)
+    assert np.array_equal(a128["xt"], a256["xt"])
+    assert np.array_equal(a256["sa"], a128["sa"].reshape(7, -1, 2).max(axis=2))
+    assert np.array_equal(a128["sa"], a64["sa"].reshape(7, -1, 2).max(axis=2))
+    # dequantization at g = 64 is within half a step of the transformed values
+    xh = oracle.dequantize(a64["codes"], a64["sa"], 64)
+    assert np.all(np.abs(xh - a64["xt"]) <= np.repeat(a64["sa"], 64, axis=1) / 2 * (1 + 1e-12))
