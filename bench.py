@@ -101,6 +101,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny"])
+    ap.add_argument("--group", type=int, default=128, choices=[128, 256],
+                    help="quantization group size (block-128 Hadamard workloads for 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -154,10 +156,10 @@ def workload(name):
     return datagen.make(name)
 
 
-def algorithmic_bytes(wl):
+def algorithmic_bytes(wl, group=128):
     """Quantize: read X once, write qa and sa.  GEMM: read qa, sa, qw, sw once, write Y."""
     M, K, N = wl.M, wl.K, wl.N
-    G = K // 128
+    G = K // group
     xb = 2 if wl.x_dtype == "bf16" else 4
     yb = 2 if wl.y_dtype == "bf16" else 4
     quant = M * K * xb + M * K // 2 + M * G * 4
@@ -214,19 +216,22 @@ def main():
         return
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
-    G = K // 128
+    grp = args.group
+    if grp != 128 and not (wl.transform == ("hadamard", 128) and wl.mode == "group128"):
+        raise SystemExit("--group 256 needs a block-128 Hadamard workload in per-group mode")
+    G = K // grp
     log(f"workload {wl.name} M={M} K={K} N={N} transform={wl.transform} mode={wl.mode} "
         f"device={torch.cuda.get_device_name(dev)}")
 
     t = gu.transform_for(wl)
     x0 = gu.x_to_device(wl.x, wl.x_dtype)
     w0 = torch.from_numpy(wl.w).to(dev)
-    qw0, sw0 = rw4.pack_weight(t, w0)
+    qw0, sw0 = rw4.pack_weight(t, w0, group=grp)
     torch.cuda.synchronize()
     del w0
 
     ydt = torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32
-    qbytes, gbytes = algorithmic_bytes(wl)
+    qbytes, gbytes = algorithmic_bytes(wl, grp)
     set_bytes = qbytes + gbytes
     nsets = max(2, math.ceil(MALL_FLUSH_BYTES / set_bytes))
     sets = []
@@ -248,7 +253,7 @@ def main():
         s = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
-        rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"])
+        rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"], group=grp)
         if ev is not None:
             ev[1].record(stream)
         rw4.w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"])
@@ -292,7 +297,7 @@ def main():
 
     def q_only(i):
         st = sets[i % nsets]
-        rw4.quantize_act(t, st["x"], wl.mode, qa=st["qa"], sa=st["sa"], workspace=st["ws"])
+        rw4.quantize_act(t, st["x"], wl.mode, qa=st["qa"], sa=st["sa"], workspace=st["ws"], group=grp)
 
     def g_only(i):
         st = sets[i % nsets]
@@ -303,7 +308,8 @@ def main():
 
     decode = M <= 16
     gemm_kernel = "gemm_small_kernel" if decode else "gemm_f8_kernel"
-    traffic = measured_traffic(gemm_kernel, args.workload)
+    wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
+    traffic = measured_traffic(gemm_kernel, wkey)
     if decode:
         # the small-M GEMM streams the packed weights: HBM-bound
         roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -340,13 +346,13 @@ def main():
         "config": {"workload": f"{wl.name} M={M} K={K} N={N}", "M": M, "K": K, "N": N,
                    "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,
                    "x_dtype": wl.x_dtype, "y_dtype": wl.y_dtype, "weights": "packed offline",
-                   "buffer_sets": nsets},
+                   "buffer_sets": nsets, "group": grp},
         "roofline": roof,
         "quantize": {"kernel": quant_kernel, "avg_launch_us": q_us, "gbps": quant_gbps,
                      "frac_hbm": quant_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": qbytes,
                      "back_to_back_us": q_b2b, "back_to_back_gbps": qbytes / (q_b2b * 1e-6) / 1e9,
                      "back_to_back_frac_hbm": qbytes / (q_b2b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(quant_kernel, args.workload)},
+                     "traffic": measured_traffic(quant_kernel, wkey)},
         "gemm": {"kernel": gemm_kernel, "avg_launch_us": g_us, "tops": gemm_tops,
                  "frac_mfma": gemm_tops / PEAK_I8_TOPS, "gbps": gemm_gbps,
                  "back_to_back_us": g_b2b, "back_to_back_tops": ops / (g_b2b * 1e-6) / 1e12},

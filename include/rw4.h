@@ -177,6 +177,35 @@ rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, 
                          int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype,
                          int64_t ldy, void* stream);
 
+/* ---- Group-size variants -------------------------------------------------
+ * The same four calls with the quantization group as an argument (the
+ * independent-rotation article, section 2.3, shares one set of quantization
+ * parameters per group of 128 channels; 64 and 256 are the neighbouring
+ * choices).  Scale arrays then hold K / group columns per row.  group must
+ * be 64, 128 or 256 (RW4_ERR_ARG otherwise) and divide K (RW4_ERR_SHAPE);
+ * group 128 is exactly the call without the suffix.  Supported beyond 128
+ * (RW4_ERR_UNSUPPORTED otherwise):
+ *   quantize_act_g  64 and 256 with a block-128 Hadamard transform (plain or
+ *                   signed) in RW4_ACT_GROUP128 mode (per-group scales);
+ *   pack_weight_g   256 with a block-128 Hadamard transform;
+ *   w4a4_gemm_g     256 (the two 128-wide halves of a group accumulate into
+ *                   one exact integer sum, |sum| <= 256 * 49, before the
+ *                   rescale); 64 is not supported by the GEMM;
+ *   dequantize_g    64 and 256.
+ * A 64-group INT4 KV cache is written with quantize_act_g and read with
+ * dequantize_g. */
+rw4_status rw4_quantize_act_g(const rw4_transform* t, rw4_act_mode mode, int32_t group, const void* x,
+                              rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
+                              float* workspace, void* stream);
+rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* w, rw4_dtype w_dtype,
+                             int64_t N, int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
+                             void* stream);
+rw4_status rw4_w4a4_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, rw4_dtype y_dtype,
+                           int64_t ldy, void* stream);
+rw4_status rw4_dequantize_g(const uint8_t* q, const float* s, int64_t M, int64_t K, int32_t group, void* out,
+                            rw4_dtype out_dtype, int64_t ldo, void* stream);
+
 /* Static description of a status code. */
 const char* rw4_status_str(rw4_status s);
 

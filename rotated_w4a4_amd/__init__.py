@@ -33,7 +33,8 @@ MODES = {"group128": 0, "rrs": 1}
 EXPORTED_SYMBOLS = (
     "rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
     "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
-    "rw4_dequantize", "rw4_w4a4_gemm", "rw4_status_str", "rw4_version",
+    "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
+    "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_status_str", "rw4_version",
 )
 
 
@@ -68,6 +69,10 @@ lib.rw4_quantize_act.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64,
 lib.rw4_pack_weight.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_w4a4_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int, _i64, _p]
 lib.rw4_dequantize.argtypes = [_p, _p, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+lib.rw4_quantize_act_g.argtypes = [_p, ctypes.c_int, _i32, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
+lib.rw4_pack_weight_g.argtypes = [_p, _i32, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
+lib.rw4_w4a4_gemm_g.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
+lib.rw4_dequantize_g.argtypes = [_p, _p, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 for _name in ("rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
               "rw4_transform_destroy", "rw4_quantize_act", "rw4_pack_weight", "rw4_dequantize",
               "rw4_w4a4_gemm"):
@@ -172,11 +177,13 @@ class Transform:
             pass
 
 
-def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, workspace=None):
+def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, workspace=None,
+                 group: int = 128):
     """Transform + INT4-quantize activations x [M, K] (bf16/fp32, unit stride in K).
 
-    Returns (qa uint8 [M, K/2], sa fp32 [M, K/128]).  For mode="rrs" a
+    Returns (qa uint8 [M, K/2], sa fp32 [M, K/group]).  For mode="rrs" a
     workspace of K/128 fp32 is allocated unless given (it receives s_g).
+    mode "group128" means per-group scales, of `group` channels.
     """
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
@@ -186,19 +193,19 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
     if qa is None:
         qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     if sa is None:
-        sa = torch.empty((M, G), dtype=torch.float32, device=x.device)
+        sa = torch.empty((M, K // group), dtype=torch.float32, device=x.device)
     if mode == "rrs" and workspace is None:
         workspace = torch.empty((max(G, 4),), dtype=torch.float32, device=x.device)
-    _check(lib.rw4_quantize_act(t.handle, MODES[mode], _ptr(x), _dtype_code(x), M, x.stride(0),
-                                _ptr(qa), _ptr(sa), _ptr(workspace), _stream(x.device)),
+    _check(lib.rw4_quantize_act_g(t.handle, MODES[mode], group, _ptr(x), _dtype_code(x), M, x.stride(0),
+                                  _ptr(qa), _ptr(sa), _ptr(workspace), _stream(x.device)),
            "rw4_quantize_act")
     return qa, sa
 
 
-def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None):
+def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: int = 128):
     """Transform + INT4-pack weights. layout "kn": w is [K, N]; "nk": w is [N, K] (nn.Linear).
 
-    Returns (qw uint8 [N, K/2], sw fp32 [N, K/128]).
+    Returns (qw uint8 [N, K/2], sw fp32 [N, K/group]).
     """
     torch = _torch()
     if w.dim() != 2:
@@ -214,44 +221,56 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None):
     if qw is None:
         qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
     if sw is None:
-        sw = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
-    _check(lib.rw4_pack_weight(t.handle, _ptr(w), _dtype_code(w), N, sk, sn, _ptr(qw), _ptr(sw),
-                               _stream(w.device)),
+        sw = torch.empty((N, K // group), dtype=torch.float32, device=w.device)
+    _check(lib.rw4_pack_weight_g(t.handle, group, _ptr(w), _dtype_code(w), N, sk, sn, _ptr(qw), _ptr(sw),
+                                 _stream(w.device)),
            "rw4_pack_weight")
     return qw, sw
 
 
+def _group_of(K, cols):
+    if cols <= 0 or K % cols or (K // cols) not in (64, 128, 256):
+        raise ValueError("scale columns do not give a group of 64, 128 or 256 channels")
+    return K // cols
+
+
 def dequantize(q, s, out_dtype=None, out=None):
-    """x_hat [M, K] = codes * group scale (transformed domain), fp32 or bf16."""
+    """x_hat [M, K] = codes * group scale (transformed domain), fp32 or bf16.
+
+    The group size is K divided by the number of scale columns."""
     torch = _torch()
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
     M, Kh = q.shape
     K = Kh * 2
-    if s.shape != (M, K // 128):
+    if s.dim() != 2 or s.shape[0] != M:
         raise ValueError("scale shape does not match the codes")
+    group = _group_of(K, s.shape[1])
     if not (q.is_contiguous() and s.is_contiguous()):
         raise ValueError("q and s must be contiguous")
     if out is None:
         out = torch.empty((M, K), dtype=out_dtype, device=q.device)
     if out.stride(1) != 1:
         raise ValueError("out must have unit stride along K")
-    _check(lib.rw4_dequantize(_ptr(q), _ptr(s), M, K, _ptr(out), _dtype_code(out), out.stride(0),
-                              _stream(q.device)),
+    _check(lib.rw4_dequantize_g(_ptr(q), _ptr(s), M, K, group, _ptr(out), _dtype_code(out), out.stride(0),
+                                _stream(q.device)),
            "rw4_dequantize")
     return out
 
 
 def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
-    """Y [M, N] = sum over groups of sa * sw * int32 group products (fp32 epilogue)."""
+    """Y [M, N] = sum over groups of sa * sw * exact integer group products (fp32 epilogue).
+
+    The group size is K divided by the number of scale columns."""
     torch = _torch()
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
     M, Kh = qa.shape
     N = qw.shape[0]
     K = Kh * 2
-    if qw.shape[1] != Kh or sa.shape != (M, K // 128) or sw.shape != (N, K // 128):
+    if qw.shape[1] != Kh or sa.dim() != 2 or sa.shape[0] != M or sw.shape != (N, sa.shape[1]):
         raise ValueError("operand shapes do not match")
+    group = _group_of(K, sa.shape[1])
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
     if out.stride(1) != 1:
@@ -259,7 +278,7 @@ def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
     for tns in (qa, sa, qw, sw):
         if not tns.is_contiguous():
             raise ValueError("qa/sa/qw/sw must be contiguous")
-    _check(lib.rw4_w4a4_gemm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, _ptr(out),
-                             _dtype_code(out), out.stride(0), _stream(qa.device)),
+    _check(lib.rw4_w4a4_gemm_g(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, group, _ptr(out),
+                               _dtype_code(out), out.stride(0), _stream(qa.device)),
            "rw4_w4a4_gemm")
     return out

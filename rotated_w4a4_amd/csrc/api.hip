@@ -191,16 +191,22 @@ rw4_status rw4_transform_destroy(rw4_transform* t) {
   return from_hip(e);
 }
 
-rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const void* x,
-                            rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
-                            float* workspace, void* stream) {
+static bool group_known(int32_t g) { return g == 64 || g == 128 || g == 256; }
+
+rw4_status rw4_quantize_act_g(const rw4_transform* t, rw4_act_mode mode, int32_t group, const void* x,
+                              rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
+                              float* workspace, void* stream) {
   if (!t) return RW4_ERR_ARG;
   if (mode != RW4_ACT_GROUP128 && mode != RW4_ACT_RRS_PER_TOKEN) return RW4_ERR_ARG;
   if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (!group_known(group)) return RW4_ERR_ARG;
   if (M < 0) return RW4_ERR_SHAPE;
   const int64_t K = t->dev.K;
+  if (K % group) return RW4_ERR_SHAPE;
   const bool rrs = mode == RW4_ACT_RRS_PER_TOKEN;
   if (rrs && (t->dev.kind != rw4::TransformKind::Hadamard || !rw4::rowh_supported(K)))
+    return RW4_ERR_UNSUPPORTED;
+  if (group != 128 && (rrs || t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
     return RW4_ERR_UNSUPPORTED;
   if (M == 0) return RW4_OK;
   if (!x || !qa || !sa) return RW4_ERR_ARG;
@@ -211,15 +217,27 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
   if (rrs && !aligned16(workspace)) return RW4_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return from_hip(rw4::launch_quantize_act(t->dev, rrs, x, x_dtype == RW4_BF16, M, ldx, qa, sa,
-                                           workspace, st));
+                                           workspace, group, st));
 }
 
-rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
-                           int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
-                           void* stream) {
+rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const void* x,
+                            rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
+                            float* workspace, void* stream) {
+  return rw4_quantize_act_g(t, mode, 128, x, x_dtype, M, ldx, qa, sa, workspace, stream);
+}
+
+rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* w, rw4_dtype w_dtype,
+                             int64_t N, int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
+                             void* stream) {
   if (!t) return RW4_ERR_ARG;
   if (w_dtype != RW4_F32 && w_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (!group_known(group)) return RW4_ERR_ARG;
   if (N < 0) return RW4_ERR_SHAPE;
+  if (t->dev.K % group) return RW4_ERR_SHAPE;
+  // the GEMM consumes 128- and 256-wide groups; 256 for the block-128 Hadamard
+  if (group == 64) return RW4_ERR_UNSUPPORTED;
+  if (group == 256 && (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
+    return RW4_ERR_UNSUPPORTED;
   if (N == 0) return RW4_OK;
   if (!w || !qw || !sw) return RW4_ERR_ARG;
   if (stride_k <= 0 || stride_n <= 0) return RW4_ERR_ARG;
@@ -227,34 +245,54 @@ rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dt
   if ((reinterpret_cast<uintptr_t>(w) % esz) || !aligned16(qw) || !aligned16(sw)) return RW4_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return from_hip(rw4::launch_pack_weight(t->dev, w, w_dtype == RW4_BF16, N, stride_k, stride_n, qw,
-                                          sw, st));
+                                          sw, group, st));
 }
 
-rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
-                          rw4_dtype out_dtype, int64_t ldo, void* stream) {
+rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
+                           int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
+                           void* stream) {
+  return rw4_pack_weight_g(t, 128, w, w_dtype, N, stride_k, stride_n, qw, sw, stream);
+}
+
+rw4_status rw4_dequantize_g(const uint8_t* q, const float* s, int64_t M, int64_t K, int32_t group, void* out,
+                            rw4_dtype out_dtype, int64_t ldo, void* stream) {
   if (out_dtype != RW4_F32 && out_dtype != RW4_BF16) return RW4_ERR_ARG;
-  if (M < 0 || K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (!group_known(group)) return RW4_ERR_ARG;
+  if (M < 0 || K <= 0 || K % group) return RW4_ERR_SHAPE;
   if (M == 0) return RW4_OK;
   if (!q || !s || !out) return RW4_ERR_ARG;
   if (ldo < K) return RW4_ERR_ARG;
   const int64_t esz = out_dtype == RW4_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(s) || !aligned16(out) || (ldo * esz) % 16) return RW4_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return from_hip(rw4::launch_dequantize(q, s, M, K, out, out_dtype == RW4_BF16, ldo, st));
+  return from_hip(rw4::launch_dequantize(q, s, M, K, group, out, out_dtype == RW4_BF16, ldo, st));
 }
 
-rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                         int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype, int64_t ldy,
-                         void* stream) {
+rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+                          rw4_dtype out_dtype, int64_t ldo, void* stream) {
+  return rw4_dequantize_g(q, s, M, K, 128, out, out_dtype, ldo, stream);
+}
+
+rw4_status rw4_w4a4_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, rw4_dtype y_dtype,
+                           int64_t ldy, void* stream) {
   if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
-  if (M < 0 || N < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
+  if (!group_known(group)) return RW4_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0 || K % kGroup || K % group || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
+  if (group == 64) return RW4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return RW4_OK;
   if (!qa || !sa || !qw || !sw || !y) return RW4_ERR_ARG;
   if (ldy < N) return RW4_ERR_ARG;
   if (!aligned16(qa) || !aligned16(qw) || !aligned16(sa) || !aligned16(sw) || !aligned16(y))
     return RW4_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return from_hip(rw4::launch_gemm(qa, sa, qw, sw, M, N, K, y, y_dtype == RW4_BF16, ldy, st));
+  return from_hip(rw4::launch_gemm(qa, sa, qw, sw, M, N, K, group, y, y_dtype == RW4_BF16, ldy, st));
+}
+
+rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                         int64_t M, int64_t N, int64_t K, void* y, rw4_dtype y_dtype, int64_t ldy,
+                         void* stream) {
+  return rw4_w4a4_gemm_g(qa, sa, qw, sw, M, N, K, 128, y, y_dtype, ldy, stream);
 }
 
 }  // extern "C"

@@ -13,17 +13,18 @@
 
 namespace rw4 {
 
+// log2g: log2 of the group (6, 7 or 8); a lane's 32 codes lie in one group.
 template <bool BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ q,
                                                       const float* __restrict__ s, int64_t M, int64_t K,
-                                                      void* __restrict__ out, int64_t ldo) {
+                                                      int log2g, void* __restrict__ out, int64_t ldo) {
   const int64_t chunks_per_row = K / 32;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= M * chunks_per_row) return;
   const int64_t row = idx / chunks_per_row;
   const int64_t k0 = (idx - row * chunks_per_row) * 32;
   const uint4 w4 = *reinterpret_cast<const uint4*>(q + row * (K / 2) + k0 / 2);
-  const float sc = s[row * (K / kGroup) + k0 / kGroup];
+  const float sc = s[row * (K >> log2g) + (k0 >> log2g)];
   const uint32_t words[4] = {w4.x, w4.y, w4.z, w4.w};
   float v[32];
 #pragma unroll
@@ -57,15 +58,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
-hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, int group, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st) {
+  const int log2g = group == 64 ? 6 : group == 256 ? 8 : 7;
   const int64_t lanes = M * (K / 32);
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL((dequant_kernel<true>), dim3(blocks), dim3(256), 0, st, q, s, M, K, out, ldo);
+    hipLaunchKernelGGL((dequant_kernel<true>), dim3(blocks), dim3(256), 0, st, q, s, M, K, log2g, out, ldo);
   else
-    hipLaunchKernelGGL((dequant_kernel<false>), dim3(blocks), dim3(256), 0, st, q, s, M, K, out, ldo);
+    hipLaunchKernelGGL((dequant_kernel<false>), dim3(blocks), dim3(256), 0, st, q, s, M, K, log2g, out, ldo);
   return hipGetLastError();
 }
 

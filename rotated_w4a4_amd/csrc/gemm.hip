@@ -218,7 +218,11 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t nb, int64_t til
   nt = li / gm;
 }
 
-template <bool BF16>
+// G256: scales per 256-wide group (the two 128-groups of a stage share one
+// scale pair): the accumulator runs over both groups of the stage (partial
+// sums below 256 * 49 < 2^24, still exact) and the scale products and the
+// epilogue run once per stage.
+template <bool BF16, bool G256>
 __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restrict__ qa,
                                                          const float* __restrict__ sa,
                                                          const uint8_t* __restrict__ qw,
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t G = K / kGroup;
+  const int64_t GS = G256 ? G / 2 : G;  // scale columns
   const int64_t rowbytes = K / 2;
   int64_t mt, nt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, mt, nt);
@@ -266,16 +271,16 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   // or sw of tile column tid - 128 (waves 0-1 rows, waves 2-3 columns)
   const bool row_scale = wave < 2;
   const __amdgpu_buffer_rsrc_t rs =
-      row_scale ? make_rsrc(sa + m0 * G, rows_a * G * 4) : make_rsrc(sw + n0 * G, rows_b * G * 4);
+      row_scale ? make_rsrc(sa + m0 * GS, rows_a * GS * 4) : make_rsrc(sw + n0 * GS, rows_b * GS * 4);
   uint32_t sc_off;  // byte offset of this thread's scale row
   {
     const int64_t r = row_scale ? tid : tid - 128;
     const int64_t lim = row_scale ? rows_a : rows_b;
-    sc_off = uint32_t((r < lim ? r : lim - 1) * G * 4);
+    sc_off = uint32_t((r < lim ? r : lim - 1) * GS * 4);
   }
-  auto sc_load = [&](int64_t g) {
+  auto sc_load = [&](int64_t g) {  // scale column g (clamped; past the end never read)
     return __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rs, int(sc_off), int((g < G ? g : G - 1) * 4), 0));
+        __builtin_amdgcn_raw_buffer_load_b32(rs, int(sc_off), int((g < GS ? g : GS - 1) * 4), 0));
   };
   const SplitSel sel = split_selectors(row_scale);
   const uint32_t sp_addr = lds_off(sm.split + tid * 16);
@@ -314,17 +319,25 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
 
-  auto compute = [&](auto q_const) {
+  // One 128-group from group buffer q.  INIT: the accumulators start at
+  // zero (else they continue); EPI: the scale products (split operands of
+  // group buffer QS) and the epilogue follow.
+  v16f acc[2][2];
+  auto compute = [&](auto q_const, auto qs_const, auto init_const, auto epi_const) {
     constexpr int q = decltype(q_const)::value;
+    constexpr int qs = decltype(qs_const)::value;
+    constexpr bool init = decltype(init_const)::value;
+    constexpr bool epi = decltype(epi_const)::value;
     v4u fr[4], ps[4];
-    v16f acc[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // fr: A tile 0, A tile 1, B tile 0, B tile 1 of this K-half
       if (ks == 0)
         lds_read_half0<tile_off(q)>(fr, ba0, bb0);
+      else if constexpr (epi)
+        lds_read_half1<tile_off(q), split_off(qs)>(fr, ps, ba1, bb1, bsa, bsb);
       else
-        lds_read_half1<tile_off(q), split_off(q)>(fr, ps, ba1, bb1, bsa, bsb);
+        lds_read_half0<tile_off(q)>(fr, ba1, bb1);  // K-half 1 fragments only
       v8i oa[2], ob[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) oa[i] = f8_operand(fr[i]);
@@ -334,13 +347,14 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const v16f c = ks == 0 ? v16f{} : acc[i][j];
+          const v16f c = (init && ks == 0) ? v16f{} : acc[i][j];
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], c, 0, 0, 0, kE8Scale,
                                                                      0, kE8Scale);
         }
       // keep each half's unpack and MFMAs together (bounds register use)
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!epi) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -381,20 +395,37 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   using Q1 = std::integral_constant<int, 1>;
   using Q2 = std::integral_constant<int, 2>;
   using Q3 = std::integral_constant<int, 3>;
-  put_split(Q0{}, sc_load(0));
-  put_split(Q1{}, sc_load(1));
+  // With 256-wide scale groups (G even) stage s is scale column s: one split
+  // per stage, in the stage's first buffer.
+  using T = std::true_type;
+  using F = std::false_type;
+  if constexpr (G256) {
+    put_split(Q0{}, sc_load(0));
+  } else {
+    put_split(Q0{}, sc_load(0));
+    put_split(Q1{}, sc_load(1));
+  }
   issue(0, 0);
   issue(1, 1);
   const int64_t S = (G + 1) / 2;
   auto stage = [&](auto q0, auto q1, auto n0_, auto n1_, int64_t s) {
     wait_vm_barrier<0>();
-    const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
-    issue(decltype(n0_)::value, 2 * s + 2);
-    issue(decltype(n1_)::value, 2 * s + 3);
-    compute(q0);
-    if (2 * s + 1 < G) compute(q1);
-    put_split(n0_, x0);
-    put_split(n1_, x1);
+    if constexpr (G256) {
+      const float x0 = sc_load(s + 1);
+      issue(decltype(n0_)::value, 2 * s + 2);
+      issue(decltype(n1_)::value, 2 * s + 3);
+      compute(q0, q0, T{}, F{});
+      compute(q1, q0, F{}, T{});
+      put_split(n0_, x0);
+    } else {
+      const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
+      issue(decltype(n0_)::value, 2 * s + 2);
+      issue(decltype(n1_)::value, 2 * s + 3);
+      compute(q0, q0, T{}, T{});
+      if (2 * s + 1 < G) compute(q1, q1, T{}, T{});
+      put_split(n0_, x0);
+      put_split(n1_, x1);
+    }
   };
   for (int64_t s = 0; s < S; s += 2) {
     stage(Q0{}, Q1{}, Q2{}, Q3{}, s);
@@ -461,19 +492,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 // MFMA covers a whole group.  Fragments come straight from global memory
 // (no reuse to stage); the partial results are summed across waves in LDS.
 // ---------------------------------------------------------------------------
+// G256: each scale column covers two consecutive 128-groups, whose two
+// MFMAs chain into one accumulator before the scale is applied.
 constexpr int kSmallWaves = 8;
-template <bool BF16>
+template <bool BF16, bool G256>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint8_t* __restrict__ qa,
                                                                       const float* __restrict__ sa,
                                                                       const uint8_t* __restrict__ qw,
                                                                       const float* __restrict__ sw, int64_t M,
                                                                       int64_t N, int64_t K, void* __restrict__ y,
                                                                       int64_t ldy) {
-  constexpr int NB = 4;  // groups in flight per wave
+  constexpr int P = G256 ? 2 : 1;       // 128-groups per scale column
+  constexpr int NB = 4 / P;             // scale columns in flight per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t G = K / kGroup;
+  const int64_t GS = K / (kGroup * P);  // scale columns
   const int64_t rowbytes = K / 2;
   const int64_t n0 = int64_t(blockIdx.x) * 16;
   const int64_t am = lane & 15;               // A row supplied by this lane
@@ -482,30 +516,35 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
   const bool a_ok = am < M, b_ok = bn < N;
 
   float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t gb = wave; gb < G; gb += kSmallWaves * NB) {
-    v4u pa[NB], pb[NB];
+  for (int64_t gb = wave; gb < GS; gb += kSmallWaves * NB) {
+    v4u pa[NB][P], pb[NB][P];
     float swv[NB], sav[NB][4];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + kSmallWaves * t;
-      const bool in = g < G;
-      pa[t] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + g * 64 + part * 16)
-                           : v4u{0u, 0u, 0u, 0u};
-      pb[t] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + g * 64 + part * 16)
-                           : v4u{0u, 0u, 0u, 0u};
-      swv[t] = (in && b_ok) ? sw[bn * G + g] : 0.0f;
+      const bool in = g < GS;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int64_t off = (g * P + p) * 64 + part * 16;
+        pa[t][p] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
+        pb[t][p] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
+      }
+      swv[t] = (in && b_ok) ? sw[bn * GS + g] : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = part * 4 + r;
-        sav[t][r] = (in && m < M) ? sa[m * G + g] : 0.0f;
+        sav[t][r] = (in && m < M) ? sa[m * GS + g] : 0.0f;
       }
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + kSmallWaves * t;
-      if (g >= G) break;
-      const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          f8_operand(pa[t]), f8_operand(pb[t]), v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+      if (g >= GS) break;
+      v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0]), f8_operand(pb[t][0]),
+                                                                 v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+      if constexpr (G256)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1]), f8_operand(pb[t][1]), acc,
+                                                               0, 0, 0, kE8Scale, 0, kE8Scale);
 #pragma unroll
       for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][r] * swv[t], yv[r]);
     }
@@ -526,16 +565,17 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
   }
 }
 
-hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                       int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
-                       hipStream_t st) {
+template <bool G256>
+hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                         int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
+                         hipStream_t st) {
   if (M <= 16) {
     const int64_t blocks = (N + 15) / 16;
     if (y_bf16)
-      hipLaunchKernelGGL((gemm_small_kernel<true>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa, sa,
-                         qw, sw, M, N, K, y, ldy);
+      hipLaunchKernelGGL((gemm_small_kernel<true, G256>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+                         sa, qw, sw, M, N, K, y, ldy);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<false>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+      hipLaunchKernelGGL((gemm_small_kernel<false, G256>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
                          sa, qw, sw, M, N, K, y, ldy);
     return hipGetLastError();
   }
@@ -545,12 +585,21 @@ hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, co
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (y_bf16)
-    hipLaunchKernelGGL((gemm_f8_kernel<true>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N, K,
-                       y, ldy, tiles_m);
+    hipLaunchKernelGGL((gemm_f8_kernel<true, G256>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
+                       K, y, ldy, tiles_m);
   else
-    hipLaunchKernelGGL((gemm_f8_kernel<false>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
+    hipLaunchKernelGGL((gemm_f8_kernel<false, G256>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
                        K, y, ldy, tiles_m);
   return hipGetLastError();
+}
+
+// group: 128 or 256 (K a multiple of it, checked by the caller)
+hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                       int64_t M, int64_t N, int64_t K, int group, void* y, bool y_bf16, int64_t ldy,
+                       hipStream_t st) {
+  if (group == 256) return launch_gemm_g<true>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  if (group == 128) return launch_gemm_g<false>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rw4

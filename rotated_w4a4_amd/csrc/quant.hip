@@ -42,7 +42,8 @@ typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 // group, 8 channels per lane (one 16-byte load for bf16).  Blocks run over
 // rows and their group ranges in a flat 1-D grid; the row and range come
 // from the block index (uniform), so the lanes do no index division.
-template <class Src, int U>
+// GS: quantization group, 128 or 256 (two adjacent groups of a quad).
+template <class Src, int U, int GS>
 __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int64_t blocks_per_row,
                                                          uint8_t* __restrict__ q, float* __restrict__ s,
                                                          float post_scale) {
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     }
   }
   uint8_t* qrow = q + row * (G * 64);
-  float* srow = s + row * G;
+  float* srow = s + row * (G * kGroup / GS);
   // lane stages in the negating form: the values of this lane end up
   // multiplied by flip = (-1)^popcount(lane & 15), undone in the encoder
   const float c1 = (lane & 1) ? -1.0f : 1.0f, c2 = (lane & 2) ? -1.0f : 1.0f;
@@ -90,13 +91,18 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     m = max_x<2>(m);
     m = max_x<4>(m);
     m = max_x<8>(m);
+    if constexpr (GS == 256) m = max_x<16>(m);
     uint32_t b[8];
     encode<8>(v[u], m, b, flip);
     const uint32_t packed = pack8_bits(b);
     const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
     if (grp < G) {
       reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
-      if (sub == 0) srow[grp] = m * post_scale;
+      if constexpr (GS == 128) {
+        if (sub == 0) srow[grp] = m * post_scale;
+      } else {
+        if ((lane & 31) == 0) srow[grp >> 1] = m * post_scale;
+      }
     }
   }
 }
@@ -173,12 +179,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// 2 x 2 transposes of a register pair and lane bit 4 (swap16) or lane bit 5
+// (swap32): afterwards a holds the values of lane bit 0 of (a, b), b those
+// of lane bit 1, and the lane bit indexes the old register.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Maximum over each 8-lane half of a DPP row (lane masks 1, 2, 7).
+__device__ __forceinline__ float row8_max_dpp(float m) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      : "+v"(m));
+  return m;
+}
+
 template <bool BF16>
 struct RawRow {
   v4u32 w[BF16 ? 1 : 2];
 };
 
-template <bool BF16, bool SIGNED, int D>
+// GS: quantization group (64, 128 or 256 channels).  The transform block
+// stays 128: a 64-group is one 8-lane half of a DPP row (lane l holds
+// Sylvester lane f(l), and f keeps lane bit 3), a 256-group two adjacent
+// rows (lanes l and l ^ 16).
+template <bool BF16, bool SIGNED, int D, int GS>
 __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                              int64_t rows, int64_t G, int64_t Q, int64_t R,
                                                              const uint32_t* __restrict__ sign_mask,
@@ -197,7 +234,14 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   // the row's buffer range (their loads read zeros, their stores vanish)
   const uint32_t x_off = uint32_t((grp * kGroup + sub * 8) * ES);
   const uint32_t q_off = uint32_t(grp * 64 + h128_lane_word(sub) * 4);
-  const uint32_t s_off = sub == 0 ? uint32_t(grp * 4) : kOutOfRange;
+  const int64_t GSN = G * kGroup / GS;  // scale columns per row
+  uint32_t s_off;
+  if constexpr (GS == 64)
+    s_off = (sub & 7) == 0 ? uint32_t((grp * 2 + (sub >> 3)) * 4) : kOutOfRange;
+  else if constexpr (GS == 128)
+    s_off = sub == 0 ? uint32_t(grp * 4) : kOutOfRange;
+  else
+    s_off = (lane & 31) == 0 ? uint32_t((grp >> 1) * 4) : kOutOfRange;
 
   uint32_t smask[8];
   if constexpr (SIGNED) {
@@ -258,7 +302,16 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-      m = row16_max_dpp(m);
+      if constexpr (GS == 64) {
+        m = row8_max_dpp(m);
+      } else {
+        m = row16_max_dpp(m);
+        if constexpr (GS == 256) {
+          float t = m;
+          swap16(m, t);
+          m = fmaxf(m, t);
+        }
+      }
       // groups whose maximum is below 2^-100 are lifted by 2^64 (exact) so
       // that 7 / m stays finite; rare, so the whole wave branches around it
       float mm = m;
@@ -280,7 +333,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
       for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
       const uint32_t packed = pack8_bits(b);
       const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
-      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, live ? G * 4 : 0);
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * GSN, live ? GSN * 4 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * post_scale), rs, int(s_off), 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -487,17 +540,6 @@ __device__ __forceinline__ int64_t rrs_word(int l, int c) {  // index of the 8-c
 }
 __device__ __forceinline__ int rrs_group(int l, int c) {  // 128-channel group
   return (c & 3) | (((l >> 4) & 3) << 2) | ((c >> 2) << 4);
-}
-
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
 }
 
 template <int NC>
@@ -790,6 +832,7 @@ int grid_for_waves(int64_t waves_needed, int64_t cap_blocks) {
 // wave: measured best at 2048 x 4096 and 4096 x 14336 (more rows per wave
 // leave the memory system less work in flight, fewer cost more setup; a
 // deeper prefetch only added work at the end of each wave).
+template <int GS>
 hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t* sign_mask, int64_t rows,
                            int64_t G, uint8_t* q, float* s, float post, hipStream_t st) {
   constexpr int D = 1;
@@ -801,7 +844,7 @@ hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t
   const int64_t blocks = (Q * R + 3) / 4;
   if (Q * R > 0x7FFFFFFF - 3 || G * 64 * (bf16 ? 4 : 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
 #define RW4_H128_ACT(B, S)                                                                              \
-  hipLaunchKernelGGL((quant_h128_act_kernel<B, S, D>), dim3(blocks), dim3(256), 0, st, x, ldx, rows, G, Q, R, \
+  hipLaunchKernelGGL((quant_h128_act_kernel<B, S, D, GS>), dim3(blocks), dim3(256), 0, st, x, ldx, rows, G, Q, R, \
                      sign_mask, q, s, post)
   if (bf16) {
     if (sign_mask) RW4_H128_ACT(true, true); else RW4_H128_ACT(true, false);
@@ -833,14 +876,14 @@ hipError_t launch_rrs_full(const void* x, bool bf16, int64_t ldx, int64_t rows, 
   return hipGetLastError();
 }
 
-template <class Src>
+template <int GS, class Src>
 hipError_t launch_h128(const Src& src, int64_t rows, int64_t G, uint8_t* q, float* s, float post,
                        hipStream_t st) {
   // 16 groups per block, one quad of groups per wave: measured faster than
   // two quads per wave at both the 4096- and the 14336-channel shapes
   const int64_t bpr = (G + 15) / 16, blocks = rows * bpr;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_h128_kernel<Src, 1>), dim3(blocks), dim3(256), 0, st, src, G, bpr, q, s, post);
+  hipLaunchKernelGGL((quant_h128_kernel<Src, 1, GS>), dim3(blocks), dim3(256), 0, st, src, G, bpr, q, s, post);
   return hipGetLastError();
 }
 
@@ -900,14 +943,20 @@ bool rowh_supported(int64_t K) {
 }
 
 // Activations: X [M, K] row-major.
+// group: 64, 128 or 256 for the block-128 Hadamard in per-group mode, else
+// 128 (the caller checks).
 hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, bool bf16, int64_t M,
-                               int64_t ldx, uint8_t* q, float* s, float* smooth, hipStream_t st) {
+                               int64_t ldx, uint8_t* q, float* s, float* smooth, int group, hipStream_t st) {
   const int64_t K = t.K, G = K / kGroup;
   if (t.kind == TransformKind::Hadamard) {
     const float post = (rrs ? 1.0f : 1.0f / 7.0f) / sqrtf(float(t.block));
     int log2b = 0;
     while ((int64_t(1) << log2b) < t.block) ++log2b;
-    if (t.block == 128 && !rrs) return launch_h128_act(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+    if (t.block == 128 && !rrs) {
+      if (group == 64) return launch_h128_act<64>(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+      if (group == 256) return launch_h128_act<256>(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+      return launch_h128_act<128>(x, bf16, ldx, t.sign_mask, M, G, q, s, post, st);
+    }
     if (rrs && t.block == K && !t.sign_mask) {
       if (K == 2048) return launch_rrs_full<4>(x, bf16, ldx, M, q, s, smooth, post, st);
       if (K == 4096) return launch_rrs_full<8>(x, bf16, ldx, M, q, s, smooth, post, st);
@@ -930,8 +979,9 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
 }
 
 // Weights: element (k, n) at w[k * sk + n * sn]; rows of the output are n.
+// group: 128, or 256 for the block-128 Hadamard (the caller checks).
 hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
-                              int64_t sn, uint8_t* q, float* s, hipStream_t st) {
+                              int64_t sn, uint8_t* q, float* s, int group, hipStream_t st) {
   const int64_t K = t.K, G = K / kGroup;
   if (t.kind == TransformKind::Hadamard) {
     const float post = (1.0f / 7.0f) / sqrtf(float(t.block));
@@ -940,7 +990,8 @@ hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, i
     // W_tilde = R^T W with R = diag(signs) H / sqrt(b): H / sqrt(b) applied
     // to the rows of diag(signs) W, so the same sign flip on channel k
     auto run = [&](const auto& src) {
-      if (t.block == 128) return launch_h128(src, N, G, q, s, post, st);
+      if (t.block == 128 && group == 256) return launch_h128<256>(src, N, G, q, s, post, st);
+      if (t.block == 128) return launch_h128<128>(src, N, G, q, s, post, st);
       return dispatch_rowh(src, K, N, log2b, false, q, s, nullptr, post, st);
     };
     if (t.sign_mask) {

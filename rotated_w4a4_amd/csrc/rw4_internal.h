@@ -25,17 +25,19 @@ struct TransformDev {
 
 bool rowh_supported(int64_t K);
 
+// group: the quantization group size (64, 128 or 256; which combinations
+// are supported is checked by the C ABI layer before these are called).
 hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, bool bf16, int64_t M,
-                               int64_t ldx, uint8_t* q, float* s, float* smooth, hipStream_t st);
+                               int64_t ldx, uint8_t* q, float* s, float* smooth, int group, hipStream_t st);
 
 hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
-                              int64_t sn, uint8_t* q, float* s, hipStream_t st);
+                              int64_t sn, uint8_t* q, float* s, int group, hipStream_t st);
 
-hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, void* out,
+hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, int group, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st);
 
 hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                       int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
+                       int64_t M, int64_t N, int64_t K, int group, void* y, bool y_bf16, int64_t ldy,
                        hipStream_t st);
 
 }  // namespace rw4

@@ -199,3 +199,50 @@ def test_dequantize_validation():
     assert d(FAKE, FAKE, 4, 128, FAKE + 4, 0, 128, None) == ARG
     assert d(FAKE, FAKE, 4, 128, FAKE, 1, 132, None) == ARG   # bf16 rows of 264 bytes: not 16-aligned
 
+
+
+def _plain_hadamard(K, block):
+    h = ctypes.c_void_p()
+    assert lib.rw4_transform_hadamard(K, block, None, ctypes.byref(h)) == OK
+    return h
+
+
+def test_group_size_validation_quantize_and_pack():
+    """Group sizes other than 64/128/256 are argument errors, a group that does
+    not divide K is a shape error, and combinations without a kernel say so;
+    all of it before any pointer is looked at or anything is launched."""
+    q, p = lib.rw4_quantize_act_g, lib.rw4_pack_weight_g
+    h128 = _plain_hadamard(512, 128)
+    h512 = _plain_hadamard(512, 512)
+    h384 = _plain_hadamard(384, 128)
+    try:
+        for g, expect in ((96, ARG), (0, ARG), (-128, ARG), (512, ARG)):
+            assert q(h128, 0, g, FAKE, 1, 4, 512, FAKE, FAKE, None, None) == expect
+            assert p(h128, g, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == expect
+        assert q(h384, 0, 256, FAKE, 1, 4, 384, FAKE, FAKE, None, None) == SHAPE
+        assert p(h384, 256, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == SHAPE
+        assert q(h512, 0, 64, FAKE, 1, 4, 512, FAKE, FAKE, None, None) == UNSUP   # block 512
+        assert q(h128, 1, 256, FAKE, 1, 4, 512, FAKE, FAKE, FAKE, None) == UNSUP  # RRS
+        assert p(h128, 64, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == UNSUP           # no 64-group GEMM
+        assert p(h512, 256, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == UNSUP
+        # supported combinations with nothing to do
+        for g in (64, 128, 256):
+            assert q(h128, 0, g, None, 1, 0, 512, None, None, None, None) == OK
+        assert p(h128, 256, None, 0, 0, 4, 1, None, None, None) == OK
+    finally:
+        for h in (h128, h512, h384):
+            lib.rw4_transform_destroy(h)
+
+
+def test_group_size_validation_gemm_and_dequantize():
+    gm, dq = lib.rw4_w4a4_gemm_g, lib.rw4_dequantize_g
+    assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 512, 96, FAKE, 0, 4, None) == ARG
+    assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 384, 256, FAKE, 0, 4, None) == SHAPE
+    assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 512, 64, FAKE, 0, 4, None) == UNSUP
+    assert gm(None, None, None, None, 0, 4, 512, 256, None, 0, 4, None) == OK
+    assert dq(FAKE, FAKE, 4, 512, 96, FAKE, 0, 512, None) == ARG
+    assert dq(FAKE, FAKE, 4, 384, 256, FAKE, 0, 384, None) == SHAPE
+    assert dq(FAKE, FAKE, 4, 192, 128, FAKE, 0, 192, None) == SHAPE
+    assert dq(None, None, 0, 192, 64, None, 0, 192, None) == OK
+    # the unsuffixed calls are the 128-group ones
+    assert lib.rw4_dequantize(FAKE, FAKE, 4, 192, FAKE, 0, 192, None) == SHAPE

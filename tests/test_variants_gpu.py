@@ -131,3 +131,78 @@ def test_givens_layer_counts(layers):
     t, xd, qa, sa, aref = tp._quant_parity(wl)
     qw, sw, wref = tp._weight_parity(wl, t)
     tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+# ---------------------------------------------------------------------------
+# Quantization group sizes 64 and 256 (block-128 Hadamard)
+# ---------------------------------------------------------------------------
+
+def _group_quant_parity(x64, xdt, K, group, signs=None):
+    spec = {"kind": "hadamard", "block": 128}
+    if signs is not None:
+        spec["signs"] = signs
+    t = rw4.Transform.hadamard(K, 128, signs=signs)
+    x = gu.x_to_device(x64, xdt)
+    qa, sa = rw4.quantize_act(t, x, "group128", group=group)
+    ref = oracle.quantize_act(x64, spec, "group128", group)
+    tp._check_quant(tp._unpack(qa), gu.to_np(sa), ref["codes"], ref["ratio"], ref["sa"], f"act g{group}")
+    return t, spec, qa, sa, ref
+
+
+@pytest.mark.parametrize("M", [300, 7])
+@pytest.mark.parametrize("signed", [False, True])
+def test_group256_end_to_end(M, signed):
+    K, N = 1024, 200
+    rng = np.random.default_rng(31 + M)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    signs = datagen.random_signs(5, K) if signed else None
+    t, spec, qa, sa, aref = _group_quant_parity(x, "bf16", K, 256, signs)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(w).to(gu.DEV), "kn", group=256)
+    wref = oracle.pack_weight(w, spec, 256)
+    tp._check_quant(tp._unpack(qw), gu.to_np(sw), wref["codes"], wref["ratio"], wref["sw"], "weight g256")
+    assert sa.shape == (M, K // 256) and sw.shape == (N, K // 256)
+    wl = datagen.Workload(f"g256_m{M}", M, K, N, x, "bf16", w, ("hadamard", 128), "group128", "f32")
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+@pytest.mark.parametrize("M", [300, 9])
+def test_group256_accumulators_exact(M):
+    """Group isolation at g = 256: sa = 1 and sw one-hot in group j give
+    Y = acc[:, :, j] exactly (integers up to 256 * 49, exact in fp32)."""
+    K, N = 1024, 144
+    rng = np.random.default_rng(40 + M)
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[0, :256], cw[0, :256] = 7, 7          # the extreme accumulator 256 * 49
+    ca[1, 256:512], cw[0, 256:512] = -7, 7   # and its negative
+    qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
+    qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
+    acc = oracle.group_accumulators(ca, cw, 256)
+    sa = torch.ones((M, K // 256), dtype=torch.float32, device=gu.DEV)
+    for j in range(K // 256):
+        swn = np.zeros((N, K // 256), dtype=np.float32)
+        swn[:, j] = 1.0
+        y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
+        assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"group {j}"
+
+
+def test_group64_quantize_dequantize():
+    """A 64-group INT4 KV cache: quantize_act at g = 64, read back exactly."""
+    M, K = 257, 1024
+    rng = np.random.default_rng(50)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    t, spec, qa, sa, ref = _group_quant_parity(x, "bf16", K, 64)
+    assert sa.shape == (M, K // 64)
+    y = gu.to_np(rw4.dequantize(qa, sa, torch.float32))
+    exact = oracle.round_dequant_output(oracle.dequantize(tp._unpack(qa), gu.to_np(sa), 64), "f32")
+    assert np.array_equal(y, exact)
+    step = np.repeat(ref["sa"], 64, axis=1)
+    assert np.all(np.abs(y - ref["xt"]) <= step / 2 * (1 + 1e-2) + np.abs(ref["xt"]) * 2 ** -20)
+
+
+def test_group64_fp32_ragged_groups():
+    M, K = 33, 384                      # 6 groups of 64, a ragged quad of 128-blocks
+    rng = np.random.default_rng(51)
+    x = datagen.outlier_activations(rng, M, K).astype(np.float32).astype(np.float64)
+    _group_quant_parity(x, "f32", K, 64)
