@@ -125,6 +125,15 @@ rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_
                                 const float* theta_host, const float* beta_host, void* stream,
                                 rw4_transform** out);
 
+/* The same transform with the angles stored in half precision (the
+ * independent-rotation article keeps its trained angles in fp16): theta_f16
+ * holds IEEE binary16 bit patterns, [K/128][layers][64]; every value is
+ * widened exactly and must be finite (ARG otherwise).  Equivalent to
+ * rw4_transform_givens with theta = the widened values. */
+rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pairs_host,
+                                    const uint16_t* theta_f16_host, const float* beta_host, void* stream,
+                                    rw4_transform** out);
+
 /* Frees the transform and its device tables.  The caller guarantees no
  * enqueued work still uses it.  NULL is a no-op. */
 rw4_status rw4_transform_destroy(rw4_transform* t);

@@ -32,6 +32,7 @@ MODES = {"group128": 0, "rrs": 1}
 
 EXPORTED_SYMBOLS = (
     "rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
+    "rw4_transform_givens_f16",
     "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
     "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_status_str", "rw4_version",
@@ -62,6 +63,7 @@ lib.rw4_version.restype = ctypes.c_char_p
 lib.rw4_transform_hadamard.argtypes = [_i64, _i32, _p, ctypes.POINTER(_p)]
 lib.rw4_transform_hadamard_signed.argtypes = [_i64, _i32, _p, _p, ctypes.POINTER(_p)]
 lib.rw4_transform_givens.argtypes = [_i64, _i32, _p, _p, _p, _p, ctypes.POINTER(_p)]
+lib.rw4_transform_givens_f16.argtypes = [_i64, _i32, _p, _p, _p, _p, ctypes.POINTER(_p)]
 lib.rw4_transform_destroy.argtypes = [_p]
 lib.rw4_transform_k.argtypes = [_p]
 lib.rw4_transform_k.restype = _i64
@@ -151,19 +153,24 @@ class Transform:
 
     @classmethod
     def givens(cls, K: int, pairs, theta, beta, stream=None) -> "Transform":
-        """pairs uint8 [K/128, L, 64, 2] (0xFF = empty), theta fp32 [K/128, L, 64], beta fp32 [K]."""
+        """pairs uint8 [K/128, L, 64, 2] (0xFF = empty), theta [K/128, L, 64], beta fp32 [K].
+
+        theta as float16 uses the half-precision angle entry point; anything
+        else is converted to float32."""
         pairs = np.ascontiguousarray(pairs, dtype=np.uint8)
-        theta = np.ascontiguousarray(theta, dtype=np.float32)
+        half = np.asarray(theta).dtype == np.float16
+        theta = np.ascontiguousarray(theta, dtype=np.float16 if half else np.float32)
         beta = np.ascontiguousarray(beta, dtype=np.float32)
         G = int(K) // 128
         L = pairs.shape[1]
         if pairs.shape != (G, L, 64, 2) or theta.shape != (G, L, 64) or beta.shape != (int(K),):
             raise ValueError("pairs/theta/beta shapes do not match K")
         h = ctypes.c_void_p()
-        _check(lib.rw4_transform_givens(int(K), int(L), pairs.ctypes.data, theta.ctypes.data,
-                                        beta.ctypes.data, stream, ctypes.byref(h)),
+        fn = lib.rw4_transform_givens_f16 if half else lib.rw4_transform_givens
+        _check(fn(int(K), int(L), pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, stream,
+                  ctypes.byref(h)),
                "rw4_transform_givens")
-        return cls(h, int(K), f"givens{L}")
+        return cls(h, int(K), f"givens{L}" + ("_f16" if half else ""))
 
     def close(self):
         if self._h is not None and self._h.value:

@@ -177,6 +177,44 @@ rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_
   return RW4_OK;
 }
 
+// IEEE binary16 bits to float (exact: every half value is a float).
+static float half_bits_to_float(uint16_t h) {
+  const uint32_t sign = uint32_t(h >> 15) << 31;
+  const uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  uint32_t bits;
+  if (e == 0x1F) {
+    bits = sign | 0x7F800000u | (m << 13);  // inf / nan
+  } else if (e != 0) {
+    bits = sign | ((e + 112) << 23) | (m << 13);
+  } else if (m == 0) {
+    bits = sign;
+  } else {  // subnormal half: m * 2^-24
+    float f = float(m) * 0x1p-24f;
+    std::memcpy(&bits, &f, 4);
+    bits |= sign;
+  }
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pairs_host,
+                                    const uint16_t* theta_f16_host, const float* beta_host, void* stream,
+                                    rw4_transform** out) {
+  if (!out) return RW4_ERR_ARG;
+  *out = nullptr;
+  if (!theta_f16_host) return RW4_ERR_ARG;
+  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (layers < 1 || layers > 64) return RW4_ERR_SHAPE;
+  const size_t n = size_t(K / kGroup) * layers * kSlots;
+  std::vector<float> theta(n);
+  for (size_t i = 0; i < n; ++i) {
+    theta[i] = half_bits_to_float(theta_f16_host[i]);
+    if (!std::isfinite(theta[i])) return RW4_ERR_ARG;
+  }
+  return rw4_transform_givens(K, layers, pairs_host, theta.data(), beta_host, stream, out);
+}
+
 rw4_status rw4_transform_destroy(rw4_transform* t) {
   if (!t) return RW4_OK;
   hipError_t e = hipSuccess;

@@ -246,3 +246,19 @@ def test_group_size_validation_gemm_and_dequantize():
     assert dq(None, None, 0, 192, 64, None, 0, 192, None) == OK
     # the unsuffixed calls are the 128-group ones
     assert lib.rw4_dequantize(FAKE, FAKE, 4, 192, FAKE, 0, 192, None) == SHAPE
+
+
+def test_givens_f16_validation():
+    h = ctypes.c_void_p()
+    g = lib.rw4_transform_givens_f16
+    assert g(100, 8, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
+    assert g(128, 0, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
+    assert g(128, 8, FAKE, None, FAKE, None, ctypes.byref(h)) == ARG
+    assert g(128, 8, FAKE, FAKE, FAKE, None, None) == ARG
+    # a non-finite half angle is rejected before anything is uploaded
+    theta = np.zeros((1, 1, 64), dtype=np.float16)
+    theta[0, 0, 3] = np.inf
+    pairs = np.full((1, 1, 64, 2), 0xFF, dtype=np.uint8)
+    beta = np.zeros(128, dtype=np.float32)
+    assert g(128, 1, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, None, ctypes.byref(h)) == ARG
+    assert not h.value

@@ -206,3 +206,27 @@ def test_group64_fp32_ragged_groups():
     rng = np.random.default_rng(51)
     x = datagen.outlier_activations(rng, M, K).astype(np.float32).astype(np.float64)
     _group_quant_parity(x, "f32", K, 64)
+
+
+def test_givens_fp16_angles():
+    """Angles stored in half precision: the same transform as the fp32 entry
+    point given the widened angles (identical codes), and oracle parity with
+    the half-precision angles."""
+    M, K, N = 40, 512, 48
+    rng = np.random.default_rng(60)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    pairs, theta, beta = datagen.givens_plan(13, K, layers=8)
+    th16 = theta.astype(np.float16)
+    t16 = rw4.Transform.givens(K, pairs, th16, beta)
+    t32 = rw4.Transform.givens(K, pairs, th16.astype(np.float32), beta)
+    xd = gu.x_to_device(x, "bf16")
+    q16, s16 = rw4.quantize_act(t16, xd)
+    q32, s32 = rw4.quantize_act(t32, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q16, q32) and torch.equal(s16, s32)
+    wl = datagen.Workload("givens_f16", M, K, N, x, "bf16", w, ("givens", 8), "group128", "f32",
+                          pairs=pairs, theta=th16, beta=beta)
+    t, _, qa, sa, aref = tp._quant_parity(wl)
+    qw, sw, wref = tp._weight_parity(wl, t)
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
