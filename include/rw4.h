@@ -134,6 +134,11 @@ rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pa
                                     const uint16_t* theta_f16_host, const float* beta_host, void* stream,
                                     rw4_transform** out);
 
+/* Transforms with device tables (signed Hadamard, Givens) accept K up to
+ * 2^24 (RW4_ERR_SHAPE above) and must be used while the device that was
+ * current at their creation is current (RW4_ERR_ARG otherwise); a host
+ * allocation failure while building the tables is RW4_ERR_NOMEM. */
+
 /* Frees the transform and its device tables.  The caller guarantees no
  * enqueued work still uses it.  NULL is a no-op. */
 rw4_status rw4_transform_destroy(rw4_transform* t);

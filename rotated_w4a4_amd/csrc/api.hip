@@ -30,6 +30,18 @@ rw4_status from_hip(hipError_t e) {
   return RW4_ERR_HIP;
 }
 
+// Host tables beyond this many channels are refused (no GEMM takes K above
+// 2^24 either), so the host staging vectors stay bounded.
+constexpr int64_t kMaxK = int64_t(1) << 24;
+
+// A transform with device tables must be used on the device it was created on.
+bool on_home_device(const rw4_transform* t) {
+  const bool tables = t->dev.lut_idx || t->dev.sign_mask;
+  if (!tables) return true;
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == t->device;
+}
+
 }  // namespace
 
 extern "C" {
@@ -38,7 +50,7 @@ const char* rw4_status_str(rw4_status s) {
   switch (s) {
     case RW4_OK: return "RW4_OK";
     case RW4_ERR_ARG: return "RW4_ERR_ARG: invalid argument (null, unknown enum, misaligned, or bad table)";
-    case RW4_ERR_SHAPE: return "RW4_ERR_SHAPE: invalid shape (K % 128, K mismatch, block, layers)";
+    case RW4_ERR_SHAPE: return "RW4_ERR_SHAPE: invalid shape (K % 128, group does not divide K, block, layers)";
     case RW4_ERR_UNSUPPORTED: return "RW4_ERR_UNSUPPORTED: valid but unimplemented combination";
     case RW4_ERR_HIP: return "RW4_ERR_HIP: HIP runtime call or kernel launch failed";
     case RW4_ERR_NOMEM: return "RW4_ERR_NOMEM: device allocation failed";
@@ -65,12 +77,12 @@ rw4_status rw4_transform_hadamard(int64_t K, int32_t block, void* stream, rw4_tr
   return RW4_OK;
 }
 
-rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t* signs_host,
+static rw4_status transform_hadamard_signed_impl(int64_t K, int32_t block, const int8_t* signs_host,
                                         void* stream, rw4_transform** out) {
   if (!out) return RW4_ERR_ARG;
   *out = nullptr;
   if (!signs_host) return RW4_ERR_ARG;
-  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (K <= 0 || K % kGroup || K > kMaxK) return RW4_ERR_SHAPE;
   if (!pow2(block) || block < 128 || block > K || K % block) return RW4_ERR_SHAPE;
   if (block > 128 && !rw4::rowh_supported(K)) return RW4_ERR_UNSUPPORTED;
   std::vector<uint32_t> mask(K);
@@ -98,13 +110,22 @@ rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t*
   return RW4_OK;
 }
 
-rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_host,
+rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t* signs_host,
+                                        void* stream, rw4_transform** out) {
+  try {  // host staging vectors: no exception may cross the C ABI
+    return transform_hadamard_signed_impl(K, block, signs_host, stream, out);
+  } catch (...) {
+    return RW4_ERR_NOMEM;
+  }
+}
+
+static rw4_status transform_givens_impl(int64_t K, int32_t layers, const uint8_t* pairs_host,
                                 const float* theta_host, const float* beta_host, void* stream,
                                 rw4_transform** out) {
   if (!out) return RW4_ERR_ARG;
   *out = nullptr;
   if (!pairs_host || !theta_host || !beta_host) return RW4_ERR_ARG;
-  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (K <= 0 || K % kGroup || K > kMaxK) return RW4_ERR_SHAPE;
   if (layers < 1 || layers > 64) return RW4_ERR_SHAPE;
   const int64_t G = K / kGroup;
   const size_t n_slots = size_t(G) * layers * kSlots;
@@ -177,6 +198,16 @@ rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_
   return RW4_OK;
 }
 
+rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_host,
+                                const float* theta_host, const float* beta_host, void* stream,
+                                rw4_transform** out) {
+  try {  // host staging vectors: no exception may cross the C ABI
+    return transform_givens_impl(K, layers, pairs_host, theta_host, beta_host, stream, out);
+  } catch (...) {
+    return RW4_ERR_NOMEM;
+  }
+}
+
 // IEEE binary16 bits to float (exact: every half value is a float).
 static float half_bits_to_float(uint16_t h) {
   const uint32_t sign = uint32_t(h >> 15) << 31;
@@ -198,13 +229,13 @@ static float half_bits_to_float(uint16_t h) {
   return f;
 }
 
-rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pairs_host,
+static rw4_status transform_givens_f16_impl(int64_t K, int32_t layers, const uint8_t* pairs_host,
                                     const uint16_t* theta_f16_host, const float* beta_host, void* stream,
                                     rw4_transform** out) {
   if (!out) return RW4_ERR_ARG;
   *out = nullptr;
   if (!theta_f16_host) return RW4_ERR_ARG;
-  if (K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (K <= 0 || K % kGroup || K > kMaxK) return RW4_ERR_SHAPE;
   if (layers < 1 || layers > 64) return RW4_ERR_SHAPE;
   const size_t n = size_t(K / kGroup) * layers * kSlots;
   std::vector<float> theta(n);
@@ -213,6 +244,16 @@ rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pa
     if (!std::isfinite(theta[i])) return RW4_ERR_ARG;
   }
   return rw4_transform_givens(K, layers, pairs_host, theta.data(), beta_host, stream, out);
+}
+
+rw4_status rw4_transform_givens_f16(int64_t K, int32_t layers, const uint8_t* pairs_host,
+                                    const uint16_t* theta_f16_host, const float* beta_host, void* stream,
+                                    rw4_transform** out) {
+  try {  // host staging vectors: no exception may cross the C ABI
+    return transform_givens_f16_impl(K, layers, pairs_host, theta_f16_host, beta_host, stream, out);
+  } catch (...) {
+    return RW4_ERR_NOMEM;
+  }
 }
 
 rw4_status rw4_transform_destroy(rw4_transform* t) {
@@ -246,6 +287,7 @@ rw4_status rw4_quantize_act_g(const rw4_transform* t, rw4_act_mode mode, int32_t
     return RW4_ERR_UNSUPPORTED;
   if (group != 128 && (rrs || t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
     return RW4_ERR_UNSUPPORTED;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
   if (M == 0) return RW4_OK;
   if (!x || !qa || !sa) return RW4_ERR_ARG;
   if (rrs && !workspace) return RW4_ERR_ARG;
@@ -276,6 +318,7 @@ rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* 
   if (group == 64) return RW4_ERR_UNSUPPORTED;
   if (group == 256 && (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
     return RW4_ERR_UNSUPPORTED;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
   if (N == 0) return RW4_OK;
   if (!w || !qw || !sw) return RW4_ERR_ARG;
   if (stride_k <= 0 || stride_n <= 0) return RW4_ERR_ARG;

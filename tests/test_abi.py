@@ -262,3 +262,12 @@ def test_givens_f16_validation():
     beta = np.zeros(128, dtype=np.float32)
     assert g(128, 1, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, None, ctypes.byref(h)) == ARG
     assert not h.value
+
+
+def test_table_transforms_bound_k():
+    h = ctypes.c_void_p()
+    big = 1 << 25
+    assert lib.rw4_transform_hadamard_signed(big, 128, FAKE, None, ctypes.byref(h)) == SHAPE
+    assert lib.rw4_transform_givens(big, 8, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
+    assert lib.rw4_transform_givens_f16(big, 8, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
+    assert not h.value
