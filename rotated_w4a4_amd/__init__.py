@@ -75,10 +75,9 @@ lib.rw4_quantize_act_g.argtypes = [_p, ctypes.c_int, _i32, _p, ctypes.c_int, _i6
 lib.rw4_pack_weight_g.argtypes = [_p, _i32, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_w4a4_gemm_g.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 lib.rw4_dequantize_g.argtypes = [_p, _p, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
-for _name in ("rw4_transform_hadamard", "rw4_transform_hadamard_signed", "rw4_transform_givens",
-              "rw4_transform_destroy", "rw4_quantize_act", "rw4_pack_weight", "rw4_dequantize",
-              "rw4_w4a4_gemm"):
-    getattr(lib, _name).restype = ctypes.c_int
+for _name in EXPORTED_SYMBOLS:
+    if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k"):
+        getattr(lib, _name).restype = ctypes.c_int
 
 
 class RW4Error(RuntimeError):
@@ -121,6 +120,21 @@ def _dtype_code(t) -> int:
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _on_gpu(name, t, device=None):
+    """A tensor the kernels will touch: on a GPU (the same one as `device`)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _out(name, t, shape, dtype, device):
+    """A caller-provided output: exact shape and dtype, contiguous, same GPU."""
+    _on_gpu(name, t, device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
 class Transform:
@@ -195,14 +209,27 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride along K")
+    _on_gpu("x", x)
     M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}")
+    if group not in (64, 128, 256) or K % group:
+        raise ValueError("group must be 64, 128 or 256 and divide K")
     G = K // 128
     if qa is None:
         qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     if sa is None:
         sa = torch.empty((M, K // group), dtype=torch.float32, device=x.device)
-    if mode == "rrs" and workspace is None:
-        workspace = torch.empty((max(G, 4),), dtype=torch.float32, device=x.device)
+    _out("qa", qa, (M, K // 2), torch.uint8, x.device)
+    _out("sa", sa, (M, K // group), torch.float32, x.device)
+    if mode == "rrs":
+        if workspace is None:
+            workspace = torch.empty((max(G, 4),), dtype=torch.float32, device=x.device)
+        _on_gpu("workspace", workspace, x.device)
+        if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() < G:
+            raise ValueError(f"workspace must be a contiguous float32 tensor of at least {G} elements")
     _check(lib.rw4_quantize_act_g(t.handle, MODES[mode], group, _ptr(x), _dtype_code(x), M, x.stride(0),
                                   _ptr(qa), _ptr(sa), _ptr(workspace), _stream(x.device)),
            "rw4_quantize_act")
@@ -217,6 +244,7 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: in
     torch = _torch()
     if w.dim() != 2:
         raise ValueError("w must be 2-D")
+    _on_gpu("w", w)
     if layout == "kn":
         K, N = w.shape
         sk, sn = w.stride(0), w.stride(1)
@@ -225,10 +253,16 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: in
         sn, sk = w.stride(0), w.stride(1)
     else:
         raise ValueError(layout)
+    if K != t.K:
+        raise ValueError(f"w has {K} input channels, the transform {t.K}")
+    if group not in (64, 128, 256) or K % group:
+        raise ValueError("group must be 64, 128 or 256 and divide K")
     if qw is None:
         qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
     if sw is None:
         sw = torch.empty((N, K // group), dtype=torch.float32, device=w.device)
+    _out("qw", qw, (N, K // 2), torch.uint8, w.device)
+    _out("sw", sw, (N, K // group), torch.float32, w.device)
     _check(lib.rw4_pack_weight_g(t.handle, group, _ptr(w), _dtype_code(w), N, sk, sn, _ptr(qw), _ptr(sw),
                                  _stream(w.device)),
            "rw4_pack_weight")
@@ -253,12 +287,17 @@ def dequantize(q, s, out_dtype=None, out=None):
     if s.dim() != 2 or s.shape[0] != M:
         raise ValueError("scale shape does not match the codes")
     group = _group_of(K, s.shape[1])
+    _on_gpu("q", q)
+    _on_gpu("s", s, q.device)
+    if q.dtype != torch.uint8 or s.dtype != torch.float32:
+        raise ValueError("q must be uint8 and s float32")
     if not (q.is_contiguous() and s.is_contiguous()):
         raise ValueError("q and s must be contiguous")
     if out is None:
         out = torch.empty((M, K), dtype=out_dtype, device=q.device)
-    if out.stride(1) != 1:
-        raise ValueError("out must have unit stride along K")
+    _on_gpu("out", out, q.device)
+    if out.dim() != 2 or tuple(out.shape) != (M, K) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
     _check(lib.rw4_dequantize_g(_ptr(q), _ptr(s), M, K, group, _ptr(out), _dtype_code(out), out.stride(0),
                                 _stream(q.device)),
            "rw4_dequantize")
@@ -278,13 +317,16 @@ def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
     if qw.shape[1] != Kh or sa.dim() != 2 or sa.shape[0] != M or sw.shape != (N, sa.shape[1]):
         raise ValueError("operand shapes do not match")
     group = _group_of(K, sa.shape[1])
+    for name, tns, dt in (("qa", qa, torch.uint8), ("sa", sa, torch.float32), ("qw", qw, torch.uint8),
+                          ("sw", sw, torch.float32)):
+        _on_gpu(name, tns, qa.device)
+        if tns.dtype != dt or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
-    if out.stride(1) != 1:
-        raise ValueError("out must have unit stride along N")
-    for tns in (qa, sa, qw, sw):
-        if not tns.is_contiguous():
-            raise ValueError("qa/sa/qw/sw must be contiguous")
+    _on_gpu("out", out, qa.device)
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
     _check(lib.rw4_w4a4_gemm_g(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, group, _ptr(out),
                                _dtype_code(out), out.stride(0), _stream(qa.device)),
            "rw4_w4a4_gemm")

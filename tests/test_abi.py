@@ -271,3 +271,22 @@ def test_table_transforms_bound_k():
     assert lib.rw4_transform_givens(big, 8, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
     assert lib.rw4_transform_givens_f16(big, 8, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == SHAPE
     assert not h.value
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor's address must never reach a kernel: every compute call
+    of the binding refuses non-GPU tensors before calling the library."""
+    torch = pytest.importorskip("torch")
+    t = rw4.Transform.hadamard(256, 128)
+    x = torch.zeros((4, 256), dtype=torch.float32)
+    q = torch.zeros((4, 128), dtype=torch.uint8)
+    s = torch.zeros((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        rw4.quantize_act(t, x)
+    with pytest.raises(ValueError, match="GPU"):
+        rw4.pack_weight(t, x.t())
+    with pytest.raises(ValueError, match="GPU"):
+        rw4.dequantize(q, s, torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        rw4.w4a4_gemm(q, s, q, s, torch.float32)
+    t.close()
