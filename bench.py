@@ -101,8 +101,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny"])
-    ap.add_argument("--group", type=int, default=128, choices=[128, 256],
-                    help="quantization group size (block-128 Hadamard workloads for 256)")
+    ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
+                    help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -218,7 +218,7 @@ def main():
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group
     if grp != 128 and not (wl.transform == ("hadamard", 128) and wl.mode == "group128"):
-        raise SystemExit("--group 256 needs a block-128 Hadamard workload in per-group mode")
+        raise SystemExit("--group 64/256 needs a block-128 Hadamard workload in per-group mode")
     G = K // grp
     log(f"workload {wl.name} M={M} K={K} N={N} transform={wl.transform} mode={wl.mode} "
         f"device={torch.cuda.get_device_name(dev)}")

@@ -201,13 +201,17 @@ rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, 
  * (RW4_ERR_UNSUPPORTED otherwise):
  *   quantize_act_g  64 and 256 with a block-128 Hadamard transform (plain or
  *                   signed) in RW4_ACT_GROUP128 mode (per-group scales);
- *   pack_weight_g   256 with a block-128 Hadamard transform;
- *   w4a4_gemm_g     256 (the two 128-wide halves of a group accumulate into
- *                   one exact integer sum, |sum| <= 256 * 49, before the
- *                   rescale); 64 is not supported by the GEMM;
+ *   pack_weight_g   64 and 256 with a block-128 Hadamard transform;
+ *   w4a4_gemm_g     64 (each 64-wide K-half is rescaled on its own; the
+ *                   64-group kernel for M > 16 needs 96 KiB of LDS, one
+ *                   block per CU) and 256 (the two 128-wide halves of a
+ *                   group accumulate into one exact integer sum,
+ *                   |sum| <= 256 * 49, before the rescale); K stays a
+ *                   multiple of 128;
  *   dequantize_g    64 and 256.
- * A 64-group INT4 KV cache is written with quantize_act_g and read with
- * dequantize_g. */
+ * The independent-rotation article gives outlier-heavy layers the smaller
+ * group (64).  A 64-group INT4 KV cache is written with quantize_act_g and
+ * read with dequantize_g. */
 rw4_status rw4_quantize_act_g(const rw4_transform* t, rw4_act_mode mode, int32_t group, const void* x,
                               rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
                               float* workspace, void* stream);

@@ -314,9 +314,8 @@ rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* 
   if (!group_known(group)) return RW4_ERR_ARG;
   if (N < 0) return RW4_ERR_SHAPE;
   if (t->dev.K % group) return RW4_ERR_SHAPE;
-  // the GEMM consumes 128- and 256-wide groups; 256 for the block-128 Hadamard
-  if (group == 64) return RW4_ERR_UNSUPPORTED;
-  if (group == 256 && (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
+  // groups other than 128 with the block-128 Hadamard
+  if (group != 128 && (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128))
     return RW4_ERR_UNSUPPORTED;
   if (!on_home_device(t)) return RW4_ERR_ARG;
   if (N == 0) return RW4_OK;
@@ -360,7 +359,6 @@ rw4_status rw4_w4a4_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw
   if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
   if (!group_known(group)) return RW4_ERR_ARG;
   if (M < 0 || N < 0 || K <= 0 || K % kGroup || K % group || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
-  if (group == 64) return RW4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return RW4_OK;
   if (!qa || !sa || !qw || !sw || !y) return RW4_ERR_ARG;
   if (ldy < N) return RW4_ERR_ARG;

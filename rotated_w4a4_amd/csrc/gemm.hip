@@ -147,14 +147,18 @@ constexpr int kTileBytes = 128 * 64;               // one operand of one group
 constexpr int kGroupBytes = 2 * kTileBytes;        // A and B
 constexpr int kStageBytes = 2 * kGroupBytes;       // two groups
 constexpr int kSplitGroupBytes = 256 * 16;         // 128 row + 128 column operands
+// NSPLIT split buffers: one per group buffer, or two (one per 64-wide
+// half) for 64-wide scale groups.
+template <int NSPLIT>
 struct alignas(16) GemmSmem {
   uint8_t tile[2 * kStageBytes];
-  uint8_t split[4 * kSplitGroupBytes];
+  uint8_t split[NSPLIT * kSplitGroupBytes];
 };
-static_assert(2 * kStageBytes <= 65536 && 4 * kSplitGroupBytes <= 65536, "ds offsets are 16-bit");
+static_assert(2 * kStageBytes <= 65536 && 8 * kSplitGroupBytes <= 65536, "ds offsets are 16-bit");
 // group buffer q (0..3: stage q / 2, slot q % 2)
 constexpr int tile_off(int q) { return q * kGroupBytes; }
 constexpr int split_off(int q) { return q * kSplitGroupBytes; }
+constexpr int split_off64(int q, int h) { return (2 * q + h) * kSplitGroupBytes; }
 
 // LDS reads of one group for a wave, in two batches that each wait for
 // their own results (the compiler cannot see these reads, so it adds no
@@ -218,25 +222,29 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t nb, int64_t til
   nt = li / gm;
 }
 
-// G256: scales per 256-wide group (the two 128-groups of a stage share one
-// scale pair): the accumulator runs over both groups of the stage (partial
-// sums below 256 * 49 < 2^24, still exact) and the scale products and the
-// epilogue run once per stage.
-template <bool BF16, bool G256>
+// GSZ: scale group width.  128: one scale pair per group buffer.  256: the
+// two 128-groups of a stage share one scale pair; the accumulator runs over
+// both (partial sums below 256 * 49 < 2^24, still exact) and the scale
+// products and the epilogue run once per stage.  64: each K-half of a
+// group has its own scale pair, so each K-half ends with the scale products
+// and the epilogue; the split buffers double (96 KiB of LDS: one block per
+// CU).
+template <bool BF16, int GSZ>
 __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restrict__ qa,
                                                          const float* __restrict__ sa,
                                                          const uint8_t* __restrict__ qw,
                                                          const float* __restrict__ sw, int64_t M,
                                                          int64_t N, int64_t K, void* __restrict__ y,
                                                          int64_t ldy, int64_t tiles_m) {
-  __shared__ GemmSmem sm;
+  constexpr bool G256 = GSZ == 256, G64 = GSZ == 64;
+  __shared__ GemmSmem<G64 ? 8 : 4> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t G = K / kGroup;
-  const int64_t GS = G256 ? G / 2 : G;  // scale columns
+  const int64_t GS = G256 ? G / 2 : G64 ? 2 * G : G;  // scale columns
   const int64_t rowbytes = K / 2;
   int64_t mt, nt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, mt, nt);
@@ -292,6 +300,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
     const uint4 o = split_operand(x, sel);
     lds_write_split<split_off(q)>(sp_addr, v4u{o.x, o.y, o.z, o.w});
   };
+  auto put_split64 = [&](auto q_const, float x0, float x1) {  // the two halves of group buffer q
+    constexpr int q = decltype(q_const)::value;
+    const uint4 o0 = split_operand(x0, sel), o1 = split_operand(x1, sel);
+    lds_write_split<split_off64(q, 0)>(sp_addr, v4u{o0.x, o0.y, o0.z, o0.w});
+    lds_write_split<split_off64(q, 1)>(sp_addr, v4u{o1.x, o1.y, o1.z, o1.w});
+  };
 
   // per-lane LDS read bases (group buffer 0).  Lanes 32..63 supply K slots
   // 8..15 of the bf16 scale-product MFMA: their row operands are zeroed in
@@ -302,10 +316,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
     const uint32_t t0 = lds_off(sm.tile), s0 = lds_off(sm.split);
     const int ra_ = wm * 64 + frow, rb_ = wn * 64 + frow;
     const int xa = (ra_ >> 2) & 3, xb = (rb_ >> 2) & 3;
-    ba0 = t0 + ra_ * 64 + (((2 * h) ^ xa) * 16);
-    ba1 = t0 + ra_ * 64 + (((2 * h + 1) ^ xa) * 16);
-    bb0 = t0 + rb_ * 64 + (((2 * h) ^ xb) * 16);
-    bb1 = t0 + rb_ * 64 + (((2 * h + 1) ^ xb) * 16);
+    // 16-byte slot (32 codes) of K-half ks for lane half h: the MFMA takes
+    // K 0-31 from lanes 0-31 and K 32-63 from lanes 32-63.  With 64-wide
+    // scale groups each K-half must be one 64-group (slots 2 ks, 2 ks + 1);
+    // otherwise any split works and slot 2 h + ks is used.
+    const int s0_ = G64 ? h : 2 * h, s1_ = G64 ? 2 + h : 2 * h + 1;
+    ba0 = t0 + ra_ * 64 + ((s0_ ^ xa) * 16);
+    ba1 = t0 + ra_ * 64 + ((s1_ ^ xa) * 16);
+    bb0 = t0 + rb_ * 64 + ((s0_ ^ xb) * 16);
+    bb1 = t0 + rb_ * 64 + ((s1_ ^ xb) * 16);
     bsa = s0 + (wm * 64 + frow) * 16;
     bsb = s0 + (wn * 64 + frow) * 16;  // + 2048 (column operands) in the read offsets
   }
@@ -319,10 +338,43 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
 
+  // Scale products of the four 32 x 32 tiles from the split operands ps
+  // (rows, rows, columns, columns), then y += acc * p.
+  v16f acc[2][2];
+  auto epilogue = [&](v4u (&ps)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
+    // tile by tile, one tile ahead of the accumulation (the scheduling
+    // barriers keep at most two product tiles live)
+    auto prod = [&](int t) {
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ps[t >> 1]),
+                                                     __builtin_bit_cast(v8bf, ps[2 + (t & 1)]), v16f{}, 0,
+                                                     0, 0);
+    };
+    auto accum = [&](int t, const v16f& p) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        yacc[t >> 1][t & 1][r] = fmaf(acc[t >> 1][t & 1][r], p[r], yacc[t >> 1][t & 1][r]);
+    };
+    v16f p0 = prod(0);
+    v16f p1 = prod(1);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(0, p0);
+    p0 = prod(2);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(1, p1);
+    p1 = prod(3);
+    __builtin_amdgcn_sched_barrier(0);
+    accum(2, p0);
+    accum(3, p1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // One 128-group from group buffer q.  INIT: the accumulators start at
   // zero (else they continue); EPI: the scale products (split operands of
   // group buffer QS) and the epilogue follow.
-  v16f acc[2][2];
   auto compute = [&](auto q_const, auto qs_const, auto init_const, auto epi_const) {
     constexpr int q = decltype(q_const)::value;
     constexpr int qs = decltype(qs_const)::value;
@@ -354,35 +406,35 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
       // keep each half's unpack and MFMAs together (bounds register use)
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!epi) return;
+    if constexpr (epi) epilogue(ps);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One 128-group with 64-wide scale groups: each K-half reads its own
+  // splits and ends with its own epilogue.
+  auto compute64 = [&](auto q_const) {
+    constexpr int q = decltype(q_const)::value;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int ks = 0; ks < 2; ++ks) {
+      v4u fr[4], ps[4];
+      if (ks == 0)
+        lds_read_half1<tile_off(q), split_off64(q, 0)>(fr, ps, ba0, bb0, bsa, bsb);
+      else
+        lds_read_half1<tile_off(q), split_off64(q, 1)>(fr, ps, ba1, bb1, bsa, bsb);
+      v8i oa[2], ob[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
-    // scale products, tile by tile, one tile ahead of the accumulation (the
-    // scheduling barriers keep at most two product tiles live)
-    auto prod = [&](int t) {
-      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ps[t >> 1]),
-                                                     __builtin_bit_cast(v8bf, ps[2 + (t & 1)]), v16f{}, 0,
-                                                     0, 0);
-    };
-    auto accum = [&](int t, const v16f& p) {
+      for (int i = 0; i < 2; ++i) oa[i] = f8_operand(fr[i]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        yacc[t >> 1][t & 1][r] = fmaf(acc[t >> 1][t & 1][r], p[r], yacc[t >> 1][t & 1][r]);
-    };
-    v16f p0 = prod(0);
-    v16f p1 = prod(1);
-    __builtin_amdgcn_sched_barrier(0);
-    accum(0, p0);
-    p0 = prod(2);
-    __builtin_amdgcn_sched_barrier(0);
-    accum(1, p1);
-    p1 = prod(3);
-    __builtin_amdgcn_sched_barrier(0);
-    accum(2, p0);
-    accum(3, p1);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 2; ++j) ob[j] = f8_operand(fr[2 + j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], v16f{}, 0, 0, 0, kE8Scale, 0,
+                                                                     kE8Scale);
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue(ps);
+    }
   };
 
   // Stage s holds groups 2s and 2s + 1 in group buffers 2 (s % 2) and
@@ -401,6 +453,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   using F = std::false_type;
   if constexpr (G256) {
     put_split(Q0{}, sc_load(0));
+  } else if constexpr (G64) {
+    put_split64(Q0{}, sc_load(0), sc_load(1));
+    put_split64(Q1{}, sc_load(2), sc_load(3));
   } else {
     put_split(Q0{}, sc_load(0));
     put_split(Q1{}, sc_load(1));
@@ -417,6 +472,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
       compute(q0, q0, T{}, F{});
       compute(q1, q0, F{}, T{});
       put_split(n0_, x0);
+    } else if constexpr (G64) {
+      const float x0 = sc_load(4 * s + 4), x1 = sc_load(4 * s + 5);
+      const float x2 = sc_load(4 * s + 6), x3 = sc_load(4 * s + 7);
+      issue(decltype(n0_)::value, 2 * s + 2);
+      issue(decltype(n1_)::value, 2 * s + 3);
+      compute64(q0);
+      if (2 * s + 1 < G) compute64(q1);
+      put_split64(n0_, x0, x1);
+      put_split64(n1_, x2, x3);
     } else {
       const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
       issue(decltype(n0_)::value, 2 * s + 2);
@@ -492,22 +556,27 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 // MFMA covers a whole group.  Fragments come straight from global memory
 // (no reuse to stage); the partial results are summed across waves in LDS.
 // ---------------------------------------------------------------------------
-// G256: each scale column covers two consecutive 128-groups, whose two
-// MFMAs chain into one accumulator before the scale is applied.
+// GSZ 256: a scale column covers two consecutive 128-groups, whose two
+// MFMAs chain into one accumulator before the scale is applied.  GSZ 64: a
+// 128-group has two scale columns; its MFMA runs twice, each time with the
+// A fragments of the other 64-wide half zeroed (lanes 0-31 supply codes
+// 0-63 of the group, lanes 32-63 codes 64-127).
 constexpr int kSmallWaves = 8;
-template <bool BF16, bool G256>
+template <bool BF16, int GSZ>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint8_t* __restrict__ qa,
                                                                       const float* __restrict__ sa,
                                                                       const uint8_t* __restrict__ qw,
                                                                       const float* __restrict__ sw, int64_t M,
                                                                       int64_t N, int64_t K, void* __restrict__ y,
                                                                       int64_t ldy) {
-  constexpr int P = G256 ? 2 : 1;       // 128-groups per scale column
-  constexpr int NB = 4 / P;             // scale columns in flight per wave
+  constexpr int P = GSZ == 256 ? 2 : 1;  // 128-groups per unit (one scale column, or two for GSZ 64)
+  constexpr int H = GSZ == 64 ? 2 : 1;   // scale columns per unit
+  constexpr int NB = 4 / P;              // units in flight per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t GS = K / (kGroup * P);  // scale columns
+  const int64_t GU = K / (kGroup * P);  // units
+  const int64_t GS = GU * H;            // scale columns
   const int64_t rowbytes = K / 2;
   const int64_t n0 = int64_t(blockIdx.x) * 16;
   const int64_t am = lane & 15;               // A row supplied by this lane
@@ -516,37 +585,52 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
   const bool a_ok = am < M, b_ok = bn < N;
 
   float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t gb = wave; gb < GS; gb += kSmallWaves * NB) {
+  for (int64_t gb = wave; gb < GU; gb += kSmallWaves * NB) {
     v4u pa[NB][P], pb[NB][P];
-    float swv[NB], sav[NB][4];
+    float swv[NB][H], sav[NB][H][4];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + kSmallWaves * t;
-      const bool in = g < GS;
+      const bool in = g < GU;
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int64_t off = (g * P + p) * 64 + part * 16;
         pa[t][p] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
         pb[t][p] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
       }
-      swv[t] = (in && b_ok) ? sw[bn * GS + g] : 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = part * 4 + r;
-        sav[t][r] = (in && m < M) ? sa[m * GS + g] : 0.0f;
+      for (int h = 0; h < H; ++h) {
+        swv[t][h] = (in && b_ok) ? sw[bn * GS + g * H + h] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = part * 4 + r;
+          sav[t][h][r] = (in && m < M) ? sa[m * GS + g * H + h] : 0.0f;
+        }
       }
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + kSmallWaves * t;
-      if (g >= GS) break;
-      v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0]), f8_operand(pb[t][0]),
-                                                                 v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
-      if constexpr (G256)
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1]), f8_operand(pb[t][1]), acc,
-                                                               0, 0, 0, kE8Scale, 0, kE8Scale);
+      if (g >= GU) break;
+      if constexpr (GSZ == 64) {
+        const v8i a = f8_operand(pa[t][0]), b = f8_operand(pb[t][0]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][r] * swv[t], yv[r]);
+        for (int h = 0; h < 2; ++h) {
+          const v8i ah = (part >> 1) == h ? a : v8i{};
+          const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, v4f{}, 0, 0, 0, kE8Scale, 0,
+                                                                           kE8Scale);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][h][r] * swv[t][h], yv[r]);
+        }
+      } else {
+        v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0]), f8_operand(pb[t][0]),
+                                                                   v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+        if constexpr (P == 2)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1]), f8_operand(pb[t][1]), acc,
+                                                                 0, 0, 0, kE8Scale, 0, kE8Scale);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][0][r] * swv[t][0], yv[r]);
+      }
     }
   }
   __shared__ float red[kSmallWaves][64][4];
@@ -565,17 +649,17 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
   }
 }
 
-template <bool G256>
+template <int GSZ>
 hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                          hipStream_t st) {
   if (M <= 16) {
     const int64_t blocks = (N + 15) / 16;
     if (y_bf16)
-      hipLaunchKernelGGL((gemm_small_kernel<true, G256>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+      hipLaunchKernelGGL((gemm_small_kernel<true, GSZ>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
                          sa, qw, sw, M, N, K, y, ldy);
     else
-      hipLaunchKernelGGL((gemm_small_kernel<false, G256>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+      hipLaunchKernelGGL((gemm_small_kernel<false, GSZ>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
                          sa, qw, sw, M, N, K, y, ldy);
     return hipGetLastError();
   }
@@ -585,20 +669,21 @@ hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, 
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (y_bf16)
-    hipLaunchKernelGGL((gemm_f8_kernel<true, G256>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
+    hipLaunchKernelGGL((gemm_f8_kernel<true, GSZ>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
                        K, y, ldy, tiles_m);
   else
-    hipLaunchKernelGGL((gemm_f8_kernel<false, G256>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
+    hipLaunchKernelGGL((gemm_f8_kernel<false, GSZ>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
                        K, y, ldy, tiles_m);
   return hipGetLastError();
 }
 
-// group: 128 or 256 (K a multiple of it, checked by the caller)
+// group: 64, 128 or 256 (K a multiple of 128 and of it, checked by the caller)
 hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, bool y_bf16, int64_t ldy,
                        hipStream_t st) {
-  if (group == 256) return launch_gemm_g<true>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
-  if (group == 128) return launch_gemm_g<false>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  if (group == 256) return launch_gemm_g<256>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  if (group == 128) return launch_gemm_g<128>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
+  if (group == 64) return launch_gemm_g<64>(qa, sa, qw, sw, M, N, K, y, y_bf16, ldy, st);
   return hipErrorInvalidValue;
 }
 

@@ -42,7 +42,8 @@ typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 // group, 8 channels per lane (one 16-byte load for bf16).  Blocks run over
 // rows and their group ranges in a flat 1-D grid; the row and range come
 // from the block index (uniform), so the lanes do no index division.
-// GS: quantization group, 128 or 256 (two adjacent groups of a quad).
+// GS: quantization group, 64 (lanes 0-7 / 8-15 of a group's 16), 128, or
+// 256 (two adjacent groups of a quad).
 template <class Src, int U, int GS>
 __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int64_t blocks_per_row,
                                                          uint8_t* __restrict__ q, float* __restrict__ s,
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     m = max_x<1>(m);
     m = max_x<2>(m);
     m = max_x<4>(m);
-    m = max_x<8>(m);
+    if constexpr (GS >= 128) m = max_x<8>(m);
     if constexpr (GS == 256) m = max_x<16>(m);
     uint32_t b[8];
     encode<8>(v[u], m, b, flip);
@@ -98,7 +99,9 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
     if (grp < G) {
       reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
-      if constexpr (GS == 128) {
+      if constexpr (GS == 64) {
+        if ((sub & 7) == 0) srow[grp * 2 + (sub >> 3)] = m * post_scale;
+      } else if constexpr (GS == 128) {
         if (sub == 0) srow[grp] = m * post_scale;
       } else {
         if ((lane & 31) == 0) srow[grp >> 1] = m * post_scale;
@@ -979,7 +982,7 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
 }
 
 // Weights: element (k, n) at w[k * sk + n * sn]; rows of the output are n.
-// group: 128, or 256 for the block-128 Hadamard (the caller checks).
+// group: 128, or 64 / 256 for the block-128 Hadamard (the caller checks).
 hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
                               int64_t sn, uint8_t* q, float* s, int group, hipStream_t st) {
   const int64_t K = t.K, G = K / kGroup;
@@ -991,6 +994,7 @@ hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, i
     // to the rows of diag(signs) W, so the same sign flip on channel k
     auto run = [&](const auto& src) {
       if (t.block == 128 && group == 256) return launch_h128<256>(src, N, G, q, s, post, st);
+      if (t.block == 128 && group == 64) return launch_h128<64>(src, N, G, q, s, post, st);
       if (t.block == 128) return launch_h128<128>(src, N, G, q, s, post, st);
       return dispatch_rowh(src, K, N, log2b, false, q, s, nullptr, post, st);
     };

@@ -223,8 +223,8 @@ def test_group_size_validation_quantize_and_pack():
         assert p(h384, 256, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == SHAPE
         assert q(h512, 0, 64, FAKE, 1, 4, 512, FAKE, FAKE, None, None) == UNSUP   # block 512
         assert q(h128, 1, 256, FAKE, 1, 4, 512, FAKE, FAKE, FAKE, None) == UNSUP  # RRS
-        assert p(h128, 64, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == UNSUP           # no 64-group GEMM
         assert p(h512, 256, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == UNSUP
+        assert p(h512, 64, FAKE, 0, 4, 4, 1, FAKE, FAKE, None) == UNSUP
         # supported combinations with nothing to do
         for g in (64, 128, 256):
             assert q(h128, 0, g, None, 1, 0, 512, None, None, None, None) == OK
@@ -238,7 +238,8 @@ def test_group_size_validation_gemm_and_dequantize():
     gm, dq = lib.rw4_w4a4_gemm_g, lib.rw4_dequantize_g
     assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 512, 96, FAKE, 0, 4, None) == ARG
     assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 384, 256, FAKE, 0, 4, None) == SHAPE
-    assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 512, 64, FAKE, 0, 4, None) == UNSUP
+    assert gm(FAKE, FAKE, FAKE, FAKE, 4, 4, 192, 64, FAKE, 0, 4, None) == SHAPE   # K % 128
+    assert gm(None, None, None, None, 4, 0, 512, 64, None, 0, 4, None) == OK
     assert gm(None, None, None, None, 0, 4, 512, 256, None, 0, 4, None) == OK
     assert dq(FAKE, FAKE, 4, 512, 96, FAKE, 0, 512, None) == ARG
     assert dq(FAKE, FAKE, 4, 384, 256, FAKE, 0, 384, None) == SHAPE

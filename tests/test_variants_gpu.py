@@ -230,3 +230,38 @@ def test_givens_fp16_angles():
     t, _, qa, sa, aref = tp._quant_parity(wl)
     qw, sw, wref = tp._weight_parity(wl, t)
     tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+@pytest.mark.parametrize("M", [300, 7])
+def test_group64_end_to_end(M):
+    """64-wide groups (the article's choice for outlier-heavy layers) through
+    the GEMM: both kernels (large M and decode-sized M)."""
+    K, N = 1024, 136
+    rng = np.random.default_rng(70 + M)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    t, spec, qa, sa, aref = _group_quant_parity(x, "bf16", K, 64)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(w).to(gu.DEV), "kn", group=64)
+    wref = oracle.pack_weight(w, spec, 64)
+    tp._check_quant(tp._unpack(qw), gu.to_np(sw), wref["codes"], wref["ratio"], wref["sw"], "weight g64")
+    wl = datagen.Workload(f"g64_m{M}", M, K, N, x, "bf16", w, ("hadamard", 128), "group128", "f32")
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+@pytest.mark.parametrize("M", [200, 5])
+def test_group64_accumulators_exact(M):
+    """Group isolation at g = 64 on both kernels: Y = acc[:, :, j] exactly."""
+    K, N = 512, 72
+    rng = np.random.default_rng(80 + M)
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[0, 64:128], cw[1, 64:128] = -7, -7     # 64 * 49 in the odd half of a 128-group
+    qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
+    qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
+    acc = oracle.group_accumulators(ca, cw, 64)
+    sa = torch.ones((M, K // 64), dtype=torch.float32, device=gu.DEV)
+    for j in range(K // 64):
+        swn = np.zeros((N, K // 64), dtype=np.float32)
+        swn[:, j] = 1.0
+        y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
+        assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"group {j}"
