@@ -363,10 +363,16 @@ def dequant_gemm(qa: np.ndarray, sa: np.ndarray, qw: np.ndarray, sw: np.ndarray,
 
 
 def round_bf16(y: np.ndarray) -> np.ndarray:
-    """Round float64 to the nearest bfloat16 value (ties to even), as float64."""
+    """Round float64 to the nearest bfloat16 value (ties to even), as float64.
+
+    bfloat16 is the binary format with 8 exponent bits (as fp32) and 7
+    fraction bits: 8 significant bits for normal values, and below 2^-126
+    the subnormal grid with spacing 2^-133.  Inputs must lie below the bf16
+    maximum."""
     y = np.asarray(y, dtype=np.float64)
-    m, e = np.frexp(y)
-    return np.ldexp(np.rint(m * 256.0), e - 8)
+    _, e = np.frexp(y)  # y = m * 2**e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)
+    return np.ldexp(np.rint(np.ldexp(y, -q)), q)
 
 
 def round_output(y: np.ndarray, dtype: str) -> np.ndarray:

@@ -179,3 +179,21 @@ def test_quantize_act_group_size_follows_the_transform():
     # dequantization at g = 64 is within half a step of the transformed values
     xh = oracle.dequantize(a64["codes"], a64["sa"], 64)
     assert np.all(np.abs(xh - a64["xt"]) <= np.repeat(a64["sa"], 64, axis=1) / 2 * (1 + 1e-12))
+
+
+def test_round_bf16_grid():
+    """bf16 rounding: 8 significant bits for normal values, ties to even, and
+    below 2^-126 the subnormal grid of spacing 2^-133 (the same format as
+    fp32 with 16 fewer fraction bits)."""
+    t = 2.0 ** -133
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 3.0, -(1.0 + 2 ** -7 + 2 ** -9),
+                  2.0 ** -149, t, 1.5 * t, 2.5 * t, 33.2 * t, 2.0 ** -126 * (1 + 2 ** -8), 0.0])
+    want = np.array([1.0, 1.0 + 2 ** -6, 3.0, -(1.0 + 2 ** -7),
+                     0.0, t, 2 * t, 2 * t, 33 * t, 2.0 ** -126, 0.0])
+    assert np.array_equal(oracle.round_bf16(x), want)
+    # every float32 value already on the bf16 grid is unchanged
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2 ** 16, size=4000, dtype=np.uint32) << 16
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]    # finite values only
+    u = bits.view(np.float32).astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(u), u)
