@@ -100,7 +100,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
-                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny"])
+                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny", "kv"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -191,6 +191,79 @@ def cpu_baseline(wl, rows):
     return dt, threads
 
 
+KV_METRIC = "INT4 KV-cache quantize + dequantize GB/s (block-128 Hadamard per head) at 4096 tokens x 8 heads x 128"
+
+
+def main_kv(args, torch, rw4, gu, dev):
+    """The INT4 KV-cache use: quantize_act writes the cache, dequantize reads
+    it back (bf16).  One step = both calls over 4096 tokens x 1024 channels."""
+    import datagen
+    wl = datagen.make("kv")
+    M, K, grp = wl.M, wl.K, args.group
+    t = gu.transform_for(wl)
+    x0 = gu.x_to_device(wl.x, wl.x_dtype)
+    qbytes = M * K * 2 + M * K // 2 + M * (K // grp) * 4
+    dbytes = M * K // 2 + M * (K // grp) * 4 + M * K * 2
+    nsets = max(2, math.ceil(MALL_FLUSH_BYTES / (qbytes + dbytes)))
+    sets = [dict(x=x0.clone(), qa=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                 sa=torch.empty((M, K // grp), dtype=torch.float32, device=dev),
+                 out=torch.empty((M, K), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i, ev=None):
+        st = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        rw4.quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp)
+        if ev is not None:
+            ev[1].record(stream)
+        rw4.dequantize(st["qa"], st["sa"], out=st["out"])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[1]) for e in events]))
+    d_us = 1e3 * float(np.mean([e[1].elapsed_ms(e[2]) for e in events]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = (qbytes + dbytes) / (ms_per_step * 1e-3) / 1e9
+    q_gbps, d_gbps = qbytes / (q_us * 1e-6) / 1e9, dbytes / (d_us * 1e-6) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us  quantize {q_us:.2f} us ({q_gbps:.0f} GB/s)  "
+        f"dequantize {d_us:.2f} us ({d_gbps:.0f} GB/s)")
+    out = {
+        "metric": KV_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in/out, int4 codes, fp32 transform and scales", "data": "synthetic",
+        "config": {"workload": f"kv M={M} K={K} (8 heads x 128)", "group": grp, "buffer_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": q_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quant_h128_act_kernel",
+                     "algorithmic_bytes_per_launch": qbytes, "avg_launch_us": q_us},
+        "dequantize": {"kernel": "dequant_kernel", "avg_launch_us": d_us, "gbps": d_gbps,
+                       "frac_hbm": d_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": dbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.helpers import spec_of
+        rows = args.cpu_rows or 1024
+        t1 = time.perf_counter()
+        a = oracle.quantize_act(wl.x[:rows], spec_of(wl), "group128", grp)
+        oracle.round_dequant_output(oracle.dequantize(a["codes"], a["sa"], grp), "bf16")
+        dt = time.perf_counter() - t1
+        cpu_bytes = (qbytes + dbytes) * rows / M
+        out["cpu_baseline"] = {"value": cpu_bytes / dt / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{rows} of {M} tokens, quantize_act + dequantize "
+                                                         f"(float64 numpy)", "seconds": dt}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +287,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {args.calibrate_copy} MiB x5 ({n * 4} bytes read and written per copy)")
         return
+    if args.workload == "kv":
+        return main_kv(args, torch, rw4, gu, dev)
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group

@@ -265,3 +265,21 @@ def test_group64_accumulators_exact(M):
         swn[:, j] = 1.0
         y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
         assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"group {j}"
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_dequantize_extreme_scales(out):
+    """Scales from subnormal to near the fp32 maximum, on both sides of the
+    2^119 bound where the widened-FP8 path hands over to the per-code path:
+    the product is still the exact c * s rounded once."""
+    M, K = 6, 256
+    rng = np.random.default_rng(90)
+    codes = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    scales = np.array([[1e-45, 3e-39], [2.0 ** -126, 1.0], [2.0 ** 118, 2.0 ** 119],
+                       [1e36, 4e37], [0.0, 7.5e-3], [2.0 ** 119 * 0.999, 3.3e38 / 7]], dtype=np.float32)
+    q = torch.from_numpy(oracle.pack_int4(codes)).to(gu.DEV)
+    s = torch.from_numpy(scales).to(gu.DEV)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = gu.to_np(rw4.dequantize(q, s, dt))
+    ref = oracle.round_dequant_output(oracle.dequantize(codes, scales.astype(np.float64)), out)
+    assert np.array_equal(y, ref)
