@@ -283,3 +283,32 @@ def test_dequantize_extreme_scales(out):
     y = gu.to_np(rw4.dequantize(q, s, dt))
     ref = oracle.round_dequant_output(oracle.dequantize(codes, scales.astype(np.float64)), out)
     assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("case", [("h128", 128, "group128", "bf16"), ("h128", 128, "group128", "f32"),
+                                  ("rrs2048", 2048, "rrs", "bf16"), ("rrs2048", 2048, "rrs", "f32")],
+                         ids=lambda c: f"{c[0]}-{c[3]}")
+def test_strided_activations_and_output(case):
+    """Activations as a column slice of a wider tensor (ldx > K) and the GEMM
+    writing into a column slice of a wider output (ldy > N): same results as
+    the contiguous calls, and the padding untouched."""
+    name, block, mode, xdt = case
+    M, K, N = 37, 2048, 40
+    rng = np.random.default_rng(101)
+    x = datagen.outlier_activations(rng, M, K)
+    x = datagen.round_to_bf16(x) if xdt == "bf16" else x.astype(np.float32).astype(np.float64)
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    t = rw4.Transform.hadamard(K, block)
+    xd = gu.x_to_device(x, xdt)
+    wide = torch.zeros((M, K + 96), dtype=xd.dtype, device=gu.DEV)
+    wide[:, 32:32 + K] = xd
+    qa0, sa0 = rw4.quantize_act(t, xd, mode)
+    qa1, sa1 = rw4.quantize_act(t, wide[:, 32:32 + K], mode)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(w).to(gu.DEV))
+    y0 = rw4.w4a4_gemm(qa0, sa0, qw, sw, torch.bfloat16)
+    ybig = torch.full((M, N + 24), 5.0, dtype=torch.bfloat16, device=gu.DEV)
+    rw4.w4a4_gemm(qa0, sa0, qw, sw, out=ybig[:, 8:8 + N])
+    torch.cuda.synchronize()
+    assert torch.equal(qa0, qa1) and torch.equal(sa0, sa1)
+    assert torch.equal(y0, ybig[:, 8:8 + N])
+    assert torch.all(ybig[:, :8] == 5.0) and torch.all(ybig[:, 8 + N:] == 5.0)
