@@ -100,7 +100,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
-                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "tiny", "kv"])
+                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64", "tiny", "kv"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -25,7 +25,7 @@
 //                      come from one v_mfma_f32_32x32x16_bf16 on a 3-way
 //                      bf16 split of each scale, split once per block and
 //                      group into LDS; the VALU unpacks and accumulates.
-//   gemm_small_kernel  M <= 16 (decode): 16 output channels per block, the
+//   gemm_small_kernel  M <= 64 (decode, small batches): 16 output channels per block, the
 //                      eight waves split the groups, one
 //                      v_mfma_scale_f32_16x16x128_f8f6f4 per group with
 //                      fragments loaded straight from global memory.
@@ -562,7 +562,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 // A fragments of the other 64-wide half zeroed (lanes 0-31 supply codes
 // 0-63 of the group, lanes 32-63 codes 64-127).
 constexpr int kSmallWaves = 8;
-template <bool BF16, int GSZ>
+// MT: 16-row tiles of A (M <= 16 MT); the B fragment of a group feeds MT
+// MFMAs, so the weights are still read once.
+template <bool BF16, int GSZ, int MT>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint8_t* __restrict__ qa,
                                                                       const float* __restrict__ sa,
                                                                       const uint8_t* __restrict__ qw,
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
                                                                       int64_t ldy) {
   constexpr int P = GSZ == 256 ? 2 : 1;  // 128-groups per unit (one scale column, or two for GSZ 64)
   constexpr int H = GSZ == 64 ? 2 : 1;   // scale columns per unit
-  constexpr int NB = 4 / P;              // units in flight per wave
+  constexpr int NB = MT == 4 ? 2 : 4 / P;  // units in flight per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -579,15 +581,19 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
   const int64_t GS = GU * H;            // scale columns
   const int64_t rowbytes = K / 2;
   const int64_t n0 = int64_t(blockIdx.x) * 16;
-  const int64_t am = lane & 15;               // A row supplied by this lane
+  const int64_t am = lane & 15;               // A row (within each 16-row tile) supplied by this lane
   const int64_t bn = n0 + (lane & 15);        // B row (output channel)
   const int part = lane >> 4;
-  const bool a_ok = am < M, b_ok = bn < N;
+  const bool b_ok = bn < N;
 
-  float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float yv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yv[mt][r] = 0.0f;
   for (int64_t gb = wave; gb < GU; gb += kSmallWaves * NB) {
-    v4u pa[NB][P], pb[NB][P];
-    float swv[NB][H], sav[NB][H][4];
+    v4u pa[NB][P][MT], pb[NB][P];
+    float swv[NB][H], sav[NB][H][MT][4];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int64_t g = gb + kSmallWaves * t;
@@ -595,17 +601,24 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int64_t off = (g * P + p) * 64 + part * 16;
-        pa[t][p] = (in && a_ok) ? *reinterpret_cast<const v4u*>(qa + am * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int64_t m = mt * 16 + am;
+          pa[t][p][mt] = (in && m < M) ? *reinterpret_cast<const v4u*>(qa + m * rowbytes + off)
+                                       : v4u{0u, 0u, 0u, 0u};
+        }
         pb[t][p] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         swv[t][h] = (in && b_ok) ? sw[bn * GS + g * H + h] : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = part * 4 + r;
-          sav[t][h][r] = (in && m < M) ? sa[m * GS + g * H + h] : 0.0f;
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = mt * 16 + part * 4 + r;
+            sav[t][h][mt][r] = (in && m < M) ? sa[m * GS + g * H + h] : 0.0f;
+          }
       }
     }
 #pragma unroll
@@ -613,37 +626,51 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint
       const int64_t g = gb + kSmallWaves * t;
       if (g >= GU) break;
       if constexpr (GSZ == 64) {
-        const v8i a = f8_operand(pa[t][0]), b = f8_operand(pb[t][0]);
+        const v8i b = f8_operand(pb[t][0]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v8i ah = (part >> 1) == h ? a : v8i{};
-          const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, v4f{}, 0, 0, 0, kE8Scale, 0,
-                                                                           kE8Scale);
+        for (int mt = 0; mt < MT; ++mt) {
+          const v8i a = f8_operand(pa[t][0][mt]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][h][r] * swv[t][h], yv[r]);
+          for (int h = 0; h < 2; ++h) {
+            const v8i ah = (part >> 1) == h ? a : v8i{};
+            const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, v4f{}, 0, 0, 0, kE8Scale, 0,
+                                                                             kE8Scale);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yv[mt][r] = fmaf(acc[r], sav[t][h][mt][r] * swv[t][h], yv[mt][r]);
+          }
         }
       } else {
-        v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0]), f8_operand(pb[t][0]),
-                                                                   v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
-        if constexpr (P == 2)
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1]), f8_operand(pb[t][1]), acc,
-                                                                 0, 0, 0, kE8Scale, 0, kE8Scale);
+        v8i b[P];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yv[r] = fmaf(acc[r], sav[t][0][r] * swv[t][0], yv[r]);
+        for (int p = 0; p < P; ++p) b[p] = f8_operand(pb[t][p]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0][mt]), b[0], v4f{}, 0, 0,
+                                                                     0, kE8Scale, 0, kE8Scale);
+          if constexpr (P == 2)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1][mt]), b[1], acc, 0, 0, 0,
+                                                                   kE8Scale, 0, kE8Scale);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yv[mt][r] = fmaf(acc[r], sav[t][0][mt][r] * swv[t][0], yv[mt][r]);
+        }
       }
     }
   }
-  __shared__ float red[kSmallWaves][64][4];
+  __shared__ float red[kSmallWaves][64][4 * MT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][lane][r] = yv[r];
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][lane][4 * mt + r] = yv[mt][r];
   __syncthreads();
-  if (wave == 0) {
+  // wave w sums tile rows mt = w % MT (the others idle)
+  if (wave < MT) {
+    const int mt = wave;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kSmallWaves; ++w) v += red[w][lane][r];
-      const int64_t m = part * 4 + r;
+      for (int w = 0; w < kSmallWaves; ++w) v += red[w][lane][4 * mt + r];
+      const int64_t m = mt * 16 + part * 4 + r;
       if (m < M && b_ok) store_y<BF16>(y, ldy, m, bn, v);
     }
   }
@@ -653,15 +680,21 @@ template <int GSZ>
 hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                          hipStream_t st) {
-  if (M <= 16) {
+  if (M <= 64) {  // decode and small batches: weights streamed once, 16 output channels per block
     const int64_t blocks = (N + 15) / 16;
-    if (y_bf16)
-      hipLaunchKernelGGL((gemm_small_kernel<true, GSZ>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
-                         sa, qw, sw, M, N, K, y, ldy);
-    else
-      hipLaunchKernelGGL((gemm_small_kernel<false, GSZ>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
-                         sa, qw, sw, M, N, K, y, ldy);
-    return hipGetLastError();
+    auto run = [&](auto mt_const) {
+      constexpr int MT = decltype(mt_const)::value;
+      if (y_bf16)
+        hipLaunchKernelGGL((gemm_small_kernel<true, GSZ, MT>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+                           sa, qw, sw, M, N, K, y, ldy);
+      else
+        hipLaunchKernelGGL((gemm_small_kernel<false, GSZ, MT>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+                           sa, qw, sw, M, N, K, y, ldy);
+      return hipGetLastError();
+    };
+    if (M <= 16) return run(std::integral_constant<int, 1>{});
+    if (M <= 32) return run(std::integral_constant<int, 2>{});
+    return run(std::integral_constant<int, 4>{});
   }
   // per-block buffer ranges: 128 rows of K / 2 bytes, 128 rows of K / 128 scales
   if (K > (int64_t(1) << 24)) return hipErrorInvalidValue;

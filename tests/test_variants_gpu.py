@@ -312,3 +312,33 @@ def test_strided_activations_and_output(case):
     assert torch.equal(qa0, qa1) and torch.equal(sa0, sa1)
     assert torch.equal(y0, ybig[:, 8:8 + N])
     assert torch.all(ybig[:, :8] == 5.0) and torch.all(ybig[:, 8 + N:] == 5.0)
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+@pytest.mark.parametrize("M", [17, 32, 33, 50, 64, 65])
+def test_small_batch_accumulators_exact(M, g):
+    """Small batches (the decode kernel with 2 or 4 row tiles up to M = 64,
+    the tiled kernel above): exact integer group sums by group isolation,
+    with extreme accumulators in the last rows."""
+    K, N = 512, 40
+    rng = np.random.default_rng(1000 + M + g)
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[M - 1, :g], cw[N - 1, :g] = 7, -7            # -g * 49 in the last row and column
+    qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
+    qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
+    acc = oracle.group_accumulators(ca, cw, g)
+    sa = torch.ones((M, K // g), dtype=torch.float32, device=gu.DEV)
+    for j in (0, K // g - 1):
+        swn = np.zeros((N, K // g), dtype=np.float32)
+        swn[:, j] = 1.0
+        y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
+        assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"M {M} g {g} group {j}"
+
+
+@pytest.mark.parametrize("M", [24, 48, 64])
+def test_small_batch_end_to_end(M):
+    wl = datagen.make("decode", M=M, K=1024, N=256)
+    t, xd, qa, sa, aref = tp._quant_parity(wl)
+    qw, sw, wref = tp._weight_parity(wl, t)
+    tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
