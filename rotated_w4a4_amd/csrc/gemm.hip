@@ -25,10 +25,11 @@
 //                      come from one v_mfma_f32_32x32x16_bf16 on a 3-way
 //                      bf16 split of each scale, split once per block and
 //                      group into LDS; the VALU unpacks and accumulates.
-//   gemm_small_kernel  M <= 64 (decode, small batches): 16 output channels per block, the
-//                      eight waves split the groups, one
-//                      v_mfma_scale_f32_16x16x128_f8f6f4 per group with
-//                      fragments loaded straight from global memory.
+//   gemm_small_kernel  M <= 64 (decode, small batches): 16 or 32 output
+//                      channels per block, the eight waves split K; A and
+//                      the scales staged in LDS per iteration, the weights
+//                      read straight into registers, one
+//                      v_mfma_scale_f32_16x16x128_f8f6f4 per 128 codes.
 // MFMA result layouts: for 32 x 32, lane l holds
 // D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15; for 16 x 16,
 // D[4 (l / 16) + r][l % 16], r = 0..3.
@@ -549,129 +550,243 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel (decode, M <= 16): one block of 8 waves per 16 output
-// channels; the waves split the groups (4 groups in flight per wave, with
-// their scales); lane l supplies row l % 16 and codes [32 (l / 16),
-// 32 (l / 16) + 32) of the group for both operands, so one 16 x 16 x 128
-// MFMA covers a whole group.  Fragments come straight from global memory
-// (no reuse to stage); the partial results are summed across waves in LDS.
+// Small-M kernel (decode and small batches, M <= 64): one block of 8 waves
+// per CT tiles of 16 output channels.  K is cut into slices of 128 codes,
+// one v_mfma_scale_f32_16x16x128_f8f6f4 per slice, 16-channel tile and
+// 16-row A tile; lane l supplies row l % 16 and codes
+// [32 (l / 16), 32 (l / 16) + 32) of the slice for both operands.  An
+// iteration covers GB slices, NS consecutive ones per wave.
+//
+// Every block reads all of A and of sa, so these are the hot lines of the
+// launch: per iteration the block stages its A slices and the scale columns
+// they use (sa of every row, sw of its channels) into LDS with coalesced
+// loads, instead of each wave fetching them lane by lane.  The weights are
+// read once, straight into registers.  The loads of the next iteration are
+// issued before the current one computes (two register stages).  All loads
+// are buffer loads whose range or offset makes out-of-range lanes read
+// zeros, so no branch surrounds a load and the waits count exactly.
+// The partial sums of the waves are added in LDS at the end.
+//
+// GSZ 256: a scale column covers two consecutive slices, whose two MFMAs
+// chain into one accumulator before the scale is applied.  GSZ 64: a slice
+// has two scale columns; its MFMA runs twice, each time with the A
+// fragments of the other 64-code half zeroed (lanes 0-31 supply codes 0-63
+// of the slice, lanes 32-63 codes 64-127).
 // ---------------------------------------------------------------------------
-// GSZ 256: a scale column covers two consecutive 128-groups, whose two
-// MFMAs chain into one accumulator before the scale is applied.  GSZ 64: a
-// 128-group has two scale columns; its MFMA runs twice, each time with the
-// A fragments of the other 64-wide half zeroed (lanes 0-31 supply codes
-// 0-63 of the group, lanes 32-63 codes 64-127).
 constexpr int kSmallWaves = 8;
-// MT: 16-row tiles of A (M <= 16 MT); the B fragment of a group feeds MT
-// MFMAs, so the weights are still read once.
-template <bool BF16, int GSZ, int MT>
-__global__ __launch_bounds__(kSmallWaves * 64) void gemm_small_kernel(const uint8_t* __restrict__ qa,
-                                                                      const float* __restrict__ sa,
-                                                                      const uint8_t* __restrict__ qw,
-                                                                      const float* __restrict__ sw, int64_t M,
-                                                                      int64_t N, int64_t K, void* __restrict__ y,
-                                                                      int64_t ldy) {
-  constexpr int P = GSZ == 256 ? 2 : 1;  // 128-groups per unit (one scale column, or two for GSZ 64)
-  constexpr int H = GSZ == 64 ? 2 : 1;   // scale columns per unit
-  constexpr int NB = MT == 4 ? 2 : 4 / P;  // units in flight per wave
+constexpr int kSmallThreads = kSmallWaves * 64;
+constexpr uint32_t kNoRead = 0x80000000u;  // buffer offset past every range: the load returns zeros
+
+template <int GSZ, int MT, int CT>
+struct SmallCfg {
+  static constexpr int P = GSZ == 256 ? 2 : 1;                 // slices per scale column
+  static constexpr int H = GSZ == 64 ? 2 : 1;                  // scale columns per slice
+  static constexpr int NS = (MT == 4 ? 1 : 2) > P ? (MT == 4 ? 1 : 2) : P;  // slices per wave and iteration
+  static constexpr int GB = kSmallWaves * NS;                   // slices per iteration
+  static constexpr int CW = GB * H / P;                         // scale columns per iteration
+  static constexpr int AROW = GB * 4;                           // 16-byte chunks of an A row slice
+  static constexpr int AR = 16 * MT * AROW / kSmallThreads;     // A chunks staged per thread
+  static constexpr int SAE = 16 * MT * CW, SWE = 16 * CT * CW;  // staged scales
+  static constexpr int SAR = (SAE + kSmallThreads - 1) / kSmallThreads;
+  static constexpr int SWR = (SWE + kSmallThreads - 1) / kSmallThreads;
+  // LDS: A rows padded by one chunk, then sa as [column][row], sw as [column][channel]
+  // (each padded to whole rounds of the block, the idle slots never read)
+  static constexpr int A_BYTES = 16 * MT * (AROW + 1) * 16;
+  static constexpr int SA_OFF = A_BYTES, SW_OFF = SA_OFF + SAR * kSmallThreads * 4;
+  static constexpr int BYTES = SW_OFF + SWR * kSmallThreads * 4;
+  static constexpr int RED_BYTES = kSmallWaves * CT * MT * 64 * 4 * 4;  // aliases the A rows
+  static_assert(AR * kSmallThreads == 16 * MT * AROW, "A slice must split evenly over the block");
+  static_assert(RED_BYTES <= A_BYTES, "reduction buffer must fit in the A staging area");
+  static_assert(CT * MT <= kSmallWaves, "one wave per output tile in the epilogue");
+};
+
+template <int GSZ, int MT, int CT>
+struct SmallStage {
+  using C = SmallCfg<GSZ, MT, CT>;
+  float sa[C::SAR], sw[C::SWR];
+  v4u a[C::AR];
+  v4u b[CT][C::NS];
+};
+
+template <bool BF16, int GSZ, int MT, int CT>
+__global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t* __restrict__ qa,
+                                                                   const float* __restrict__ sa,
+                                                                   const uint8_t* __restrict__ qw,
+                                                                   const float* __restrict__ sw, int64_t M,
+                                                                   int64_t N, int64_t K, void* __restrict__ y,
+                                                                   int64_t ldy) {
+  using C = SmallCfg<GSZ, MT, CT>;
+  using Stage = SmallStage<GSZ, MT, CT>;
+  __shared__ __align__(16) uint8_t lds[C::BYTES];
+  v4u* const As = reinterpret_cast<v4u*>(lds);
+  float* const saT = reinterpret_cast<float*>(lds + C::SA_OFF);
+  float* const swT = reinterpret_cast<float*>(lds + C::SW_OFF);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t GU = K / (kGroup * P);  // units
-  const int64_t GS = GU * H;            // scale columns
+  const int am = lane & 15;   // A row within a 16-row tile; B channel within a 16-channel tile
+  const int part = lane >> 4;  // 32-code quarter of the slice
+  const int64_t SL = K / kGroup;             // slices
+  const int64_t GS = SL * C::H / C::P;       // scale columns
   const int64_t rowbytes = K / 2;
-  const int64_t n0 = int64_t(blockIdx.x) * 16;
-  const int64_t am = lane & 15;               // A row (within each 16-row tile) supplied by this lane
-  const int64_t bn = n0 + (lane & 15);        // B row (output channel)
-  const int part = lane >> 4;
-  const bool b_ok = bn < N;
+  const int64_t n0 = int64_t(blockIdx.x) * 16 * CT;
+  const int64_t nrows = N - n0 < 16 * CT ? N - n0 : 16 * CT;
+  const int64_t NI = (SL + C::GB - 1) / C::GB;  // iterations
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa, M * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa, M * GS * 4);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + n0 * rowbytes, nrows * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw + n0 * GS, nrows * GS * 4);
 
-  float yv[MT][4];
+  // staged A chunk j of this thread: row, chunk within the row slice
+  auto a_row = [&](int j) { return (j * kSmallThreads + tid) / C::AROW; };
+  auto a_chunk = [&](int j) { return (j * kSmallThreads + tid) % C::AROW; };
+
+  // every load of iteration it (it >= NI: all out of range); staging loads first
+  auto issue = [&](Stage& S, int64_t it) {
+    const int64_t s0 = it * C::GB;        // first slice
+    const int64_t c0 = s0 * C::H / C::P;  // first scale column
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yv[mt][r] = 0.0f;
-  for (int64_t gb = wave; gb < GU; gb += kSmallWaves * NB) {
-    v4u pa[NB][P][MT], pb[NB][P];
-    float swv[NB][H], sav[NB][H][MT][4];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const int64_t g = gb + kSmallWaves * t;
-      const bool in = g < GU;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int64_t off = (g * P + p) * 64 + part * 16;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int64_t m = mt * 16 + am;
-          pa[t][p][mt] = (in && m < M) ? *reinterpret_cast<const v4u*>(qa + m * rowbytes + off)
-                                       : v4u{0u, 0u, 0u, 0u};
-        }
-        pb[t][p] = (in && b_ok) ? *reinterpret_cast<const v4u*>(qw + bn * rowbytes + off) : v4u{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        swv[t][h] = (in && b_ok) ? sw[bn * GS + g * H + h] : 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t m = mt * 16 + part * 4 + r;
-            sav[t][h][mt][r] = (in && m < M) ? sa[m * GS + g * H + h] : 0.0f;
-          }
-      }
+    for (int j = 0; j < C::SAR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      const int64_t col = c0 + idx % C::CW;
+      const bool ok = idx < C::SAE && col < GS;
+      S.sa[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsa, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
     }
 #pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const int64_t g = gb + kSmallWaves * t;
-      if (g >= GU) break;
-      if constexpr (GSZ == 64) {
-        const v8i b = f8_operand(pb[t][0]);
+    for (int j = 0; j < C::SWR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      const int64_t col = c0 + idx % C::CW;
+      const bool ok = idx < C::SWE && col < GS;
+      S.sw[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsw, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
+    }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const v8i a = f8_operand(pa[t][0][mt]);
+    for (int j = 0; j < C::AR; ++j) {
+      const int64_t byte = s0 * 64 + a_chunk(j) * 16;
+      S.a[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ra, int(byte < rowbytes ? uint32_t(a_row(j) * rowbytes + byte) : kNoRead),
+                                           0, 0));
+    }
+#pragma unroll
+    for (int ns = 0; ns < C::NS; ++ns) {
+      const int64_t sl = s0 + wave * C::NS + ns;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        S.b[ct][ns] = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                     rb, int(sl < SL ? uint32_t((ct * 16 + am) * rowbytes + sl * 64 + part * 16) : kNoRead), 0, 0));
+    }
+  };
+  auto store = [&](const Stage& S) {
+#pragma unroll
+    for (int j = 0; j < C::SAR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      saT[idx < C::SAE ? (idx % C::CW) * (16 * MT) + idx / C::CW : idx] = S.sa[j];
+    }
+#pragma unroll
+    for (int j = 0; j < C::SWR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      swT[idx < C::SWE ? (idx % C::CW) * (16 * CT) + idx / C::CW : idx] = S.sw[j];
+    }
+#pragma unroll
+    for (int j = 0; j < C::AR; ++j) As[a_row(j) * (C::AROW + 1) + a_chunk(j)] = S.a[j];
+  };
+
+  float yv[CT][MT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yv[ct][mt][r] = 0.0f;
+
+  // y += acc * (sa * sw) of local scale column cl
+  auto apply = [&](int ct, int mt, const v4f& acc, int cl) {
+    const v4f s4 = *reinterpret_cast<const v4f*>(saT + cl * (16 * MT) + mt * 16 + part * 4);
+    const float swv = swT[cl * (16 * CT) + ct * 16 + am];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yv[ct][mt][r] = fmaf(acc[r], s4[r] * swv, yv[ct][mt][r]);
+  };
+  auto a_frag = [&](int mt, int gl) { return f8_operand(As[(mt * 16 + am) * (C::AROW + 1) + gl * 4 + part]); };
+  auto compute = [&](const Stage& S) {
+#pragma unroll
+    for (int ns = 0; ns < C::NS; ns += C::P) {
+      const int gl = wave * C::NS + ns;  // local slice
+      v8i b[C::P][CT];
+#pragma unroll
+      for (int p = 0; p < C::P; ++p)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) b[p][ct] = f8_operand(S.b[ct][ns + p]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (GSZ == 64) {
+          const v8i a = a_frag(mt, gl);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const v8i ah = (part >> 1) == h ? a : v8i{};
-            const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b, v4f{}, 0, 0, 0, kE8Scale, 0,
-                                                                             kE8Scale);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yv[mt][r] = fmaf(acc[r], sav[t][h][mt][r] * swv[t][h], yv[mt][r]);
+            for (int ct = 0; ct < CT; ++ct)
+              apply(ct, mt,
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b[0][ct], v4f{}, 0, 0, 0, kE8Scale, 0,
+                                                                     kE8Scale),
+                    2 * gl + h);
           }
-        }
-      } else {
-        v8i b[P];
+        } else {
+          v8i a[C::P];
 #pragma unroll
-        for (int p = 0; p < P; ++p) b[p] = f8_operand(pb[t][p]);
+          for (int p = 0; p < C::P; ++p) a[p] = a_frag(mt, gl + p);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][0][mt]), b[0], v4f{}, 0, 0,
-                                                                     0, kE8Scale, 0, kE8Scale);
-          if constexpr (P == 2)
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f8_operand(pa[t][1][mt]), b[1], acc, 0, 0, 0,
-                                                                   kE8Scale, 0, kE8Scale);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) yv[mt][r] = fmaf(acc[r], sav[t][0][mt][r] * swv[t][0], yv[mt][r]);
+          for (int ct = 0; ct < CT; ++ct) {
+            v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0][ct], v4f{}, 0, 0, 0, kE8Scale, 0,
+                                                                       kE8Scale);
+            if constexpr (C::P == 2)
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], b[1][ct], acc, 0, 0, 0, kE8Scale, 0,
+                                                                     kE8Scale);
+            apply(ct, mt, acc, gl / C::P);
+          }
         }
       }
     }
+  };
+  // one iteration: stage cur into LDS, issue the next iteration into nxt, compute cur
+  auto step = [&](Stage& cur, Stage& nxt, int64_t it) {
+    store(cur);
+    __syncthreads();
+    issue(nxt, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __syncthreads();  // LDS free for the next store
+  };
+
+  Stage s0, s1;
+  issue(s0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t it = 0; it < NI; it += 2) {
+    step(s0, s1, it);
+    if (it + 1 >= NI) break;
+    step(s1, s0, it + 1);
   }
-  __shared__ float red[kSmallWaves][64][4 * MT];
+
+  float* const red = reinterpret_cast<float*>(lds);  // [wave][tile][lane][4]
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][lane][4 * mt + r] = yv[mt][r];
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<v4f*>(red + ((wave * CT * MT + ct * MT + mt) * 64 + lane) * 4) =
+          v4f{yv[ct][mt][0], yv[ct][mt][1], yv[ct][mt][2], yv[ct][mt][3]};
   __syncthreads();
-  // wave w sums tile rows mt = w % MT (the others idle)
-  if (wave < MT) {
-    const int mt = wave;
+  if (wave < CT * MT) {  // wave t adds up output tile t over the waves
+    const int ct = wave / MT, mt = wave % MT;
+    v4f v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) v += *reinterpret_cast<const v4f*>(red + ((w * CT * MT + wave) * 64 + lane) * 4);
+    const int64_t bn = n0 + ct * 16 + am;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kSmallWaves; ++w) v += red[w][lane][4 * mt + r];
       const int64_t m = mt * 16 + part * 4 + r;
-      if (m < M && b_ok) store_y<BF16>(y, ldy, m, bn, v);
+      if (m < M && bn < N) store_y<BF16>(y, ldy, m, bn, v[r]);
     }
   }
 }
@@ -680,21 +795,24 @@ template <int GSZ>
 hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                          hipStream_t st) {
-  if (M <= 64) {  // decode and small batches: weights streamed once, 16 output channels per block
-    const int64_t blocks = (N + 15) / 16;
-    auto run = [&](auto mt_const) {
-      constexpr int MT = decltype(mt_const)::value;
+  if (M <= 64) {  // decode and small batches: weights streamed once, 16 CT output channels per block
+    auto run = [&](auto mt_const, auto ct_const) {
+      constexpr int MT = decltype(mt_const)::value, CT = decltype(ct_const)::value;
+      const int64_t blocks = (N + 16 * CT - 1) / (16 * CT);
+      if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
       if (y_bf16)
-        hipLaunchKernelGGL((gemm_small_kernel<true, GSZ, MT>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+        hipLaunchKernelGGL((gemm_small_kernel<true, GSZ, MT, CT>), dim3(blocks), dim3(kSmallThreads), 0, st, qa,
                            sa, qw, sw, M, N, K, y, ldy);
       else
-        hipLaunchKernelGGL((gemm_small_kernel<false, GSZ, MT>), dim3(blocks), dim3(kSmallWaves * 64), 0, st, qa,
+        hipLaunchKernelGGL((gemm_small_kernel<false, GSZ, MT, CT>), dim3(blocks), dim3(kSmallThreads), 0, st, qa,
                            sa, qw, sw, M, N, K, y, ldy);
       return hipGetLastError();
     };
-    if (M <= 16) return run(std::integral_constant<int, 1>{});
-    if (M <= 32) return run(std::integral_constant<int, 2>{});
-    return run(std::integral_constant<int, 4>{});
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (M <= 16) return N > 12288 ? run(I1{}, I2{}) : run(I1{}, I1{});  // past 3 blocks per CU: 32 channels
+    if (M <= 32) return run(I2{}, I1{});
+    return run(std::integral_constant<int, 4>{}, I1{});
   }
   // per-block buffer ranges: 128 rows of K / 2 bytes, 128 rows of K / 128 scales
   if (K > (int64_t(1) << 24)) return hipErrorInvalidValue;
