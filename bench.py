@@ -17,8 +17,13 @@ Prints one JSON line (stdout).  Per-kernel times come from HIP events
 (created without the system-scope fence, so recording them flushes no
 caches) recorded on the stream the library launches on; the GEMM is the
 dominant kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported,
-the quantize kernel's HBM roofline beside it.  The CPU oracle is timed on a bounded sample of the same
-workload as a reported baseline (not a target).
+the quantize kernel's HBM roofline beside it.  Each kernel is also timed
+alone, 20 launches queued behind a 1 GiB device copy so that the host is
+ahead of the GPU: for decode-sized and KV-cache steps, which are shorter
+than the host's Python calls, that is the kernel's own duration and the
+roofline uses it (HBM-bound: the weights or the cache are streamed once).
+The CPU oracle is timed on a bounded sample of the same workload as a
+reported baseline (not a target).
 """
 from __future__ import annotations
 
@@ -94,6 +99,54 @@ class HipEvent:
             self._lib.hipEventDestroy(self.h)
 
 
+_COVER = {}
+
+
+def gpu_bound_us(torch, stream, fn, reps=20):
+    """Average duration of `reps` launches fn(0..reps-1) with the host ahead of the GPU.
+
+    A device copy of 1 GiB is queued first; while the GPU runs it, the host
+    queues every launch, so no launch waits for the host (the Python binding
+    takes longer per call than a decode-sized kernel runs, which inflates
+    events recorded around single launches).  Returns (us per launch, whether
+    the host finished queueing before the copy ended)."""
+    if "src" not in _COVER:
+        _COVER["src"] = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        _COVER["dst"] = torch.empty_like(_COVER["src"])
+    c0, e0, e1 = HipEvent(), HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    c0.record(stream)
+    _COVER["dst"].copy_(_COVER["src"])
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    host_ms = (time.perf_counter() - h0) * 1e3
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) * 1e3 / reps, host_ms < c0.elapsed_ms(e0)
+
+
+def capture_steps(torch, step, nsets):
+    """One HIP graph per buffer set holding that set's step (the library only launches
+    kernels on the current stream: nothing to allocate, clear or synchronise inside)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager warm-up off the capture stream
+        for i in range(nsets):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +156,9 @@ def parse():
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64", "tiny", "kv"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
+    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
+                    help="how a step is issued: eager Python calls, or one HIP graph replay per step "
+                         "(a replay costs more GPU time than the two kernels of a decode step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -222,32 +278,62 @@ def main_kv(args, torch, rw4, gu, dev):
         if ev is not None:
             ev[2].record(stream)
 
+    graph = args.launch == "graph"
+    if graph:
+        graphs = capture_steps(torch, step, nsets)
+
+        def run(i, ev=None):  # the whole step, one graph launch
+            if ev is not None:
+                ev[0].record(stream)
+            graphs[i % nsets].replay()
+            if ev is not None:
+                ev[2].record(stream)
+    else:
+        run = step
+
     for i in range(args.warmup):
-        step(i)
+        run(i)
     events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        run(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[1]) for e in events]))
-    d_us = 1e3 * float(np.mean([e[1].elapsed_ms(e[2]) for e in events]))
+    step_gpu_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[2]) for e in events]))
     ms_per_step = wall * 1e3 / args.steps
     value = (qbytes + dbytes) / (ms_per_step * 1e-3) / 1e9
-    q_gbps, d_gbps = qbytes / (q_us * 1e-6) / 1e9, dbytes / (d_us * 1e-6) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us  quantize {q_us:.2f} us ({q_gbps:.0f} GB/s)  "
-        f"dequantize {d_us:.2f} us ({d_gbps:.0f} GB/s)")
+    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else 'eager calls'}; "
+        f"GPU {step_gpu_us:.1f} us)")
+
+    def q_only(i):
+        st = sets[i % nsets]
+        rw4.quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp)
+
+    def d_only(i):
+        st = sets[i % nsets]
+        rw4.dequantize(st["qa"], st["sa"], out=st["out"])
+
+    # the kernels run about as long as the host takes per Python call: time them with the host ahead
+    (q_b2b, q_ahead), (d_b2b, d_ahead) = gpu_bound_us(torch, stream, q_only), gpu_bound_us(torch, stream, d_only)
+    qb_gbps, db_gbps = qbytes / (q_b2b * 1e-6) / 1e9, dbytes / (d_b2b * 1e-6) / 1e9
+    log(f"back-to-back (host ahead: {q_ahead and d_ahead}): quantize {q_b2b:.2f} us ({qb_gbps:.0f} GB/s)  "
+        f"dequantize {d_b2b:.2f} us ({db_gbps:.0f} GB/s)")
     out = {
         "metric": KV_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in/out, int4 codes, fp32 transform and scales", "data": "synthetic",
-        "config": {"workload": f"kv M={M} K={K} (8 heads x 128)", "group": grp, "buffer_sets": nsets},
-        "roofline": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": q_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quant_h128_act_kernel",
-                     "algorithmic_bytes_per_launch": qbytes, "avg_launch_us": q_us},
-        "dequantize": {"kernel": "dequant_kernel", "avg_launch_us": d_us, "gbps": d_gbps,
-                       "frac_hbm": d_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": dbytes},
+        "config": {"workload": f"kv M={M} K={K} (8 heads x 128)", "group": grp, "buffer_sets": nsets,
+                   "launch": "one HIP graph replay per step" if graph else "eager calls"},
+        "step_gpu_us": step_gpu_us,
+        "roofline": {"bound": "hbm", "achieved": qb_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": qb_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quant_h128_act_kernel",
+                     "algorithmic_bytes_per_launch": qbytes, "avg_launch_us": q_b2b,
+                     "timing": "HIP events around 20 launches queued behind a 1 GiB copy (host ahead: "
+                               f"{q_ahead}): the kernel's own duration"},
+        "dequantize": {"kernel": "dequant_kernel", "avg_launch_us": d_b2b,
+                       "gbps": db_gbps, "frac_hbm": db_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": dbytes,
+                       "host_ahead": d_ahead},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -335,8 +421,21 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    graph = args.launch == "graph"
+    if graph:
+        graphs = capture_steps(torch, step, nsets)
+
+        def run(i, ev=None):  # the whole step, one graph launch
+            if ev is not None:
+                ev[0].record(stream)
+            graphs[i % nsets].replay()
+            if ev is not None:
+                ev[2].record(stream)
+    else:
+        run = step
+
     for i in range(args.warmup):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, events on the launch stream
@@ -344,32 +443,20 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        run(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_ms = [e[0].elapsed_ms(e[1]) for e in events]
-    g_ms = [e[1].elapsed_ms(e[2]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * M * N * K
-    q_us, g_us = 1e3 * float(np.mean(q_ms)), 1e3 * float(np.mean(g_ms))
+    step_gpu_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[2]) for e in events]))
+    if graph:
+        q_us = g_us = float("nan")  # replaced by the back-to-back times below
+    else:
+        q_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[1]) for e in events]))
+        g_us = 1e3 * float(np.mean([e[1].elapsed_ms(e[2]) for e in events]))
     layer_tops = ops / (ms_per_step * 1e-3) / 1e12
-    gemm_tops = ops / (g_us * 1e-6) / 1e12
-    quant_gbps = qbytes / (q_us * 1e-6) / 1e9
-    gemm_gbps = gbytes / (g_us * 1e-6) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
-        f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    # each kernel alone, launched back to back (no event between launches)
-    def back_to_back(fn, reps=20):
-        e0, e1 = HipEvent(), HipEvent()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_ms(e1) * 1e3 / reps
-
+    # each kernel alone, launched back to back behind a copy that lets the host run ahead
     def q_only(i):
         st = sets[i % nsets]
         rw4.quantize_act(t, st["x"], wl.mode, qa=st["qa"], sa=st["sa"], workspace=st["ws"], group=grp)
@@ -378,19 +465,33 @@ def main():
         st = sets[i % nsets]
         rw4.w4a4_gemm(st["qa"], st["sa"], st["qw"], st["sw"], out=st["y"])
 
-    q_b2b, g_b2b = back_to_back(q_only), back_to_back(g_only)
-    log(f"back-to-back: quantize {q_b2b:.2f} us, gemm {g_b2b:.2f} us")
+    (q_b2b, q_ahead), (g_b2b, g_ahead) = gpu_bound_us(torch, stream, q_only), gpu_bound_us(torch, stream, g_only)
+    log(f"back-to-back (host ahead: {q_ahead and g_ahead}): quantize {q_b2b:.2f} us, gemm {g_b2b:.2f} us")
+    if graph:  # per-kernel times of a graph step: the kernels alone, back to back
+        q_us, g_us = q_b2b, g_b2b
+    gemm_tops = ops / (g_us * 1e-6) / 1e12
+    quant_gbps = qbytes / (q_us * 1e-6) / 1e9
+    gemm_gbps = gbytes / (g_us * 1e-6) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else 'eager calls'}; "
+        f"GPU {step_gpu_us:.1f} us)  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
+        f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    decode = M <= 16
+    decode = M <= 64  # the small-M GEMM: weights streamed once, below the MFMA ridge point
     gemm_kernel = "gemm_small_kernel" if decode else "gemm_f8_kernel"
     wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
     traffic = measured_traffic(gemm_kernel, wkey)
     if decode:
-        # the small-M GEMM streams the packed weights: HBM-bound
-        roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": gemm_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+        # the small-M GEMM streams the packed weights: HBM-bound.  A decode step is shorter than
+        # the host's two Python calls, so events around each launch in the step also count the
+        # GPU waiting for the host; the kernel's own rate is the back-to-back one.
+        b2b_gbps = gbytes / (g_b2b * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": b2b_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": b2b_gbps / PEAK_HBM_GBPS, "traffic": traffic,
                 "kernel": gemm_kernel, "algorithmic_bytes_per_launch": gbytes,
-                "avg_launch_us": g_us}
+                "avg_launch_us": g_b2b,
+                "timing": "HIP events around 20 launches queued behind a 1 GiB copy (host ahead: "
+                          f"{g_ahead}): the kernel's own duration, which events around one launch of an "
+                          "eager step overstate by the host's launch gaps"}
     else:
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
                 "frac": gemm_tops / PEAK_I8_TOPS, "traffic": traffic,
@@ -421,17 +522,21 @@ def main():
         "config": {"workload": f"{wl.name} M={M} K={K} N={N}", "M": M, "K": K, "N": N,
                    "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,
                    "x_dtype": wl.x_dtype, "y_dtype": wl.y_dtype, "weights": "packed offline",
-                   "buffer_sets": nsets, "group": grp},
+                   "buffer_sets": nsets, "group": grp,
+                   "launch": "one HIP graph replay per step" if graph else "eager calls"},
         "roofline": roof,
         "quantize": {"kernel": quant_kernel, "avg_launch_us": q_us, "gbps": quant_gbps,
                      "frac_hbm": quant_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": qbytes,
                      "back_to_back_us": q_b2b, "back_to_back_gbps": qbytes / (q_b2b * 1e-6) / 1e9,
+                     "back_to_back_host_ahead": q_ahead,
                      "back_to_back_frac_hbm": qbytes / (q_b2b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(quant_kernel, wkey)},
         "gemm": {"kernel": gemm_kernel, "avg_launch_us": g_us, "tops": gemm_tops,
                  "frac_mfma": gemm_tops / PEAK_I8_TOPS, "gbps": gemm_gbps,
-                 "back_to_back_us": g_b2b, "back_to_back_tops": ops / (g_b2b * 1e-6) / 1e12},
+                 "back_to_back_us": g_b2b, "back_to_back_tops": ops / (g_b2b * 1e-6) / 1e12,
+                 "back_to_back_gbps": gbytes / (g_b2b * 1e-6) / 1e9, "back_to_back_host_ahead": g_ahead},
         "layer_us": ms_per_step * 1e3,
+        "step_gpu_us": step_gpu_us,
     }
 
     if not args.no_cpu_baseline:

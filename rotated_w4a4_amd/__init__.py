@@ -104,9 +104,17 @@ def _torch():
     return torch
 
 
-def _stream(device):
-    torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = None
+
+
+def _stream(dev: int) -> int:
+    """The current HIP stream of device index `dev`, as the raw handle the C ABI takes."""
+    global _raw_stream
+    if _raw_stream is None:
+        torch = _torch()
+        fast = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = fast if fast is not None else (lambda d: torch.cuda.current_stream(d).cuda_stream)
+    return _raw_stream(dev)
 
 
 def _dtype_code(t) -> int:
@@ -118,22 +126,20 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
-
-
-def _on_gpu(name, t, device=None):
-    """A tensor the kernels will touch: on a GPU (the same one as `device`)."""
+def _on_gpu(name, t, dev=None) -> int:
+    """A tensor the kernels will touch: on a GPU (device index `dev` if given); returns its index."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    d = t.get_device()
+    if dev is not None and d != dev:
+        raise ValueError(f"{name} is on cuda:{d}, expected cuda:{dev}")
+    return d
 
 
-def _out(name, t, shape, dtype, device):
-    """A caller-provided output: exact shape and dtype, contiguous, same GPU."""
-    _on_gpu(name, t, device)
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+def _out(name, t, shape, dtype, dev):
+    """A caller-provided output: exact shape and dtype, contiguous, on GPU `dev`."""
+    _on_gpu(name, t, dev)
+    if t.shape != shape or t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
@@ -209,7 +215,7 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride along K")
-    _on_gpu("x", x)
+    dev = _on_gpu("x", x)
     M, K = x.shape
     if K != t.K:
         raise ValueError(f"x has {K} channels, the transform {t.K}")
@@ -222,16 +228,17 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
         qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     if sa is None:
         sa = torch.empty((M, K // group), dtype=torch.float32, device=x.device)
-    _out("qa", qa, (M, K // 2), torch.uint8, x.device)
-    _out("sa", sa, (M, K // group), torch.float32, x.device)
+    _out("qa", qa, (M, K // 2), torch.uint8, dev)
+    _out("sa", sa, (M, K // group), torch.float32, dev)
     if mode == "rrs":
         if workspace is None:
             workspace = torch.empty((max(G, 4),), dtype=torch.float32, device=x.device)
-        _on_gpu("workspace", workspace, x.device)
+        _on_gpu("workspace", workspace, dev)
         if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() < G:
             raise ValueError(f"workspace must be a contiguous float32 tensor of at least {G} elements")
-    _check(lib.rw4_quantize_act_g(t.handle, MODES[mode], group, _ptr(x), _dtype_code(x), M, x.stride(0),
-                                  _ptr(qa), _ptr(sa), _ptr(workspace), _stream(x.device)),
+    _check(lib.rw4_quantize_act_g(t.handle, MODES[mode], group, x.data_ptr(), _dtype_code(x), M, x.stride(0),
+                                  qa.data_ptr(), sa.data_ptr(),
+                                  workspace.data_ptr() if workspace is not None else None, _stream(dev)),
            "rw4_quantize_act")
     return qa, sa
 
@@ -244,7 +251,7 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: in
     torch = _torch()
     if w.dim() != 2:
         raise ValueError("w must be 2-D")
-    _on_gpu("w", w)
+    dev = _on_gpu("w", w)
     if layout == "kn":
         K, N = w.shape
         sk, sn = w.stride(0), w.stride(1)
@@ -261,10 +268,10 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: in
         qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
     if sw is None:
         sw = torch.empty((N, K // group), dtype=torch.float32, device=w.device)
-    _out("qw", qw, (N, K // 2), torch.uint8, w.device)
-    _out("sw", sw, (N, K // group), torch.float32, w.device)
-    _check(lib.rw4_pack_weight_g(t.handle, group, _ptr(w), _dtype_code(w), N, sk, sn, _ptr(qw), _ptr(sw),
-                                 _stream(w.device)),
+    _out("qw", qw, (N, K // 2), torch.uint8, dev)
+    _out("sw", sw, (N, K // group), torch.float32, dev)
+    _check(lib.rw4_pack_weight_g(t.handle, group, w.data_ptr(), _dtype_code(w), N, sk, sn, qw.data_ptr(),
+                                 sw.data_ptr(), _stream(dev)),
            "rw4_pack_weight")
     return qw, sw
 
@@ -287,19 +294,19 @@ def dequantize(q, s, out_dtype=None, out=None):
     if s.dim() != 2 or s.shape[0] != M:
         raise ValueError("scale shape does not match the codes")
     group = _group_of(K, s.shape[1])
-    _on_gpu("q", q)
-    _on_gpu("s", s, q.device)
+    dev = _on_gpu("q", q)
+    _on_gpu("s", s, dev)
     if q.dtype != torch.uint8 or s.dtype != torch.float32:
         raise ValueError("q must be uint8 and s float32")
     if not (q.is_contiguous() and s.is_contiguous()):
         raise ValueError("q and s must be contiguous")
     if out is None:
         out = torch.empty((M, K), dtype=out_dtype, device=q.device)
-    _on_gpu("out", out, q.device)
-    if out.dim() != 2 or tuple(out.shape) != (M, K) or out.stride(1) != 1:
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, K) or out.stride(1) != 1:
         raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
-    _check(lib.rw4_dequantize_g(_ptr(q), _ptr(s), M, K, group, _ptr(out), _dtype_code(out), out.stride(0),
-                                _stream(q.device)),
+    _check(lib.rw4_dequantize_g(q.data_ptr(), s.data_ptr(), M, K, group, out.data_ptr(), _dtype_code(out),
+                                out.stride(0), _stream(dev)),
            "rw4_dequantize")
     return out
 
@@ -317,17 +324,18 @@ def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
     if qw.shape[1] != Kh or sa.dim() != 2 or sa.shape[0] != M or sw.shape != (N, sa.shape[1]):
         raise ValueError("operand shapes do not match")
     group = _group_of(K, sa.shape[1])
-    for name, tns, dt in (("qa", qa, torch.uint8), ("sa", sa, torch.float32), ("qw", qw, torch.uint8),
-                          ("sw", sw, torch.float32)):
-        _on_gpu(name, tns, qa.device)
+    dev = _on_gpu("qa", qa)
+    u8, f32 = torch.uint8, torch.float32
+    for name, tns, dt in (("qa", qa, u8), ("sa", sa, f32), ("qw", qw, u8), ("sw", sw, f32)):
+        _on_gpu(name, tns, dev)
         if tns.dtype != dt or not tns.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dt} tensor")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
-    _on_gpu("out", out, qa.device)
-    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
-    _check(lib.rw4_w4a4_gemm_g(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, group, _ptr(out),
-                               _dtype_code(out), out.stride(0), _stream(qa.device)),
+    _check(lib.rw4_w4a4_gemm_g(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, group,
+                               out.data_ptr(), _dtype_code(out), out.stride(0), _stream(dev)),
            "rw4_w4a4_gemm")
     return out

@@ -1,0 +1,90 @@
+"""HIP graph capture of the hot path.
+
+quantize_act + w4a4_gemm only launch kernels on the caller's stream (no
+allocation, no memset, no synchronisation), so a serving loop can record a
+step once into a graph and replay it, paying one graph launch on the host
+instead of two Python calls.  Each case records the step on torch's capture
+stream, then replays it several times with new inputs copied into the
+recorded input buffer and unrelated eager work and synchronisations between
+the replays; every replay must equal, bit for bit, the eager calls on the
+same input (the same kernels run on the same data).
+"""
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import datagen  # noqa: E402
+
+if torch.cuda.is_available():
+    import rotated_w4a4_amd as rw4  # noqa: E402
+    from tests import gpu_util as gu  # noqa: E402
+
+CASES = [
+    # name, workload, overrides: the decode step (Givens layers, small-M GEMM), a prefill
+    # q_proj slice (block-128 Hadamard, tiled GEMM), Rotated Runtime Smooth (two passes and
+    # a fill kernel on the workspace)
+    ("decode16_givens", "decode", dict(M=16, K=1024, N=512)),
+    ("q_proj_h128", "q_proj", dict(M=300, K=1024, N=384)),
+    ("rrs_full_row", "rrs", dict(M=200, K=2048, N=256)),
+]
+
+
+def _inputs(x0):
+    """Three distinct inputs of the same shape whose values stay exact in bf16."""
+    return [x0, torch.roll(x0, 7, dims=0) * 2.0, torch.roll(x0, -3, dims=0) * 0.5]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_graph_replays_match_eager(case):
+    name, kind, kw = case
+    print(f"graph case {name}", flush=True)
+    wl = datagen.make(kind, seed=11, **kw)
+    t = gu.transform_for(wl)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(wl.w).to(gu.DEV))
+    x0 = gu.x_to_device(wl.x, wl.x_dtype)
+    M, K, N = wl.M, wl.K, wl.N
+    G = K // 128
+
+    def buffers():
+        return dict(qa=torch.empty((M, K // 2), dtype=torch.uint8, device=gu.DEV),
+                    sa=torch.empty((M, G), dtype=torch.float32, device=gu.DEV),
+                    ws=torch.zeros((max(G, 4),), dtype=torch.float32, device=gu.DEV),
+                    y=torch.empty((M, N), dtype=torch.bfloat16, device=gu.DEV))
+
+    def step(x, b):
+        rw4.quantize_act(t, x, wl.mode, qa=b["qa"], sa=b["sa"], workspace=b["ws"])
+        rw4.w4a4_gemm(b["qa"], b["sa"], qw, sw, out=b["y"])
+
+    xs = _inputs(x0)
+    refs = []
+    for x in xs:  # eager results, each in buffers of its own
+        b = buffers()
+        step(x, b)
+        refs.append(b)
+    torch.cuda.synchronize()
+
+    x_static = x0.clone()
+    bs = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager run on a side stream before capture
+        step(x_static, bs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(x_static, bs)
+    torch.cuda.synchronize()
+
+    noise_a = torch.randn((512, 512), device=gu.DEV)
+    for rep in range(2):
+        for k, x in enumerate(xs):
+            x_static.copy_(x)
+            _ = noise_a @ noise_a  # unrelated eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for key in ("qa", "sa", "y"):
+                assert torch.equal(bs[key], refs[k][key]), f"{name}: replay {rep}/{k} differs in {key}"
