@@ -342,3 +342,44 @@ def test_small_batch_end_to_end(M):
     t, xd, qa, sa, aref = tp._quant_parity(wl)
     qw, sw, wref = tp._weight_parity(wl, t)
     tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
+
+
+SMALL_ITER = [
+    # M, g, K, N, scale columns to isolate: several K iterations (odd counts, a partial last
+    # one) for 16-, 32- and 64-row tiles and every group size; 32-channel blocks (M <= 16,
+    # N > 12288) with a partial last block
+    (16, 128, 14336, 64, (0, 15, 16, 111)),
+    (5, 64, 2176, 48, (0, 31, 32, 33)),
+    (16, 256, 4352, 40, (0, 7, 8, 16)),
+    (30, 128, 2176, 33, (0, 15, 16)),
+    (64, 128, 1152, 24, (0, 7, 8)),
+    (40, 256, 2304, 20, (0, 7, 8)),
+    (64, 64, 1152, 17, (0, 15, 16, 17)),
+    (3, 128, 256, 12304, (0, 1)),
+    (16, 64, 512, 12296, (0, 7)),
+    (16, 128, 4352, 12304, (0, 15, 16, 33)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_ITER, ids=[f"M{c[0]}_g{c[1]}_K{c[2]}_N{c[3]}" for c in SMALL_ITER])
+def test_small_batch_iterations_exact(case):
+    """The decode kernel over several K iterations and with 32-channel blocks:
+    with sa = 1 and sw one-hot on scale column j, Y is the exact integer
+    group sum of column j (fp32 output), for columns on both sides of the
+    iteration boundaries."""
+    M, g, K, N, cols = case
+    print(f"small-M iterations M={M} g={g} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M * 7 + g + K + N)
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[M - 1, K - g:], cw[N - 1, K - g:] = -7, 7     # -g * 49 in the last group of the last row and column
+    qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
+    qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
+    acc = oracle.group_accumulators(ca, cw, g)
+    G = K // g
+    sa = torch.ones((M, G), dtype=torch.float32, device=gu.DEV)
+    for j in cols + (G - 1,):
+        swn = np.zeros((N, G), dtype=np.float32)
+        swn[:, j] = 1.0
+        y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
+        assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"M {M} g {g} K {K} N {N} column {j}"
