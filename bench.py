@@ -17,7 +17,10 @@ Prints one JSON line (stdout).  Per-kernel times come from HIP events
 (created without the system-scope fence, so recording them flushes no
 caches) recorded on the stream the library launches on; the GEMM is the
 dominant kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported,
-the quantize kernel's HBM roofline beside it.  Each kernel is also timed
+the quantize kernel's HBM roofline beside it.  Steps are issued through
+calls prepared once per buffer set (arguments checked and marshalled once,
+as a serving loop reuses its buffers; `--launch eager` checks on every
+call).  Each kernel is also timed
 alone, 20 launches queued behind a 1 GiB device copy so that the host is
 ahead of the GPU: for decode-sized and KV-cache steps, which are shorter
 than the host's Python calls, that is the kernel's own duration and the
@@ -156,9 +159,11 @@ def parse():
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64", "tiny", "kv"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
-    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
-                    help="how a step is issued: eager Python calls, or one HIP graph replay per step "
-                         "(a replay costs more GPU time than the two kernels of a decode step)")
+    ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
+                    help="how a step is issued: calls prepared once per buffer set (arguments checked "
+                         "and marshalled once, as a serving loop reuses its buffers), the checking Python "
+                         "functions on every call, or one HIP graph replay per step (a replay costs more "
+                         "GPU time than the two kernels of a decode step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -267,14 +272,31 @@ def main_kv(args, torch, rw4, gu, dev):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
+    if args.launch == "eager":
+        def q_only(i):
+            st = sets[i % nsets]
+            rw4.quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp)
+
+        def d_only(i):
+            st = sets[i % nsets]
+            rw4.dequantize(st["qa"], st["sa"], out=st["out"])
+    else:
+        qc = [rw4.prepare_quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp) for st in sets]
+        dc = [rw4.prepare_dequantize(st["qa"], st["sa"], out=st["out"]) for st in sets]
+
+        def q_only(i):
+            qc[i % nsets]()
+
+        def d_only(i):
+            dc[i % nsets]()
+
     def step(i, ev=None):
-        st = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
-        rw4.quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp)
+        q_only(i)
         if ev is not None:
             ev[1].record(stream)
-        rw4.dequantize(st["qa"], st["sa"], out=st["out"])
+        d_only(i)
         if ev is not None:
             ev[2].record(stream)
 
@@ -293,26 +315,22 @@ def main_kv(args, torch, rw4, gu, dev):
 
     for i in range(args.warmup):
         run(i)
-    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
+    # the kernels' durations come from the back-to-back runs below; the timed region is
+    # bracketed as a whole (events around each short launch would slow the host further)
+    r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record(stream)
     for i in range(args.steps):
-        run(args.warmup + i, events[i])
+        run(args.warmup + i)
+    r1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_gpu_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[2]) for e in events]))
+    step_gpu_us = 1e3 * r0.elapsed_ms(r1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = (qbytes + dbytes) / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else 'eager calls'}; "
+    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else args.launch + ' calls'}; "
         f"GPU {step_gpu_us:.1f} us)")
-
-    def q_only(i):
-        st = sets[i % nsets]
-        rw4.quantize_act(t, st["x"], "group128", qa=st["qa"], sa=st["sa"], group=grp)
-
-    def d_only(i):
-        st = sets[i % nsets]
-        rw4.dequantize(st["qa"], st["sa"], out=st["out"])
 
     # the kernels run about as long as the host takes per Python call: time them with the host ahead
     (q_b2b, q_ahead), (d_b2b, d_ahead) = gpu_bound_us(torch, stream, q_only), gpu_bound_us(torch, stream, d_only)
@@ -324,7 +342,7 @@ def main_kv(args, torch, rw4, gu, dev):
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in/out, int4 codes, fp32 transform and scales", "data": "synthetic",
         "config": {"workload": f"kv M={M} K={K} (8 heads x 128)", "group": grp, "buffer_sets": nsets,
-                   "launch": "one HIP graph replay per step" if graph else "eager calls"},
+                   "launch": "one HIP graph replay per step" if graph else args.launch + " calls"},
         "step_gpu_us": step_gpu_us,
         "roofline": {"bound": "hbm", "achieved": qb_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": qb_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quant_h128_act_kernel",
@@ -410,14 +428,32 @@ def main():
 
     stream = torch.cuda.current_stream(dev).cuda_stream  # the stream the kernels run on
 
+    if args.launch == "eager":
+        def q_call(i):
+            s = sets[i % nsets]
+            rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"], group=grp)
+
+        def g_call(i):
+            s = sets[i % nsets]
+            rw4.w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"])
+    else:
+        qc = [rw4.prepare_quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"], group=grp)
+              for s in sets]
+        gc = [rw4.prepare_w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"]) for s in sets]
+
+        def q_call(i):
+            qc[i % nsets]()
+
+        def g_call(i):
+            gc[i % nsets]()
+
     def step(i, ev=None):
-        s = sets[i % nsets]
         if ev is not None:
             ev[0].record(stream)
-        rw4.quantize_act(t, s["x"], wl.mode, qa=s["qa"], sa=s["sa"], workspace=s["ws"], group=grp)
+        q_call(i)
         if ev is not None:
             ev[1].record(stream)
-        rw4.w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"])
+        g_call(i)
         if ev is not None:
             ev[2].record(stream)
 
@@ -438,45 +474,44 @@ def main():
         run(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, events on the launch stream
-    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, events on the launch stream.  Decode-sized steps
+    # take the kernels' durations from the back-to-back runs below (events around each of
+    # their launches would count host gaps, and recording them slows the host further), so
+    # only the whole region is bracketed there.
+    decode = M <= 64  # the small-M GEMM: weights streamed once, below the MFMA ridge point
+    per_step = not decode and not graph
+    events = [[HipEvent() for _ in range(3)] for _ in range(args.steps if per_step else 0)]
+    r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record(stream)
     for i in range(args.steps):
-        run(args.warmup + i, events[i])
+        run(args.warmup + i, events[i] if per_step else None)
+    r1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * M * N * K
-    step_gpu_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[2]) for e in events]))
-    if graph:
-        q_us = g_us = float("nan")  # replaced by the back-to-back times below
-    else:
+    step_gpu_us = 1e3 * r0.elapsed_ms(r1) / args.steps
+    if per_step:
         q_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[1]) for e in events]))
         g_us = 1e3 * float(np.mean([e[1].elapsed_ms(e[2]) for e in events]))
+    else:
+        q_us = g_us = float("nan")  # replaced by the back-to-back times below
     layer_tops = ops / (ms_per_step * 1e-3) / 1e12
 
     # each kernel alone, launched back to back behind a copy that lets the host run ahead
-    def q_only(i):
-        st = sets[i % nsets]
-        rw4.quantize_act(t, st["x"], wl.mode, qa=st["qa"], sa=st["sa"], workspace=st["ws"], group=grp)
-
-    def g_only(i):
-        st = sets[i % nsets]
-        rw4.w4a4_gemm(st["qa"], st["sa"], st["qw"], st["sw"], out=st["y"])
-
-    (q_b2b, q_ahead), (g_b2b, g_ahead) = gpu_bound_us(torch, stream, q_only), gpu_bound_us(torch, stream, g_only)
+    (q_b2b, q_ahead), (g_b2b, g_ahead) = gpu_bound_us(torch, stream, q_call), gpu_bound_us(torch, stream, g_call)
     log(f"back-to-back (host ahead: {q_ahead and g_ahead}): quantize {q_b2b:.2f} us, gemm {g_b2b:.2f} us")
-    if graph:  # per-kernel times of a graph step: the kernels alone, back to back
+    if not per_step:  # per-kernel times: the kernels alone, back to back
         q_us, g_us = q_b2b, g_b2b
     gemm_tops = ops / (g_us * 1e-6) / 1e12
     quant_gbps = qbytes / (q_us * 1e-6) / 1e9
     gemm_gbps = gbytes / (g_us * 1e-6) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else 'eager calls'}; "
+    log(f"step {ms_per_step * 1e3:.1f} us ({'one graph launch' if graph else args.launch + ' calls'}; "
         f"GPU {step_gpu_us:.1f} us)  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
         f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    decode = M <= 64  # the small-M GEMM: weights streamed once, below the MFMA ridge point
     gemm_kernel = "gemm_small_kernel" if decode else "gemm_f8_kernel"
     wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
     traffic = measured_traffic(gemm_kernel, wkey)
@@ -523,7 +558,7 @@ def main():
                    "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,
                    "x_dtype": wl.x_dtype, "y_dtype": wl.y_dtype, "weights": "packed offline",
                    "buffer_sets": nsets, "group": grp,
-                   "launch": "one HIP graph replay per step" if graph else "eager calls"},
+                   "launch": "one HIP graph replay per step" if graph else args.launch + " calls"},
         "roofline": roof,
         "quantize": {"kernel": quant_kernel, "avg_launch_us": q_us, "gbps": quant_gbps,
                      "frac_hbm": quant_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": qbytes,

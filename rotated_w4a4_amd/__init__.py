@@ -11,6 +11,8 @@ not been built (``python -m rotated_w4a4_amd._build``).
     qw, sw = pack_weight(t, w)                       # w: [K, N] (offline)
     qa, sa = quantize_act(t, x)                      # x: [M, K] bf16 / fp32
     y = w4a4_gemm(qa, sa, qw, sw, torch.bfloat16)    # [M, N]
+
+    step = prepare_w4a4_gemm(qa, sa, qw, sw, out=y)  # checked once; step() launches again
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
-    "dequantize", "status_str", "version", "EXPORTED_SYMBOLS",
+    "dequantize", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
+    "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librw4.so")
@@ -143,6 +146,29 @@ def _out(name, t, shape, dtype, dev):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
+class Call:
+    """One library call with its arguments checked and marshalled once.
+
+    Calling it launches the kernels again on the current stream of the
+    tensors' GPU, with the same buffers (a serving loop reuses its buffers
+    every step; this skips the per-call checks, which cost the host more
+    time than a decode-sized kernel runs).  It holds references to every
+    tensor and transform it uses, so they stay allocated while it exists.
+    """
+
+    __slots__ = ("_fn", "_args", "_dev", "_what", "_keep", "result")
+
+    def __init__(self, fn, args, dev, what, keep, result):
+        self._fn, self._args, self._dev, self._what = fn, args, dev, what
+        self._keep, self.result = keep, result
+
+    def __call__(self):
+        status = self._fn(*self._args, _stream(self._dev))
+        if status != RW4_OK:
+            raise RW4Error(status, self._what)
+        return self.result
+
+
 class Transform:
     """Owns a library transform object (a host struct plus device tables)."""
 
@@ -212,6 +238,12 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
     workspace of K/128 fp32 is allocated unless given (it receives s_g).
     mode "group128" means per-group scales, of `group` channels.
     """
+    return prepare_quantize_act(t, x, mode, qa, sa, workspace, group)()
+
+
+def prepare_quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, workspace=None,
+                         group: int = 128) -> Call:
+    """quantize_act checked and marshalled once; calling the result runs it (returns (qa, sa))."""
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride along K")
@@ -236,11 +268,9 @@ def quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=None, work
         _on_gpu("workspace", workspace, dev)
         if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() < G:
             raise ValueError(f"workspace must be a contiguous float32 tensor of at least {G} elements")
-    _check(lib.rw4_quantize_act_g(t.handle, MODES[mode], group, x.data_ptr(), _dtype_code(x), M, x.stride(0),
-                                  qa.data_ptr(), sa.data_ptr(),
-                                  workspace.data_ptr() if workspace is not None else None, _stream(dev)),
-           "rw4_quantize_act")
-    return qa, sa
+    args = (t.handle, MODES[mode], group, x.data_ptr(), _dtype_code(x), M, x.stride(0), qa.data_ptr(),
+            sa.data_ptr(), workspace.data_ptr() if workspace is not None else None)
+    return Call(lib.rw4_quantize_act_g, args, dev, "rw4_quantize_act", (t, x, workspace), (qa, sa))
 
 
 def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: int = 128):
@@ -286,6 +316,11 @@ def dequantize(q, s, out_dtype=None, out=None):
     """x_hat [M, K] = codes * group scale (transformed domain), fp32 or bf16.
 
     The group size is K divided by the number of scale columns."""
+    return prepare_dequantize(q, s, out_dtype, out)()
+
+
+def prepare_dequantize(q, s, out_dtype=None, out=None) -> Call:
+    """dequantize checked and marshalled once; calling the result runs it (returns out)."""
     torch = _torch()
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
@@ -305,16 +340,19 @@ def dequantize(q, s, out_dtype=None, out=None):
     _on_gpu("out", out, dev)
     if out.dim() != 2 or out.shape != (M, K) or out.stride(1) != 1:
         raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
-    _check(lib.rw4_dequantize_g(q.data_ptr(), s.data_ptr(), M, K, group, out.data_ptr(), _dtype_code(out),
-                                out.stride(0), _stream(dev)),
-           "rw4_dequantize")
-    return out
+    args = (q.data_ptr(), s.data_ptr(), M, K, group, out.data_ptr(), _dtype_code(out), out.stride(0))
+    return Call(lib.rw4_dequantize_g, args, dev, "rw4_dequantize", (q, s), out)
 
 
 def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
     """Y [M, N] = sum over groups of sa * sw * exact integer group products (fp32 epilogue).
 
     The group size is K divided by the number of scale columns."""
+    return prepare_w4a4_gemm(qa, sa, qw, sw, out_dtype, out)()
+
+
+def prepare_w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None) -> Call:
+    """w4a4_gemm checked and marshalled once; calling the result runs it (returns out)."""
     torch = _torch()
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
@@ -335,7 +373,6 @@ def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):
     _on_gpu("out", out, dev)
     if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
-    _check(lib.rw4_w4a4_gemm_g(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, group,
-                               out.data_ptr(), _dtype_code(out), out.stride(0), _stream(dev)),
-           "rw4_w4a4_gemm")
-    return out
+    args = (qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, group, out.data_ptr(),
+            _dtype_code(out), out.stride(0))
+    return Call(lib.rw4_w4a4_gemm_g, args, dev, "rw4_w4a4_gemm", (qa, sa, qw, sw), out)
