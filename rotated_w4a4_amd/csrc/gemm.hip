@@ -19,17 +19,19 @@
 // unchanged.
 //
 // Kernels:
-//   gemm_f8_kernel     M > 16: 128 x 128 block tiles, 4 waves of 64 x 64,
+//   gemm_f8_kernel     large products: 128 x 128 block tiles, 4 waves of 64 x 64,
 //                      v_mfma_scale_f32_32x32x64_f8f6f4 (2 per group per
 //                      32 x 32 tile); the scale products sa * sw of a tile
 //                      come from one v_mfma_f32_32x32x16_bf16 on a 3-way
 //                      bf16 split of each scale, split once per block and
 //                      group into LDS; the VALU unpacks and accumulates.
-//   gemm_small_kernel  M <= 64 (decode, small batches): 16 or 32 output
-//                      channels per block, the eight waves split K; A and
-//                      the scales staged in LDS per iteration, the weights
-//                      read straight into registers, one
-//                      v_mfma_scale_f32_16x16x128_f8f6f4 per 128 codes.
+//   gemm_small_kernel  M <= 64, and batches up to 1024 rows whose tiled grid
+//                      would have fewer than 128 blocks (in 64-row chunks,
+//                      grid y): 16 or 32 output channels per block, the
+//                      eight waves split K; A and the scales staged in LDS
+//                      per iteration, the weights read straight into
+//                      registers, one v_mfma_scale_f32_16x16x128_f8f6f4 per
+//                      128 codes.
 // MFMA result layouts: for 32 x 32, lane l holds
 // D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r = 0..15; for 16 x 16,
 // D[4 (l / 16) + r][l % 16], r = 0..3.
@@ -550,8 +552,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel (decode and small batches, M <= 64): one block of 8 waves
-// per CT tiles of 16 output channels.  K is cut into slices of 128 codes,
+// Small-M kernel (decode and small batches): one block of 8 waves per CT
+// tiles of 16 output channels and one chunk of 16 MT rows of A (grid y).  K is cut into slices of 128 codes,
 // one v_mfma_scale_f32_16x16x128_f8f6f4 per slice, 16-channel tile and
 // 16-row A tile; lane l supplies row l % 16 and codes
 // [32 (l / 16), 32 (l / 16) + 32) of the slice for both operands.  An
@@ -632,9 +634,11 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
   const int64_t rowbytes = K / 2;
   const int64_t n0 = int64_t(blockIdx.x) * 16 * CT;
   const int64_t nrows = N - n0 < 16 * CT ? N - n0 : 16 * CT;
+  const int64_t m0 = int64_t(blockIdx.y) * 16 * MT;  // this block's chunk of A rows
+  const int64_t mrows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
   const int64_t NI = (SL + C::GB - 1) / C::GB;  // iterations
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa, M * rowbytes);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa, M * GS * 4);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(qa + m0 * rowbytes, mrows * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + m0 * GS, mrows * GS * 4);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + n0 * rowbytes, nrows * rowbytes);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw + n0 * GS, nrows * GS * 4);
 
@@ -786,26 +790,42 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mt * 16 + part * 4 + r;
-      if (m < M && bn < N) store_y<BF16>(y, ldy, m, bn, v[r]);
+      if (m < mrows && bn < N) store_y<BF16>(y, ldy, m0 + m, bn, v[r]);
     }
   }
+}
+
+// Which kernel runs a product.  The tiled kernel gives one 128 x 128 tile per
+// block; below about one block per CU its time is one block's K loop (about
+// 30 us at K = 4096 for any M up to 1024 at N = 4096, measured), while the
+// small-M kernel, run over 64-row chunks of A in one launch, streams the
+// whole product at about 600 TOPS.  With ~4.5 TOPS per busy CU for the tiled
+// kernel, the small kernel wins while the tiled grid has fewer than 128 blocks
+// (measured crossover at N = 4096: M = 512, small 29.8 us against 31.2 us).
+constexpr int64_t kSmallMaxM = 1024;
+constexpr int64_t kTiledMinBlocks = 128;
+__host__ __forceinline__ bool use_small_kernel(int64_t M, int64_t N) {
+  if (M <= 64) return true;
+  return M <= kSmallMaxM && ((M + 127) / 128) * ((N + 127) / 128) < kTiledMinBlocks;
 }
 
 template <int GSZ>
 hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                          hipStream_t st) {
-  if (M <= 64) {  // decode and small batches: weights streamed once, 16 CT output channels per block
+  if (use_small_kernel(M, N)) {  // 16 CT output channels per block, the rows in chunks of 16 MT (grid y)
     auto run = [&](auto mt_const, auto ct_const) {
       constexpr int MT = decltype(mt_const)::value, CT = decltype(ct_const)::value;
       const int64_t blocks = (N + 16 * CT - 1) / (16 * CT);
-      if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+      const int64_t chunks = (M + 16 * MT - 1) / (16 * MT);
+      if (blocks > 0x7FFFFFFF || chunks > 65535) return hipErrorInvalidValue;
+      const dim3 grid{unsigned(blocks), unsigned(chunks), 1u};
       if (y_bf16)
-        hipLaunchKernelGGL((gemm_small_kernel<true, GSZ, MT, CT>), dim3(blocks), dim3(kSmallThreads), 0, st, qa,
-                           sa, qw, sw, M, N, K, y, ldy);
+        hipLaunchKernelGGL((gemm_small_kernel<true, GSZ, MT, CT>), grid, dim3(kSmallThreads), 0, st, qa, sa, qw,
+                           sw, M, N, K, y, ldy);
       else
-        hipLaunchKernelGGL((gemm_small_kernel<false, GSZ, MT, CT>), dim3(blocks), dim3(kSmallThreads), 0, st, qa,
-                           sa, qw, sw, M, N, K, y, ldy);
+        hipLaunchKernelGGL((gemm_small_kernel<false, GSZ, MT, CT>), grid, dim3(kSmallThreads), 0, st, qa, sa, qw,
+                           sw, M, N, K, y, ldy);
       return hipGetLastError();
     };
     using I1 = std::integral_constant<int, 1>;

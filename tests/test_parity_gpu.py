@@ -206,6 +206,12 @@ RAGGED = [
     ("h4096_rrs_f32", 9, 4096, 16, ("hadamard", 4096), "rrs", "f32"),
     ("givens_prefill", 70, 512, 96, ("givens", 3), "group128", "bf16"),
     ("givens_f32", 5, 256, 17, ("givens", 8), "group128", "f32"),
+    # batches the tiled kernel takes (M > 1024, or a tiled grid of >= 128 blocks), partial
+    # tiles on both edges and output rows that break 16-byte alignment; the cases above with
+    # 64 < M <= 1024 and few output tiles run on the small-M kernel in 64-row chunks
+    ("h128_tiled_m1100", 1100, 256, 72, ("hadamard", 128), "group128", "bf16"),
+    ("h128_tiled_wide", 200, 256, 16257, ("hadamard", 128), "group128", "bf16"),
+    ("givens_tiled_m1030", 1030, 256, 131, ("givens", 8), "group128", "bf16"),
 ]
 
 

@@ -317,9 +317,9 @@ def test_strided_activations_and_output(case):
 @pytest.mark.parametrize("g", [64, 128, 256])
 @pytest.mark.parametrize("M", [17, 32, 33, 50, 64, 65])
 def test_small_batch_accumulators_exact(M, g):
-    """Small batches (the decode kernel with 2 or 4 row tiles up to M = 64,
-    the tiled kernel above): exact integer group sums by group isolation,
-    with extreme accumulators in the last rows."""
+    """Small batches (the small-M kernel with 2 or 4 row tiles up to M = 64,
+    two 64-row chunks at M = 65): exact integer group sums by group
+    isolation, with extreme accumulators in the last rows."""
     K, N = 512, 40
     rng = np.random.default_rng(1000 + M + g)
     ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
@@ -358,12 +358,47 @@ SMALL_ITER = [
     (3, 128, 256, 12304, (0, 1)),
     (16, 64, 512, 12296, (0, 7)),
     (16, 128, 4352, 12304, (0, 15, 16, 33)),
+    # batches above 64 rows with few output tiles: 64-row chunks of A in one launch
+    (100, 128, 2176, 40, (0, 15, 16)),
+    (257, 64, 1152, 24, (0, 15, 16, 17)),
+    (1000, 256, 512, 48, (0, 1)),
 ]
+
+TILED_EDGES = [
+    # M, g, K, N: products the tiled kernel takes (M > 1024, or a tiled grid of >= 128
+    # blocks), with partial tiles on both edges and unaligned output rows
+    (1100, 64, 384, 200),
+    (1030, 256, 512, 129),
+    (300, 128, 256, 5499),
+]
+
+
+@pytest.mark.parametrize("case", TILED_EDGES, ids=[f"M{c[0]}_g{c[1]}_K{c[2]}_N{c[3]}" for c in TILED_EDGES])
+def test_tiled_kernel_edges_exact(case):
+    """Exact integer group sums through the tiled kernel at ragged shapes (group
+    isolation: sa = 1, sw one-hot on the first and the last scale column)."""
+    M, g, K, N = case
+    print(f"tiled edges M={M} g={g} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M + g + K + N)
+    ca = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ca[M - 1, :g], cw[N - 1, :g] = 7, -7
+    qa = torch.from_numpy(oracle.pack_int4(ca)).to(gu.DEV)
+    qw = torch.from_numpy(oracle.pack_int4(cw)).to(gu.DEV)
+    acc = oracle.group_accumulators(ca, cw, g)
+    G = K // g
+    sa = torch.ones((M, G), dtype=torch.float32, device=gu.DEV)
+    for j in (0, G - 1):
+        swn = np.zeros((N, G), dtype=np.float32)
+        swn[:, j] = 1.0
+        y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
+        assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"M {M} g {g} K {K} N {N} column {j}"
 
 
 @pytest.mark.parametrize("case", SMALL_ITER, ids=[f"M{c[0]}_g{c[1]}_K{c[2]}_N{c[3]}" for c in SMALL_ITER])
 def test_small_batch_iterations_exact(case):
-    """The decode kernel over several K iterations and with 32-channel blocks:
+    """The small-M kernel over several K iterations, with 32-channel blocks and over
+    64-row chunks of A:
     with sa = 1 and sw one-hot on scale column j, Y is the exact integer
     group sum of column j (fp32 output), for columns on both sides of the
     iteration boundaries."""
