@@ -156,7 +156,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
-                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64", "tiny", "kv"])
+                    choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
+                             "decode128", "decode256", "tiny", "kv"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
@@ -512,7 +513,10 @@ def main():
         f"GPU {step_gpu_us:.1f} us)  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
         f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    gemm_kernel = "gemm_small_kernel" if decode else "gemm_f8_kernel"
+    # the library's routing: the small-M kernel up to 64 rows, and up to 1024 rows (in 64-row
+    # chunks) while the 128 x 128-tile grid would have fewer than 128 blocks
+    small = M <= 64 or (M <= 1024 and ((M + 127) // 128) * ((N + 127) // 128) < 128)
+    gemm_kernel = "gemm_small_kernel" if small else "gemm_f8_kernel"
     wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
     traffic = measured_traffic(gemm_kernel, wkey)
     if decode:

@@ -149,7 +149,7 @@ def _group_quant_parity(x64, xdt, K, group, signs=None):
     return t, spec, qa, sa, ref
 
 
-@pytest.mark.parametrize("M", [300, 7])
+@pytest.mark.parametrize("M", [1100, 300, 7])  # 1100: the tiled kernel; 300 and 7: the small-M kernel
 @pytest.mark.parametrize("signed", [False, True])
 def test_group256_end_to_end(M, signed):
     K, N = 1024, 200
@@ -232,7 +232,7 @@ def test_givens_fp16_angles():
     tp._gemm_parity(wl, qa, sa, qw, sw, np.arange(M), aref, wref)
 
 
-@pytest.mark.parametrize("M", [300, 7])
+@pytest.mark.parametrize("M", [1100, 300, 7])  # 1100: the tiled kernel; 300 and 7: the small-M kernel
 def test_group64_end_to_end(M):
     """64-wide groups (the article's choice for outlier-heavy layers) through
     the GEMM: both kernels (large M and decode-sized M)."""
