@@ -229,6 +229,14 @@ def algorithmic_bytes(wl, group=128):
     return quant, gemm
 
 
+def gemm_kernel_for(M, N):
+    """The GEMM kernel the library runs for an M x N product: the small-M kernel up to 64
+    rows, and up to 1024 rows (in 64-row chunks) while the 128 x 128-tile grid would have
+    fewer than 128 blocks; the tiled kernel otherwise."""
+    small = M <= 64 or (M <= 1024 and ((M + 127) // 128) * ((N + 127) // 128) < 128)
+    return "gemm_small_kernel" if small else "gemm_f8_kernel"
+
+
 def cpu_baseline(wl, rows):
     """The oracle as it stands on a sample of `rows` tokens: quantize_act + w4a4_gemm.
 
@@ -513,10 +521,7 @@ def main():
         f"GPU {step_gpu_us:.1f} us)  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
         f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    # the library's routing: the small-M kernel up to 64 rows, and up to 1024 rows (in 64-row
-    # chunks) while the 128 x 128-tile grid would have fewer than 128 blocks
-    small = M <= 64 or (M <= 1024 and ((M + 127) // 128) * ((N + 127) // 128) < 128)
-    gemm_kernel = "gemm_small_kernel" if small else "gemm_f8_kernel"
+    gemm_kernel = gemm_kernel_for(M, N)
     wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
     traffic = measured_traffic(gemm_kernel, wkey)
     if decode:
