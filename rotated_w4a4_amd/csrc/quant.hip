@@ -831,18 +831,22 @@ int grid_for_waves(int64_t waves_needed, int64_t cap_blocks) {
 }
 
 // Row-major activations.  One row per wave while all (row, quad) items fit
-// in one generation of resident waves (32 per CU), else about three rows per
-// wave: measured best at 2048 x 4096 and 4096 x 14336 (more rows per wave
-// leave the memory system less work in flight, fewer cost more setup; a
-// deeper prefetch only added work at the end of each wave).
+// in one generation of resident waves (32 per CU), two rows up to two
+// generations, else about three rows per wave: measured best at 2048 x 4096
+// and 4096 x 14336 (more rows per wave leave the memory system less work in
+// flight, fewer cost more setup; a deeper prefetch only added work at the
+// end of each wave, and a wave covering 2 or 4 quads of a row instead of one
+// was 7-14 % slower at 4096 x 14336).
 template <int GS>
 hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t* sign_mask, int64_t rows,
                            int64_t G, uint8_t* q, float* s, float post, hipStream_t st) {
   constexpr int D = 1;
   constexpr int64_t kResidentWaves = 256 * 32;
-  constexpr int64_t kRowsPerWave = 3;
   const int64_t Q = (G + 3) / 4;
-  int64_t R = Q * rows <= kResidentWaves ? rows : (rows + kRowsPerWave - 1) / kRowsPerWave;
+  // rows per wave: 1 while the items fit one generation of resident waves, 2 up to two
+  // generations (2048 x 4096: 6.05 us against 6.36 us with 3), else 3 (4096 x 14336)
+  const int64_t rows_per_wave = Q * rows <= kResidentWaves ? 1 : Q * rows <= 2 * kResidentWaves ? 2 : 3;
+  int64_t R = (rows + rows_per_wave - 1) / rows_per_wave;
   if (R < 1) R = 1;
   const int64_t blocks = (Q * R + 3) / 4;
   if (Q * R > 0x7FFFFFFF - 3 || G * 64 * (bf16 ? 4 : 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
