@@ -418,3 +418,22 @@ def test_small_batch_iterations_exact(case):
         swn[:, j] = 1.0
         y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, torch.from_numpy(swn).to(gu.DEV), torch.float32))
         assert np.array_equal(y, acc[:, :, j].astype(np.float64)), f"M {M} g {g} K {K} N {N} column {j}"
+
+
+def test_many_rows_cross_the_grid_limit():
+    """70 001 rows: the dequantize launcher splits rows into launches of at most
+    65 535 (the grid's y limit), and the quantizer gives each wave several rows.
+    Quantize against the oracle on rows around the split, dequantize exactly."""
+    M, K = 70001, 256
+    print(f"many rows M={M} K={K}", flush=True)
+    rng = np.random.default_rng(70001)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    wl = datagen.Workload("many_rows", M, K, 0, x, "bf16", np.zeros((K, 0), np.float32), ("hadamard", 128),
+                          "group128", "bf16")
+    rows = np.r_[0:3, 65530:65540, M - 3:M]
+    t, xd, qa, sa, ref = tp._quant_parity(wl, rows)
+    codes = tp._unpack(qa).astype(np.float64)
+    sa_np = gu.to_np(sa).astype(np.float64)
+    got = gu.to_np(rw4.dequantize(qa, sa, torch.float32))
+    want = (codes * np.repeat(sa_np, 128, axis=1)).astype(np.float32).astype(np.float64)
+    assert np.array_equal(got, want)
