@@ -763,6 +763,23 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
   const int64_t row0 = (blockIdx.x / G) * ROWS;
   const int nrows = int(M - row0 < ROWS ? M - row0 : ROWS);
 
+  const uint16_t* idx = lut_idx + grp * L * 64;
+  const float2* cs = lut_cs + grp * L * 64;
+  // the table entries of 8 layers are loaded together (one memory latency
+  // per 8 layers instead of one per layer), then applied in order; the
+  // first 8 are requested before the rows, so both latencies overlap
+  constexpr int LB = 8;
+  uint32_t pr[LB];
+  float2 t[LB];
+  auto load_tables = [&](int l0) {
+#pragma unroll
+    for (int k = 0; k < LB; ++k) {
+      const bool in = l0 + k < L;
+      pr[k] = in ? idx[(l0 + k) * 64 + lane] : 0u;
+      t[k] = in ? cs[(l0 + k) * 64 + lane] : make_float2(1.0f, 0.0f);
+    }
+  };
+  load_tables(0);
   const float sc0 = chan_scale[grp * kGroup + 2 * lane];
   const float sc1 = chan_scale[grp * kGroup + 2 * lane + 1];
   for (int r = 0; r < nrows; ++r) {
@@ -772,20 +789,8 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
     buf[r][2 * lane + 1] = v[1];
   }
   __syncthreads();
-  const uint16_t* idx = lut_idx + grp * L * 64;
-  const float2* cs = lut_cs + grp * L * 64;
-  // the table entries of 8 layers are loaded together (one memory latency
-  // per 8 layers instead of one per layer), then applied in order
-  constexpr int LB = 8;
   for (int l0 = 0; l0 < L; l0 += LB) {
-    uint32_t pr[LB];
-    float2 t[LB];
-#pragma unroll
-    for (int k = 0; k < LB; ++k) {
-      const bool in = l0 + k < L;
-      pr[k] = in ? idx[(l0 + k) * 64 + lane] : 0u;
-      t[k] = in ? cs[(l0 + k) * 64 + lane] : make_float2(1.0f, 0.0f);
-    }
+    if (l0 > 0) load_tables(l0);
 #pragma unroll
     for (int k = 0; k < LB; ++k) {
       if (l0 + k >= L) break;
