@@ -203,7 +203,7 @@ rw4_status rw4_w4a4_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, 
  *                   signed) in RW4_ACT_GROUP128 mode (per-group scales);
  *   pack_weight_g   64 and 256 with a block-128 Hadamard transform;
  *   w4a4_gemm_g     64 (each 64-wide K-half is rescaled on its own; the
- *                   64-group kernel for M > 16 needs 96 KiB of LDS, one
+ *                   large-product kernel then needs 96 KiB of LDS, one
  *                   block per CU) and 256 (the two 128-wide halves of a
  *                   group accumulate into one exact integer sum,
  *                   |sum| <= 256 * 49, before the rescale); K stays a
