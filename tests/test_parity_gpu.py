@@ -276,8 +276,11 @@ def test_zero_weights_and_empty_calls():
     assert not qw.any() and not sw.any()
 
 
-def test_bitwise_determinism():
-    wl = datagen.make("q_proj", M=512, K=4096, N=1024)
+@pytest.mark.parametrize("shape", [(512, 4096, 1024), (2048, 1024, 1024), (16, 4096, 12304)],
+                         ids=["small_kernel_chunks", "tiled_kernel", "small_kernel_32ch"])
+def test_bitwise_determinism(shape):
+    M, K, N = shape
+    wl = datagen.make("q_proj", M=M, K=K, N=N)
     t = gu.transform_for(wl)
     x = gu.x_to_device(wl.x, wl.x_dtype)
     w = torch.from_numpy(wl.w).to(gu.DEV)
