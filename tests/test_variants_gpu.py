@@ -437,3 +437,30 @@ def test_many_rows_cross_the_grid_limit():
     got = gu.to_np(rw4.dequantize(qa, sa, torch.float32))
     want = (codes * np.repeat(sa_np, 128, axis=1)).astype(np.float32).astype(np.float64)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_tiled_kernel_strided_output(out):
+    """The tiled kernel (M > 1024) writing into a column slice of a wider
+    output (ldy > N, a row pitch that is not a multiple of 16 bytes, so the
+    element-store path): the same values as the contiguous call, and the
+    padding untouched."""
+    M, K, N = 1100, 256, 200
+    rng = np.random.default_rng(303)
+    x = datagen.round_to_bf16(datagen.outlier_activations(rng, M, K))
+    w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
+    t = rw4.Transform.hadamard(K, 128)
+    qa, sa = rw4.quantize_act(t, gu.x_to_device(x, "bf16"))
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(w).to(gu.DEV))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    y0 = rw4.w4a4_gemm(qa, sa, qw, sw, dt)
+    c0 = 16 // wide_elem_bytes(dt)  # the output base must stay 16-byte aligned; its row pitch need not
+    wide = torch.full((M, N + 27), 5.0, dtype=dt, device=gu.DEV)
+    rw4.w4a4_gemm(qa, sa, qw, sw, out=wide[:, c0:c0 + N])
+    torch.cuda.synchronize()
+    assert torch.equal(y0, wide[:, c0:c0 + N])
+    assert torch.all(wide[:, :c0] == 5.0) and torch.all(wide[:, c0 + N:] == 5.0)
+
+
+def wide_elem_bytes(dt):
+    return 2 if dt == torch.bfloat16 else 4
