@@ -221,13 +221,22 @@ def workload(name):
     return datagen.make(name)
 
 
+def givens_table_bytes(K, layers):
+    """The Givens lookup table the activation kernel reads: per (group, layer, slot) a
+    2-byte pair index and an 8-byte (cos, sin), plus alpha^-1 per channel (4 bytes)."""
+    return (K // 128) * layers * 64 * (2 + 8) + 4 * K
+
+
 def algorithmic_bytes(wl, group=128):
-    """Quantize: read X once, write qa and sa.  GEMM: read qa, sa, qw, sw once, write Y."""
+    """Quantize: read X once (and the Givens table), write qa and sa.  GEMM: read qa, sa,
+    qw, sw once, write Y."""
     M, K, N = wl.M, wl.K, wl.N
     G = K // group
     xb = 2 if wl.x_dtype == "bf16" else 4
     yb = 2 if wl.y_dtype == "bf16" else 4
     quant = M * K * xb + M * K // 2 + M * G * 4
+    if wl.transform[0] == "givens":
+        quant += givens_table_bytes(K, int(wl.transform[1]))
     gemm = M * K // 2 + M * G * 4 + N * K // 2 + N * G * 4 + M * N * yb
     return quant, gemm
 
@@ -256,12 +265,29 @@ def cpu_baseline(wl, rows):
     a = oracle.quantize_act(x, spec, wl.mode)
     oracle.w4a4_gemm(a["qa"], a["sa"], w["qw"], w["sw"], wl.y_dtype)
     dt = time.perf_counter() - t0
+    return dt, blas_info()["threads"]
+
+
+def blas_info():
+    """The BLAS numpy runs the oracle's products on, and its thread count."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            b = blas[0]
+            return {"threads": int(b.get("num_threads", 1)),
+                    "library": f"{b.get('internal_api', '?')} {b.get('version', '')}".strip(),
+                    "file": os.path.basename(b.get("filepath", ""))}
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return dt, threads
+        pass
+    return {"threads": len(os.sched_getaffinity(0)), "library": "unknown", "file": ""}
+
+
+def spread(xs):
+    """median, p10 and p90 of a list of per-launch durations (us)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
 
 
 KV_METRIC = "INT4 KV-cache quantize + dequantize GB/s (block-128 Hadamard per head) at 4096 tokens x 8 heads x 128"
@@ -377,9 +403,12 @@ def main_kv(args, torch, rw4, gu, dev):
             dt += time.perf_counter() - t1
             passes += 1
         cpu_bytes = (qbytes + dbytes) * rows / M * passes
+        bi = blas_info()
         out["cpu_baseline"] = {"value": cpu_bytes / dt / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
                                "kind": "oracle", "sample": f"{rows} of {M} tokens, {passes} pass(es), quantize_act + "
-                                                         f"dequantize (float64 numpy)", "seconds": dt}
+                                                         f"dequantize (float64 numpy)", "seconds": dt,
+                               "os_cpu_count": os.cpu_count(), "blas": bi["library"], "blas_file": bi["file"],
+                               "blas_threads": bi["threads"]}
     print(json.dumps(out), flush=True)
 
 
@@ -511,9 +540,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * M * N * K
     step_gpu_us = 1e3 * r0.elapsed_ms(r1) / args.steps
+    q_spread = g_spread = None
     if per_step:
-        q_us = 1e3 * float(np.mean([e[0].elapsed_ms(e[1]) for e in events if e]))
-        g_us = 1e3 * float(np.mean([e[1].elapsed_ms(e[2]) for e in events if e]))
+        q_list = [1e3 * e[0].elapsed_ms(e[1]) for e in events if e]
+        g_list = [1e3 * e[1].elapsed_ms(e[2]) for e in events if e]
+        q_us, g_us = float(np.mean(q_list)), float(np.mean(g_list))
+        q_spread, g_spread = spread(q_list), spread(g_list)
     else:
         q_us = g_us = float("nan")  # replaced by the back-to-back times below
     layer_tops = ops / (ms_per_step * 1e-3) / 1e12
@@ -578,13 +610,13 @@ def main():
                    "buffer_sets": nsets, "group": grp,
                    "launch": "one HIP graph replay per step" if graph else args.launch + " calls"},
         "roofline": roof,
-        "quantize": {"kernel": quant_kernel, "avg_launch_us": q_us, "gbps": quant_gbps,
+        "quantize": {"kernel": quant_kernel, "avg_launch_us": q_us, "launch_us": q_spread, "gbps": quant_gbps,
                      "frac_hbm": quant_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": qbytes,
                      "back_to_back_us": q_b2b, "back_to_back_gbps": qbytes / (q_b2b * 1e-6) / 1e9,
                      "back_to_back_host_ahead": q_ahead,
                      "back_to_back_frac_hbm": qbytes / (q_b2b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(quant_kernel, wkey)},
-        "gemm": {"kernel": gemm_kernel, "avg_launch_us": g_us, "tops": gemm_tops,
+        "gemm": {"kernel": gemm_kernel, "avg_launch_us": g_us, "launch_us": g_spread, "tops": gemm_tops,
                  "frac_mfma": gemm_tops / PEAK_I8_TOPS, "gbps": gemm_gbps,
                  "back_to_back_us": g_b2b, "back_to_back_tops": ops / (g_b2b * 1e-6) / 1e12,
                  "back_to_back_gbps": gbytes / (g_b2b * 1e-6) / 1e9, "back_to_back_host_ahead": g_ahead},
@@ -605,10 +637,13 @@ def main():
             dt += more
             passes += 1
         cpu_tops = 2.0 * rows * N * K * passes / dt / 1e12
+        bi = blas_info()
         out["cpu_baseline"] = {"value": cpu_tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
                                "sample": f"{rows} of {M} tokens of the same layer, {passes} pass(es), quantize_act + "
                                          f"w4a4_gemm (float64 numpy), weights packed beforehand",
-                               "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+                               "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)),
+                               "os_cpu_count": os.cpu_count(), "blas": bi["library"], "blas_file": bi["file"],
+                               "blas_threads": bi["threads"]}
         log(f"cpu oracle: {passes} x {rows} rows in {dt:.2f} s = {cpu_tops * 1e3:.3f} GOPS on {threads} threads")
     print(json.dumps(out), flush=True)
 

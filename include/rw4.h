@@ -35,7 +35,10 @@
  *     work; output Y [M, N] row-major with leading dimension ldy.
  *     K must be a multiple of 128; G = K / 128 is the number of groups.
  *   - Packed INT4 (this library's layout; the pages fix none): codes lie in
- *     [-7, 7] (the symmetric scale max/7 never leaves it).  Every 32-bit
+ *     [-7, 7].  The INT4 range is [-8, 7] (Rotated Runtime Smooth page,
+ *     problem definition), but the symmetric scale max/7 maps every value
+ *     into [-7, 7] (-8 never arises), and this layout stores exactly that
+ *     domain: a code of -8 cannot be represented.  Every 32-bit
  *     little-endian word (bytes 4w..4w+3 of a row) holds codes c_0..c_7 of
  *     that word as sign-magnitude nibbles: nibble e (byte e/2, low nibble
  *     for even e) = |c_e| in bits 0-2 plus the sign (1 = negative) of
@@ -80,11 +83,18 @@ typedef enum { RW4_F32 = 0, RW4_BF16 = 1 } rw4_dtype;
 
 typedef enum {
   /* transform, then per-(token, 128-channel group) symmetric INT4:
-     sa = max|x~| / 7 over the group, q = clamp(rne(x~ / sa), -8, 7) */
+     sa = max|x~| / 7 over the group, q = rne(x~ / sa).  |x~ / sa| <= 7, so
+     the codes lie in [-7, 7], inside the INT4 range [-8, 7] (no clamp is
+     needed; -8 never arises).  Rotated Runtime Smooth page, problem
+     definition (scale = max|X| / (2^(N-1) - 1)) and experimental setup
+     (symmetric round-to-nearest). */
   RW4_ACT_GROUP128 = 0,
   /* Rotated Runtime Smooth: transform, s_g = max over ALL M tokens and the
      group's channels of |x~|, z = x~ / s_g, per-token a_t = max_j |z| / 7,
-     q = clamp(rne(z / a_t), -8, 7), stored scale sa[t, g] = a_t * s_g */
+     q = rne(z / a_t) in [-7, 7], stored scale sa[t, g] = a_t * s_g.
+     Rotated Runtime Smooth page, main equation (runtime smoothing scale =
+     channel maximum over the tokens) and Figure 4 (2) (the group maximum is
+     the smoothing scale of the GEMM block). */
   RW4_ACT_RRS_PER_TOKEN = 1
 } rw4_act_mode;
 
@@ -92,6 +102,10 @@ typedef struct rw4_transform rw4_transform; /* opaque */
 
 /* Normalized block Walsh-Hadamard transform R = blockdiag(H_b / sqrt(b))
  * over K channels, H_b in Sylvester order ((H)_ij = (-1)^popcount(i AND j)).
+ * Defined by: the QuIP#/QTIP page, section 2.1 (Walsh-Hadamard matrix from
+ * the bit parity of the index pair), section 4.2 (butterfly factorization)
+ * and section 6.1 (block Hadamard); the Rotated Runtime Smooth page,
+ * term-by-term section (R = (1/sqrt(K)) [+-1], R R^T = I).
  * block: a power of two, 128 <= block <= K, block divides K.  Blocks larger
  * than 128 need K in {512, 1024, 2048, 4096, 8192} (else UNSUPPORTED).
  * Allocates nothing on the device.  *out receives the new transform. */
@@ -108,19 +122,24 @@ rw4_status rw4_transform_hadamard(int64_t K, int32_t block, void* stream, rw4_tr
 rw4_status rw4_transform_hadamard_signed(int64_t K, int32_t block, const int8_t* signs_host,
                                         void* stream, rw4_transform** out);
 
-/* ParoQuant-style independent rotation: for each 128-channel group g,
+/* ParoQuant-style independent rotation (the ParoQuant-style article,
+ * section 2.2: layers of disjoint channel-pair rotations in each group;
+ * section 2.3: alpha = exp(beta); section 3.2: the rotation patterns kept in
+ * a lookup table, only the angles supplied at run time): for each
+ * 128-channel group g,
  * R_g = G_1 G_2 ... G_L, where layer l rotates up to 64 disjoint channel
  * pairs (i, j), i < j < 128, by angle theta: (xG)_i = c x_i + s x_j,
  * (xG)_j = -s x_i + c x_j; then channel scale alpha = exp(beta):
  * activations x~ = x R D^-1, weights W~ = D R^T W, D = diag(alpha).
  *   pairs_host [K/128][layers][64][2] uint8, 0xFF in both bytes = empty slot
  *   theta_host [K/128][layers][64] fp32 (ignored for empty slots)
- *   beta_host  [K] fp32
+ *   beta_host  [K] fp32 (exp(+-beta) must be finite and nonzero in fp32)
  * The host computes cos/sin/exp in double, rounds them to fp32, pads every
  * layer to a full matching with zero-angle pairs of the unused channels
  * (exactly the identity), and uploads the tables (176 KiB at K = 4096,
  * L = 8).  ARG if a pair is out of range, not i < j, or reuses a channel
- * inside its layer.  The upload is synchronous with respect to `stream`. */
+ * inside its layer, or if an angle of a used slot or any beta is not
+ * finite.  The upload is synchronous with respect to `stream`. */
 rw4_status rw4_transform_givens(int64_t K, int32_t layers, const uint8_t* pairs_host,
                                 const float* theta_host, const float* beta_host, void* stream,
                                 rw4_transform** out);
@@ -148,6 +167,18 @@ int64_t rw4_transform_k(const rw4_transform* t);
 
 /* quantize_act: one pass (two for RRS) over X [M, K] (x_dtype F32 or BF16,
  * leading dimension ldx elements): transform, quantize, pack.
+ * Defined by: the Rotated Runtime Smooth page, main equation (X_rot = X R,
+ * then runtime smoothing and quantization of the activations) and problem
+ * definition (symmetric scale max|X| / 7 for INT4); the ParoQuant-style
+ * article, section 3.2 (rotate, scale and quantize fused in one kernel) and
+ * section 2.3 (groups of 128 channels share a scale; x R D^-1 with
+ * D = diag(exp(beta))); the QuIP#/QTIP page, sections 2.1 (Walsh-Hadamard
+ * matrix) and 6.1 (block Hadamard).
+ * Input magnitude: the transform sums up to b inputs in fp32 before the
+ * normalization (folded into the stored scale), so every block's sum of |x|
+ * must stay below FLT_MAX: |x| <= 2.6e36 for b = 128 and <= 8.3e34 for
+ * b = 4096 always suffices (bf16 inputs reach 3.4e38).  Larger inputs give
+ * infinite scales; they are not detected.
  *   qa [M, K/2] uint8 packed codes (output)
  *   sa [M, K/128] fp32 scales (output)
  *   workspace: RRS only, >= K/128 fp32 device floats, 16-byte aligned,
@@ -159,7 +190,13 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
                             float* workspace, void* stream);
 
 /* pack_weight: W~ = R^T W (Hadamard) or D R^T W (Givens) for each of the N
- * output channels, then per-(channel, 128-group) symmetric INT4 and packing.
+ * output channels, then per-(channel, 128-group) symmetric INT4 and packing
+ * (codes in [-7, 7], scale max / 7).  Defined by: the Rotated Runtime Smooth
+ * page, main equation (W_rot = R^-1 W, R^-1 = R^T); the OstQuant page,
+ * section 3.2 ((X R D^-1)(D R^T W) = X W); the QuIP#/QTIP page, section 4.2
+ * (the transform folded into the weights offline, H(AB) = (HA)B); the
+ * ParoQuant-style article, section 2.3 (W_hat = diag(alpha) W, 128-channel
+ * groups).  The same input-magnitude bound as quantize_act applies.
  * Element (k, n) of W is w[k * stride_k + n * stride_n] (w_dtype F32/BF16;
  * strides in elements, > 0).
  *   qw [N, K/2] uint8 (output), sw [N, K/128] fp32 (output). */
@@ -180,7 +217,11 @@ rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K
                           rw4_dtype out_dtype, int64_t ldo, void* stream);
 
 /* w4a4_gemm: Y = sum over groups of sa * sw * (qa . qw^T restricted to the
- * group).  Each group's integer dot products are exact (FP8 matrix cores on
+ * group).  Defined by: the Rotated Runtime Smooth page, main equation (Y is
+ * the sum of the per-channel partial products, each multiplied back by its
+ * scale) and Figure 4 (3) (the GEMM block equals the quantization group and
+ * the block's scale multiplies the block's partial result); the
+ * ParoQuant-style article, section 2.3 (one scale per 128-channel group).  Each group's integer dot products are exact (FP8 matrix cores on
  * the codes as exact small values, fp32 accumulation of integers below
  * 2^24); the per-group rescale and the sum over groups are fp32, the output
  * is rounded once to y_dtype (F32, or BF16 with round-to-nearest-even).

@@ -145,6 +145,7 @@ static rw4_status transform_givens_impl(int64_t K, int32_t layers, const uint8_t
         if (i >= kGroup || j >= kGroup || i >= j || used[i] || used[j]) return RW4_ERR_ARG;
         used[i] = used[j] = true;
         const double th = double(theta_host[base + s]);
+        if (!std::isfinite(th)) return RW4_ERR_ARG;
         idx[base + n_real] = uint16_t(i | (j << 8));
         cs[2 * (base + n_real)] = float(std::cos(th));
         cs[2 * (base + n_real) + 1] = float(std::sin(th));
@@ -171,6 +172,11 @@ static rw4_status transform_givens_impl(int64_t K, int32_t layers, const uint8_t
     const double b = double(beta_host[k]);
     alpha[k] = float(std::exp(b));
     alpha_inv[k] = float(std::exp(-b));
+    // a non-finite beta, or one whose scale leaves the fp32 range, has no
+    // usable channel scale
+    if (!std::isfinite(b) || !std::isfinite(alpha[k]) || !std::isfinite(alpha_inv[k]) || alpha[k] == 0.0f ||
+        alpha_inv[k] == 0.0f)
+      return RW4_ERR_ARG;
   }
 
   auto* t = new (std::nothrow) rw4_transform();

@@ -226,8 +226,9 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
                                                              float post_scale) {
   constexpr int ES = BF16 ? 2 : 4;  // bytes per input element
   const int lane = threadIdx.x & 63;
-  // wave index, Q and R below 2^31 (checked on the host): 32-bit division
-  const uint32_t w = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  // wave index (4 waves per block), Q * R below 2^31 (checked on the host):
+  // fits 32 bits without forming the thread index, 32-bit division
+  const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
   if (w >= uint32_t(Q * R)) return;
   const int64_t quad = w % uint32_t(Q), r0 = w / uint32_t(Q);
   const int sub = lane & 15;

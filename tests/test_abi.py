@@ -265,6 +265,27 @@ def test_givens_f16_validation():
     assert not h.value
 
 
+@pytest.mark.parametrize("where", ["theta_nan", "theta_inf", "beta_nan", "beta_overflow"])
+def test_givens_f32_rejects_non_finite(where):
+    """The fp32 entry point rejects what the fp16 one rejects: a non-finite
+    angle of a used slot, or a channel scale exp(+-beta) that is not a finite
+    nonzero fp32 value, before anything is uploaded."""
+    pairs, theta, beta = _givens_tables(K=128, L=1)
+    if where == "theta_nan":
+        theta[0, 0, 2] = np.nan
+    elif where == "theta_inf":
+        theta[0, 0, 0] = -np.inf
+    elif where == "beta_nan":
+        beta[7] = np.nan
+    else:
+        beta[5] = 100.0  # exp(100) overflows fp32
+    h = ctypes.c_void_p()
+    st = lib.rw4_transform_givens(128, 1, pairs.ctypes.data, theta.ctypes.data, beta.ctypes.data, None,
+                                  ctypes.byref(h))
+    assert st == ARG
+    assert not h.value
+
+
 def test_table_transforms_bound_k():
     h = ctypes.c_void_p()
     big = 1 << 25

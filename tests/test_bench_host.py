@@ -74,3 +74,19 @@ def test_prepared_calls_refuse_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         rw4.prepare_quantize_act(t, torch.zeros((M, K), dtype=torch.bfloat16))
     assert np.all(qa.numpy() == 0)  # nothing was written
+
+
+def test_algorithmic_bytes_givens_counts_the_lookup_table():
+    """The decode quantizer also reads the Givens table: 2-byte pair index and 8-byte
+    (cos, sin) per (group, layer, slot) and alpha^-1 per channel = 176 KiB at K = 4096,
+    8 layers; M = 16 gives 16 * (8192 + 2048 + 128) + 180224 = 346112 bytes."""
+    wl = datagen.make("decode", M=16)
+    q, _ = bench.algorithmic_bytes(wl)
+    assert bench.givens_table_bytes(4096, 8) == 176 * 1024
+    assert q == 346112
+
+
+def test_spread_reports_median_and_percentiles():
+    s = bench.spread([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert s["median"] == 3.0 and s["n"] == 5
+    assert s["p10"] == pytest.approx(1.4) and s["p90"] == pytest.approx(4.6)

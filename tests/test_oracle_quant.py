@@ -53,6 +53,45 @@ def test_quant_properties_random():
     assert np.array_equal(scales_neg, scales)
 
 
+def test_codes_in_range_and_argmax_hits_7():
+    """The INT4 container is [-8, 7] (Rotated Runtime Smooth page, problem
+    definition), but with the symmetric scale max / 7 the quantizer's image
+    is [-7, 7]: -8 never arises, even for groups built to reach it (minimum
+    exactly -max, every ratio an exact half, values just above -max), and
+    the group's extreme maps to +-7 exactly.  The same holds for the RRS
+    per-token quantizer."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((40, 256))
+    x[0, :128] = -3.0            # constant negative group: all -7
+    x[1, :128] = 0.0
+    x[1, 5], x[1, 9] = 2.0, -2.0  # min = -max
+    x[2, :128] = np.linspace(-7.0, 7.0, 128)
+    x[3, :128] = -np.arange(128) / 127 * 7.0 - 1e-12
+    x[4, :128] = (np.arange(128) % 15 - 7) + 0.5  # halves everywhere, max 7.5
+    x[5, :] = -np.abs(x[5, :]) * 1e30
+    for codes in (oracle.quantize_groups(x)[0], oracle.quantize_rrs(x)[0]):
+        assert codes.min() >= -7 and codes.max() <= 7
+    codes, scales, _ = oracle.quantize_groups(x)
+    assert np.all(codes[0, :128] == -7)
+    assert codes[1, 9] == -7 and codes[1, 5] == 7
+    xg = np.abs(x.reshape(40, 2, 128))
+    cg = np.abs(codes.reshape(40, 2, 128))
+    top = np.take_along_axis(cg, xg.argmax(axis=2)[:, :, None], axis=2)
+    assert np.all(top == 7)
+
+
+def test_pack_rejects_minus_8():
+    """The packed layout stores the quantizer's domain [-7, 7] only."""
+    for bad in (-8, 8):
+        c = np.zeros((1, 8), dtype=np.int8)
+        c[0, 3] = bad
+        with pytest.raises(ValueError):
+            oracle.pack_int4(c)
+    c = np.arange(-7, 9, dtype=np.int8).reshape(1, 16)
+    c[0, -1] = 0
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(c)), c)
+
+
 def test_quant_zero_and_constant_groups():
     x = np.zeros((2, 256))
     x[1, 128:] = -3.0

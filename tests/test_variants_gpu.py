@@ -10,7 +10,7 @@ pytestmark = [pytest.mark.gpu,
 
 import datagen  # noqa: E402
 import oracle  # noqa: E402
-from tests.helpers import compare_codes, rel_fro, spec_of  # noqa: E402
+from tests.helpers import case_seed, compare_codes, rel_fro, spec_of  # noqa: E402
 
 if torch.cuda.is_available():
     import rotated_w4a4_amd as rw4  # noqa: E402
@@ -30,7 +30,7 @@ SIGNED = [
 @pytest.mark.parametrize("case", SIGNED, ids=[c[0] for c in SIGNED])
 def test_signed_hadamard(case):
     name, M, K, N, b, mode, xdt = case
-    rng = np.random.default_rng(abs(hash(name)) % 2 ** 31)
+    rng = np.random.default_rng(case_seed(name))
     x = datagen.outlier_activations(rng, M, K)
     x = datagen.round_to_bf16(x) if xdt == "bf16" else x.astype(np.float32).astype(np.float64)
     w = rng.normal(0, 0.02, size=(K, N)).astype(np.float32)
