@@ -375,6 +375,12 @@ def main_kv(args, torch, rw4, gu, dev):
     qb_gbps, db_gbps = qbytes / (q_b2b * 1e-6) / 1e9, dbytes / (d_b2b * 1e-6) / 1e9
     log(f"back-to-back (host ahead: {q_ahead and d_ahead}): quantize {q_b2b:.2f} us ({qb_gbps:.0f} GB/s)  "
         f"dequantize {d_b2b:.2f} us ({db_gbps:.0f} GB/s)")
+    # the query side: rotate_act (same transform, unquantized bf16 out) over as many query rows
+    rbytes = M * K * 2 + M * K * 2
+    rc = [rw4.prepare_rotate_act(t, st["x"], out=st["out"]) for st in sets]
+    r_b2b, r_ahead = gpu_bound_us(torch, stream, lambda i: rc[i % nsets]())
+    rb_gbps = rbytes / (r_b2b * 1e-6) / 1e9
+    log(f"rotate_act (queries, bf16 in/out): {r_b2b:.2f} us ({rb_gbps:.0f} GB/s, host ahead: {r_ahead})")
     out = {
         "metric": KV_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -390,6 +396,8 @@ def main_kv(args, torch, rw4, gu, dev):
         "dequantize": {"kernel": "dequant_kernel", "avg_launch_us": d_b2b,
                        "gbps": db_gbps, "frac_hbm": db_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": dbytes,
                        "host_ahead": d_ahead},
+        "rotate_queries": {"kernel": "rotate_h128_kernel", "avg_launch_us": r_b2b, "gbps": rb_gbps,
+                           "frac_hbm": rb_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": rbytes, "host_ahead": r_ahead},
     }
     if not args.no_cpu_baseline:
         import oracle

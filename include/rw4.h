@@ -204,6 +204,22 @@ rw4_status rw4_pack_weight(const rw4_transform* t, const void* w, rw4_dtype w_dt
                            int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
                            void* stream);
 
+/* rotate_act: the transform alone, x~ = x R (Hadamard, plain or signed,
+ * with the 1/sqrt(b) normalization) or x~ = x R D^-1 (Givens), written
+ * unquantized as fp32 or bf16 (round to nearest even) into out [M, K]
+ * (leading dimension ldo >= K elements, 16-byte aligned rows).  This is the
+ * query side of an INT4 KV cache: keys are stored by quantize_act in the
+ * rotated domain and read back by dequantize, queries are rotated by this
+ * call, and (q R)(k R)^T = q k^T because R is orthogonal (the OstQuant page,
+ * section 3.2: an extra Hadamard on queries and keys after RoPE; the
+ * Rotated Runtime Smooth page, experimental setup: KV cache quantized in
+ * groups of 128).  For Givens transforms (q R D^-1)(k R D^-1)^T differs
+ * from q k^T by D^-2; such a transform is meant for weight products.
+ *   x [M, K] (x_dtype F32 or BF16, ldx elements), same rules as
+ *   quantize_act; any transform. */
+rw4_status rw4_rotate_act(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                          void* out, rw4_dtype out_dtype, int64_t ldo, void* stream);
+
 /* dequantize: x_hat[r, k] = code(q[r], k) * s[r, k / 128], the stored codes
  * times their group scale, in the transformed domain (for RRS the stored
  * scale already carries the smoothing factor); the complex-domain

@@ -23,7 +23,8 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
-    "dequantize", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
+    "dequantize", "rotate_act", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
+    "prepare_rotate_act",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -38,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "rw4_transform_givens_f16",
     "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
-    "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_status_str", "rw4_version",
+    "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_status_str", "rw4_version",
 )
 
 
@@ -78,6 +79,7 @@ lib.rw4_quantize_act_g.argtypes = [_p, ctypes.c_int, _i32, _p, ctypes.c_int, _i6
 lib.rw4_pack_weight_g.argtypes = [_p, _i32, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_w4a4_gemm_g.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 lib.rw4_dequantize_g.argtypes = [_p, _p, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
+lib.rw4_rotate_act.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]
 for _name in EXPORTED_SYMBOLS:
     if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k"):
         getattr(lib, _name).restype = ctypes.c_int
@@ -304,6 +306,35 @@ def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: in
                                  sw.data_ptr(), _stream(dev)),
            "rw4_pack_weight")
     return qw, sw
+
+
+def rotate_act(t: Transform, x, out_dtype=None, out=None):
+    """The transform alone: x R (Hadamard) or x R D^-1 (Givens), unquantized.
+
+    x [M, K] (bf16/fp32, unit stride in K); returns out [M, K] in out_dtype
+    (default bf16), e.g. queries rotated like the keys of an INT4 KV cache."""
+    return prepare_rotate_act(t, x, out_dtype, out)()
+
+
+def prepare_rotate_act(t: Transform, x, out_dtype=None, out=None) -> Call:
+    """rotate_act checked and marshalled once; calling the result runs it (returns out)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=x.device)
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, K) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
+    args = (t.handle, x.data_ptr(), _dtype_code(x), M, x.stride(0), out.data_ptr(), _dtype_code(out),
+            out.stride(0))
+    return Call(lib.rw4_rotate_act, args, dev, "rw4_rotate_act", (t, x), out)
 
 
 def _group_of(K, cols):

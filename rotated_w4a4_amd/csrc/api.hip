@@ -312,6 +312,24 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
   return rw4_quantize_act_g(t, mode, 128, x, x_dtype, M, ldx, qa, sa, workspace, stream);
 }
 
+rw4_status rw4_rotate_act(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                          void* out, rw4_dtype out_dtype, int64_t ldo, void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (out_dtype != RW4_F32 && out_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0) return RW4_ERR_SHAPE;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (M == 0) return RW4_OK;
+  if (!x || !out) return RW4_ERR_ARG;
+  const int64_t K = t->dev.K;
+  if (ldx < K || ldo < K) return RW4_ERR_ARG;
+  const int64_t xe = x_dtype == RW4_BF16 ? 2 : 4, oe = out_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * xe) % 16 || !aligned16(out) || (ldo * oe) % 16) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_rotate_act(t->dev, x, x_dtype == RW4_BF16, M, ldx, out, out_dtype == RW4_BF16,
+                                         ldo, st));
+}
+
 rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* w, rw4_dtype w_dtype,
                              int64_t N, int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
                              void* stream) {

@@ -27,6 +27,8 @@
 //                   a max over tokens; Figure 4 (2): one scale per block).
 //   quant_givens    ParoQuant-style layers of disjoint pair rotations from
 //                   a lookup table, then the alpha scale, in LDS.
+#include <type_traits>
+
 #include "rw4_device.h"
 #include "rw4_internal.h"
 
@@ -825,6 +827,121 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
 }
 
 // ---------------------------------------------------------------------------
+// Rotation without quantization: x~ = x R (Hadamard, optionally signed) or
+// x R D^-1 (Givens), written as fp32 or bf16 (round to nearest even).  The
+// query side of an INT4 KV cache: keys are stored rotated and quantized, the
+// queries are rotated alike so that (q R)(k R)^T = q k^T (the OstQuant page,
+// section 3.2, rotates queries and keys together after RoPE; the Rotated
+// Runtime Smooth experiments quantize the KV cache in groups of 128).
+// The transforms are the quantizers' own (same butterflies, same tables);
+// only the epilogue differs: the normalization 1/sqrt(b) (the quantizers
+// fold it into the stored scale) is applied, then the values are stored.
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__device__ __forceinline__ void store8(void* out, int64_t off, const float v[8]) {
+  if constexpr (OUT_BF16) {
+    __bf16 h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = static_cast<__bf16>(v[e]);  // round to nearest even
+    *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(out) + off) = *reinterpret_cast<const uint4*>(h);
+  } else {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// Block-128 Hadamard: 16 lanes per (row, group), 8 consecutive channels per
+// lane, as quant_h128; the lane stages in the negating form leave lane l's
+// values times (-1)^popcount(l & 15), undone with the normalization.
+template <class Src, bool OUT_BF16>
+__global__ __launch_bounds__(256) void rotate_h128_kernel(Src src, int64_t G, int64_t blocks_per_row,
+                                                          void* __restrict__ out, int64_t ldo, float norm) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 15;
+  const int64_t row = int64_t(blockIdx.x) / blocks_per_row;
+  const int64_t grp = (int64_t(blockIdx.x) - row * blocks_per_row) * 16 + wave * 4 + (lane >> 4);
+  if (grp >= G) return;  // whole 16-lane groups leave together: the stages stay inside a group
+  float v[8];
+  src.load8(row, grp * kGroup + sub * 8, v);
+  fwht8(v);
+  const float c1 = (lane & 1) ? -1.0f : 1.0f, c2 = (lane & 2) ? -1.0f : 1.0f;
+  const float c4 = (lane & 4) ? -1.0f : 1.0f, c8 = (lane & 8) ? -1.0f : 1.0f;
+  const float scale = ((__builtin_popcount(lane & 15) & 1) ? -1.0f : 1.0f) * norm;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = v[e];
+    x = butterfly_neg_x<1>(x, c1);
+    x = butterfly_neg_x<2>(x, c2);
+    x = butterfly_neg_x<4>(x, c4);
+    x = butterfly_neg_x<8>(x, c8);
+    v[e] = x * scale;
+  }
+  store8<OUT_BF16>(out, row * ldo + grp * kGroup + sub * 8, v);
+}
+
+// Hadamard blocks of 2^log2b channels over whole rows of K = 64 E channels:
+// one wave per row, lane l holds channels 512 c + 8 l + e (quant_rowh).
+template <int E, class Src, bool OUT_BF16>
+__global__ __launch_bounds__(256) void rotate_rowh_kernel(Src src, int64_t M, int log2b, void* __restrict__ out,
+                                                          int64_t ldo, float norm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+#pragma unroll
+    for (int c = 0; c < E / 8; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c * 8 + e] *= norm;
+      store8<OUT_BF16>(out, row * ldo + c * 512 + lane * 8, &v[c * 8]);
+    }
+  }
+}
+
+// Givens layers from the lookup table (as quant_givens with one row per
+// wave), then the channel scale alpha^-1.
+template <class Src, bool OUT_BF16>
+__global__ __launch_bounds__(64) void rotate_givens_kernel(Src src, int64_t G, int L,
+                                                           const uint16_t* __restrict__ lut_idx,
+                                                           const float2* __restrict__ lut_cs,
+                                                           const float* __restrict__ chan_scale,
+                                                           void* __restrict__ out, int64_t ldo) {
+  __shared__ float buf[kGroup];
+  const int lane = threadIdx.x;
+  const int64_t grp = blockIdx.x % G;
+  const int64_t row = blockIdx.x / G;
+  const uint16_t* idx = lut_idx + grp * L * 64;
+  const float2* cs = lut_cs + grp * L * 64;
+  float v[2];
+  src.load2(row, grp * kGroup + 2 * lane, v);
+  buf[2 * lane] = v[0];
+  buf[2 * lane + 1] = v[1];
+  __syncthreads();
+  for (int l = 0; l < L; ++l) {
+    const uint32_t pr = idx[l * 64 + lane];
+    const float2 t = cs[l * 64 + lane];
+    const int i = pr & 0xFF, j = pr >> 8;
+    const float a = buf[i], b = buf[j];
+    buf[i] = fmaf(t.x, a, t.y * b);
+    buf[j] = fmaf(t.x, b, -t.y * a);
+    __syncthreads();
+  }
+  const float x0 = buf[2 * lane] * chan_scale[grp * kGroup + 2 * lane];
+  const float x1 = buf[2 * lane + 1] * chan_scale[grp * kGroup + 2 * lane + 1];
+  const int64_t off = row * ldo + grp * kGroup + 2 * lane;
+  if constexpr (OUT_BF16) {
+    const __bf16 h[2] = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<__bf16*>(out) + off) = *reinterpret_cast<const uint32_t*>(h);
+  } else {
+    *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + off) = make_float2(x0, x1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -950,6 +1067,71 @@ hipError_t launch_givens(const Src& src, int64_t rows, int64_t G, int L, const u
 }
 
 }  // namespace
+
+namespace {
+
+template <class Src>
+hipError_t launch_rotate_src(const TransformDev& t, const Src& src, int64_t M, void* out, bool out_bf16,
+                             int64_t ldo, hipStream_t st) {
+  const int64_t K = t.K, G = K / kGroup;
+  const float norm = 1.0f / sqrtf(float(t.block));
+  if (t.block == 128) {
+    const int64_t bpr = (G + 15) / 16, blocks = M * bpr;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (out_bf16)
+      hipLaunchKernelGGL((rotate_h128_kernel<Src, true>), dim3(blocks), dim3(256), 0, st, src, G, bpr, out, ldo, norm);
+    else
+      hipLaunchKernelGGL((rotate_h128_kernel<Src, false>), dim3(blocks), dim3(256), 0, st, src, G, bpr, out, ldo, norm);
+    return hipGetLastError();
+  }
+  int log2b = 0;
+  while ((int64_t(1) << log2b) < t.block) ++log2b;
+  const int grid = grid_for_waves(M, 256 * 16);
+  auto run = [&](auto e_const) {
+    constexpr int E = decltype(e_const)::value;
+    if (out_bf16)
+      hipLaunchKernelGGL((rotate_rowh_kernel<E, Src, true>), dim3(grid), dim3(256), 0, st, src, M, log2b, out, ldo, norm);
+    else
+      hipLaunchKernelGGL((rotate_rowh_kernel<E, Src, false>), dim3(grid), dim3(256), 0, st, src, M, log2b, out, ldo, norm);
+    return hipGetLastError();
+  };
+  switch (K) {
+    case 512: return run(std::integral_constant<int, 8>{});
+    case 1024: return run(std::integral_constant<int, 16>{});
+    case 2048: return run(std::integral_constant<int, 32>{});
+    case 4096: return run(std::integral_constant<int, 64>{});
+    case 8192: return run(std::integral_constant<int, 128>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// Rotation without quantization of row-major activations X [M, K].
+hipError_t launch_rotate_act(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx, void* out,
+                             bool out_bf16, int64_t ldo, hipStream_t st) {
+  const int64_t K = t.K, G = K / kGroup;
+  if (t.kind == TransformKind::Hadamard) {
+    if (t.sign_mask) {
+      if (bf16) return launch_rotate_src(t, SignedSrc<RowSrc<true>>{{x, ldx}, t.sign_mask}, M, out, out_bf16, ldo, st);
+      return launch_rotate_src(t, SignedSrc<RowSrc<false>>{{x, ldx}, t.sign_mask}, M, out, out_bf16, ldo, st);
+    }
+    if (bf16) return launch_rotate_src(t, RowSrc<true>{x, ldx}, M, out, out_bf16, ldo, st);
+    return launch_rotate_src(t, RowSrc<false>{x, ldx}, M, out, out_bf16, ldo, st);
+  }
+  const int64_t blocks = G * M;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define RW4_ROT_GIVENS(B, O)                                                                               \
+  hipLaunchKernelGGL((rotate_givens_kernel<RowSrc<B>, O>), dim3(blocks), dim3(64), 0, st, RowSrc<B>{x, ldx}, G, \
+                     t.layers, t.lut_idx, t.lut_cs, t.alpha_inv, out, ldo)
+  if (bf16) {
+    if (out_bf16) RW4_ROT_GIVENS(true, true); else RW4_ROT_GIVENS(true, false);
+  } else {
+    if (out_bf16) RW4_ROT_GIVENS(false, true); else RW4_ROT_GIVENS(false, false);
+  }
+#undef RW4_ROT_GIVENS
+  return hipGetLastError();
+}
 
 bool rowh_supported(int64_t K) {
   return K == 512 || K == 1024 || K == 2048 || K == 4096 || K == 8192;

@@ -33,6 +33,9 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
 hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
                               int64_t sn, uint8_t* q, float* s, int group, hipStream_t st);
 
+hipError_t launch_rotate_act(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx, void* out,
+                             bool out_bf16, int64_t ldo, hipStream_t st);
+
 hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, int group, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st);
 

@@ -312,3 +312,32 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         rw4.w4a4_gemm(q, s, q, s, torch.float32)
     t.close()
+
+
+def test_rotate_act_validation():
+    """rotate_act rejects what quantize_act rejects, before any device work."""
+    f = lib.rw4_rotate_act
+    assert f(None, FAKE, 1, 4, 256, FAKE, 1, 256, None) == ARG          # no transform
+    st, h = _had(256, 128)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 7, 4, 256, FAKE, 1, 256, None) == ARG         # unknown input dtype
+        assert f(h, FAKE, 1, 4, 256, FAKE, 9, 256, None) == ARG         # unknown output dtype
+        assert f(h, FAKE, 1, -1, 256, FAKE, 1, 256, None) == SHAPE      # negative M
+        assert f(h, None, 1, 0, 256, None, 1, 256, None) == OK          # empty: nothing to do
+        assert f(h, None, 1, 4, 256, FAKE, 1, 256, None) == ARG         # null input
+        assert f(h, FAKE, 1, 4, 200, FAKE, 1, 256, None) == ARG         # ldx < K
+        assert f(h, FAKE, 1, 4, 256, FAKE, 1, 100, None) == ARG         # ldo < K
+        assert f(h, FAKE + 2, 1, 4, 256, FAKE, 1, 256, None) == ARG     # misaligned input
+        assert f(h, FAKE, 1, 4, 260, FAKE, 1, 256, None) == ARG         # row pitch not 16-byte aligned
+    finally:
+        lib.rw4_transform_destroy(h)
+
+
+def test_every_entry_point_declares_its_argument_types():
+    """Every C call taking pointers has ctypes argument types: without them
+    ctypes passes Python ints as 32-bit C ints and device pointers get truncated."""
+    for n in rw4.EXPORTED_SYMBOLS:
+        if n in ("rw4_version",):
+            continue
+        assert getattr(lib, n).argtypes is not None, n

@@ -197,3 +197,20 @@ def test_round_bf16_grid():
     bits = bits[(bits & 0x7F800000) != 0x7F800000]    # finite values only
     u = bits.view(np.float32).astype(np.float64)
     assert np.array_equal(oracle.round_bf16(u), u)
+
+
+def test_attention_scores_invariant_under_shared_rotation():
+    """(q R)(k R)^T = q k^T for the block Hadamard (plain and signed) applied to
+    queries and keys alike: the reason an INT4 KV cache may store keys rotated
+    (the OstQuant page, section 3.2: the same Hadamard on queries and keys)."""
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((6, 256))
+    k = rng.standard_normal((9, 256))
+    for spec in ({"kind": "hadamard", "block": 128},
+                 {"kind": "hadamard", "block": 128, "signs": np.where(rng.random(256) < 0.5, -1.0, 1.0)},
+                 {"kind": "hadamard", "block": 256}):
+        s = oracle.transform_act(q, spec) @ oracle.transform_act(k, spec).T
+        assert np.allclose(s, q @ k.T, rtol=0, atol=1e-12 * np.abs(q).sum() * np.abs(k).max())
+    # a rotation that is not shared breaks it
+    s_bad = oracle.transform_act(q, {"kind": "hadamard", "block": 128}) @ k.T
+    assert not np.allclose(s_bad, q @ k.T, atol=1e-3)
