@@ -189,6 +189,20 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
                             rw4_dtype x_dtype, int64_t M, int64_t ldx, uint8_t* qa, float* sa,
                             float* workspace, void* stream);
 
+/* quantize_act_static: rw4_quantize_act with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid allocation).  In RRS mode the
+ * group maxima s_g live in a static array of the library, 64 floats per GPU
+ * (so K <= 8192; RW4_ERR_SHAPE beyond), held by each GPU the library runs
+ * on until the process ends; the call allocates nothing and clears what it
+ * uses with a kernel.  Every call on one GPU shares that array, which keeps
+ * the last call's contents: calls that overlap on one GPU (two streams, two
+ * threads) race and must be serialized by the caller.  GROUP128 mode needs
+ * no scratch and is exactly rw4_quantize_act.  Arguments, layouts and
+ * errors otherwise as rw4_quantize_act. */
+rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, const void* x, rw4_dtype x_dtype,
+                                   int64_t M, int64_t ldx, uint8_t* qa, float* sa, void* stream);
+
 /* pack_weight: W~ = R^T W (Hadamard) or D R^T W (Givens) for each of the N
  * output channels, then per-(channel, 128-group) symmetric INT4 and packing
  * (codes in [-7, 7], scale max / 7).  Defined by: the Rotated Runtime Smooth

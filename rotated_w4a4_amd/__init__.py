@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
     "dequantize", "rotate_act", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
-    "prepare_rotate_act",
+    "prepare_rotate_act", "quantize_act_static",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -39,7 +39,8 @@ EXPORTED_SYMBOLS = (
     "rw4_transform_givens_f16",
     "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
-    "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_status_str", "rw4_version",
+    "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_quantize_act_static", "rw4_status_str",
+    "rw4_version",
 )
 
 
@@ -80,6 +81,7 @@ lib.rw4_pack_weight_g.argtypes = [_p, _i32, _p, ctypes.c_int, _i64, _i64, _i64, 
 lib.rw4_w4a4_gemm_g.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 lib.rw4_dequantize_g.argtypes = [_p, _p, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 lib.rw4_rotate_act.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+lib.rw4_quantize_act_static.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _p]
 for _name in EXPORTED_SYMBOLS:
     if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k"):
         getattr(lib, _name).restype = ctypes.c_int
@@ -273,6 +275,31 @@ def prepare_quantize_act(t: Transform, x, mode: str = "group128", qa=None, sa=No
     args = (t.handle, MODES[mode], group, x.data_ptr(), _dtype_code(x), M, x.stride(0), qa.data_ptr(),
             sa.data_ptr(), workspace.data_ptr() if workspace is not None else None)
     return Call(lib.rw4_quantize_act_g, args, dev, "rw4_quantize_act", (t, x, workspace), (qa, sa))
+
+
+def quantize_act_static(t: Transform, x, mode: str = "group128", qa=None, sa=None):
+    """quantize_act through the allocation-free entry point: no workspace; in
+    "rrs" mode the group maxima use the library's static per-GPU scratch
+    (K <= 8192).  Calls overlapping on one GPU race (shared scratch)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}")
+    if qa is None:
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _out("qa", qa, (M, K // 2), torch.uint8, dev)
+    _out("sa", sa, (M, K // 128), torch.float32, dev)
+    _check(lib.rw4_quantize_act_static(t.handle, MODES[mode], x.data_ptr(), _dtype_code(x), M, x.stride(0),
+                                       qa.data_ptr(), sa.data_ptr(), _stream(dev)),
+           "rw4_quantize_act_static")
+    return qa, sa
 
 
 def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: int = 128):

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -40,6 +41,41 @@ bool on_home_device(const rw4_transform* t) {
   if (!tables) return true;
   int d = -1;
   return hipGetDevice(&d) == hipSuccess && d == t->device;
+}
+
+}  // namespace
+
+// Scratch of rw4_quantize_act_static: the Rotated Runtime Smooth group
+// maxima s_g (K / 128 floats, K <= 8192) for callers that cannot allocate.
+// Each GPU holds its own copy for the life of the process; every call on a
+// GPU uses that GPU's copy.
+constexpr int64_t kScratchFloats = 64;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`, looked up on the
+// first call on that GPU (with it current) and kept.  The array's name is
+// only a host-side stand-in: kernels get this address.
+hipError_t scratch_address(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -328,6 +364,21 @@ rw4_status rw4_rotate_act(const rw4_transform* t, const void* x, rw4_dtype x_dty
   hipStream_t st = static_cast<hipStream_t>(stream);
   return from_hip(rw4::launch_rotate_act(t->dev, x, x_dtype == RW4_BF16, M, ldx, out, out_dtype == RW4_BF16,
                                          ldo, st));
+}
+
+rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, const void* x, rw4_dtype x_dtype,
+                                   int64_t M, int64_t ldx, uint8_t* qa, float* sa, void* stream) {
+  if (mode != RW4_ACT_RRS_PER_TOKEN)  // no scratch needed: exactly rw4_quantize_act
+    return rw4_quantize_act(t, mode, x, x_dtype, M, ldx, qa, sa, nullptr, stream);
+  if (!t) return RW4_ERR_ARG;
+  if (t->dev.K / kGroup > kScratchFloats) return RW4_ERR_SHAPE;  // beyond the static scratch
+  // the checks of rw4_quantize_act come first (a NULL workspace would fail them)
+  float* ws = nullptr;
+  if (M > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return rw4_quantize_act(t, mode, x, x_dtype, M, ldx, qa, sa, ws, stream);
 }
 
 rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* w, rw4_dtype w_dtype,
