@@ -177,6 +177,7 @@ def parse():
 
 KERNEL_SOURCES = {
     "gemm_f8_kernel": ["gemm.hip", "rw4_device.h"],
+    "gemm_f8p_kernel": ["gemm.hip", "rw4_device.h"],
     "gemm_small_kernel": ["gemm.hip", "rw4_device.h"],
     "quant_h128_act_kernel": ["quant.hip", "rw4_device.h"],
     "quant_h128_kernel": ["quant.hip", "rw4_device.h"],
@@ -241,12 +242,14 @@ def algorithmic_bytes(wl, group=128):
     return quant, gemm
 
 
-def gemm_kernel_for(M, N):
+def gemm_kernel_for(M, N, group=128):
     """The GEMM kernel the library runs for an M x N product: the small-M kernel up to 64
     rows, and up to 1024 rows (in 64-row chunks) while the 128 x 128-tile grid would have
-    fewer than 128 blocks; the tiled kernel otherwise."""
+    fewer than 128 blocks; the tiled kernel otherwise (its pipelined form for 128-wide groups)."""
     small = M <= 64 or (M <= 1024 and ((M + 127) // 128) * ((N + 127) // 128) < 128)
-    return "gemm_small_kernel" if small else "gemm_f8_kernel"
+    if small:
+        return "gemm_small_kernel"
+    return "gemm_f8p_kernel" if group == 128 else "gemm_f8_kernel"
 
 
 def cpu_baseline(wl, rows):
@@ -570,7 +573,7 @@ def main():
         f"GPU {step_gpu_us:.1f} us)  quantize {q_us:.2f} us ({quant_gbps:.0f} GB/s)  "
         f"gemm {g_us:.2f} us ({gemm_tops:.0f} TOPS)")
 
-    gemm_kernel = gemm_kernel_for(M, N)
+    gemm_kernel = gemm_kernel_for(M, N, grp)
     wkey = args.workload if grp == 128 else f"{args.workload}_g{grp}"  # counters are per configuration
     traffic = measured_traffic(gemm_kernel, wkey)
     if decode:

@@ -35,13 +35,15 @@ def test_algorithmic_bytes_q_proj():
 @pytest.mark.parametrize("M,N,kernel", [
     (1, 4096, "gemm_small_kernel"), (64, 14336, "gemm_small_kernel"),
     (65, 4096, "gemm_small_kernel"), (384, 4096, "gemm_small_kernel"),   # 3 x 32 tiles < 128
-    (512, 4096, "gemm_f8_kernel"),                                       # 4 x 32 tiles
-    (128, 14336, "gemm_small_kernel"), (256, 14336, "gemm_f8_kernel"),
-    (1024, 40, "gemm_small_kernel"), (1025, 40, "gemm_f8_kernel"),
-    (2048, 4096, "gemm_f8_kernel"),
+    (512, 4096, "gemm_f8p_kernel"),                                      # 4 x 32 tiles
+    (128, 14336, "gemm_small_kernel"), (256, 14336, "gemm_f8p_kernel"),
+    (1024, 40, "gemm_small_kernel"), (1025, 40, "gemm_f8p_kernel"),
+    (2048, 4096, "gemm_f8p_kernel"),
 ])
 def test_gemm_routing(M, N, kernel):
     assert bench.gemm_kernel_for(M, N) == kernel
+    # 64- and 256-wide groups keep the unpipelined tiled kernel
+    assert bench.gemm_kernel_for(M, N, 256) == kernel.replace("f8p", "f8")
 
 
 def test_traffic_lookup():
