@@ -67,7 +67,7 @@ __all__ = [
     "givens_layer", "givens_group_rotation",
     "act_transform_blocks", "weight_transform_blocks",
     "transform_act", "transform_weight",
-    "quantize_groups", "quantize_rrs",
+    "quantize_groups", "quantize_rrs", "rrs_channel_order", "quantize_per_channel", "permute_codes",
     "pack_int4", "unpack_int4",
     "group_accumulators", "dequant_gemm",
     "round_bf16", "round_output", "dequantize", "round_dequant_output",
@@ -275,6 +275,35 @@ def quantize_rrs(xt: np.ndarray, g: int = GROUP, quantizer=None):
     return codes, sa, s, ratio
 
 
+def rrs_channel_order(xt: np.ndarray):
+    """Channel order of the Rotated Runtime Smooth reorder.
+
+    [RRS] Figure 4 (1): activations and weights are reordered by the
+    channel-wise maxima of the activations (the reorder leaves Y unchanged,
+    Y being a sum over channels in any order); Figure 4 (2): the reordered
+    channels are then grouped by the GEMM block.  Reading: the maxima are
+    taken over all tokens of the call, m_j = max_t |xt[t, j]|, and channels
+    are sorted by decreasing m_j, equal maxima in increasing channel index
+    (a stable sort), so channels of similar magnitude share a group.
+    Returns (order, m): order[r] = the channel placed at position r.
+    """
+    xt = np.asarray(xt, dtype=np.float64)
+    m = np.abs(xt).max(axis=0)
+    order = np.argsort(-m, kind="stable")
+    return order, m
+
+
+def quantize_per_channel(wt_rows: np.ndarray):
+    """Per-row symmetric INT4 over the whole row: scale = max|row| / 7 (the
+    per-channel weight scheme of the [RRS] experimental setup, one scale per
+    output channel).  Returns (codes, scale [R], ratio)."""
+    x = np.asarray(wt_rows, dtype=np.float64)
+    scale = np.abs(x).max(axis=1) / QMAX
+    safe = np.where(scale > 0, scale, 1.0)
+    ratio = np.where(scale[:, None] > 0, x / safe[:, None], 0.0)
+    return _rtn(ratio).astype(np.int8), scale, ratio
+
+
 # --------------------------------------------------------------------------
 # Packing
 # --------------------------------------------------------------------------
@@ -411,34 +440,59 @@ def round_dequant_output(x: np.ndarray, dtype: str) -> np.ndarray:
 # The three library calls, as plain definitions
 # --------------------------------------------------------------------------
 
-def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GROUP):
+def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GROUP, order=None):
     """Oracle of quantize_act: transform, then per-group or RRS per-token INT4.
 
     ``g`` is the quantization group ([Paro] section 2.3 uses 128; other
-    group sizes are a knob of the same quantizer).  Returns dict(qa=packed
-    uint8 [M, K/2], sa=float64 [M, K/g], codes, ratio, xt=transformed
-    activations, s=RRS group scales or None).
+    group sizes are a knob of the same quantizer).  Mode "rrs_reorder" is
+    Rotated Runtime Smooth with the channel reorder of [RRS] Figure 4 (1):
+    the transformed channels are permuted by ``order`` (default: the
+    rrs_channel_order of this call's activations) before grouping, and the
+    codes are stored in that order.  Returns dict(qa=packed uint8 [M, K/2],
+    sa=float64 [M, K/g], codes, ratio, xt=transformed activations, s=RRS
+    group scales or None, order=the channel order or None, m=channel maxima
+    or None).
     """
     xt = transform_act(X, spec)
+    m = None
     if mode == "group128":
         codes, sa, ratio = quantize_groups(xt, g)
         s = None
     elif mode == "rrs":
         codes, sa, s, ratio = quantize_rrs(xt, g)
+    elif mode == "rrs_reorder":
+        if order is None:
+            order, m = rrs_channel_order(xt)
+        order = np.asarray(order)
+        codes, sa, s, ratio = quantize_rrs(xt[:, order], g)
     else:
         raise ValueError(mode)
-    return {"qa": pack_int4(codes), "sa": sa, "codes": codes, "ratio": ratio, "xt": xt, "s": s}
+    return {"qa": pack_int4(codes), "sa": sa, "codes": codes, "ratio": ratio, "xt": xt, "s": s,
+            "order": order if mode == "rrs_reorder" else None, "m": m}
 
 
-def pack_weight(W: np.ndarray, spec: dict, g: int = GROUP):
+def pack_weight(W: np.ndarray, spec: dict, g: int = GROUP, per_channel: bool = False):
     """Oracle of pack_weight: W_tilde = T_w W, per-(output channel, group) INT4.
 
     W is [K, N].  Returns dict(qw=packed uint8 [N, K/2], sw=float64 [N, K/g],
-    codes [N, K], ratio [N, K], wt=W_tilde [K, N]).
+    codes [N, K], ratio [N, K], wt=W_tilde [K, N]).  ``per_channel`` uses one
+    scale per output channel over all K ([RRS] experimental setup: weights
+    per-channel symmetric), stored repeated in every group column, so that
+    a permutation of the K channels only permutes the codes.
     """
     wt = transform_weight(W, spec)
-    codes, sw, ratio = quantize_groups(wt.T, g)
+    if per_channel:
+        codes, scale, ratio = quantize_per_channel(wt.T)
+        sw = np.repeat(scale[:, None], wt.shape[0] // g, axis=1)
+    else:
+        codes, sw, ratio = quantize_groups(wt.T, g)
     return {"qw": pack_int4(codes), "sw": sw, "codes": codes, "ratio": ratio, "wt": wt}
+
+
+def permute_codes(codes: np.ndarray, order) -> np.ndarray:
+    """Codes of every row taken in channel order ``order``: out[r, j] = codes[r, order[j]]
+    (the weight side of the [RRS] Figure 4 (1) reorder)."""
+    return np.asarray(codes)[:, np.asarray(order)]
 
 
 def w4a4_gemm(qa_packed, sa, qw_packed, sw, out_dtype: str = "f32") -> np.ndarray:
