@@ -160,7 +160,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
-                             "decode128", "decode256", "tiny", "kv"])
+                             "decode128", "decode256", "tiny", "kv", "rrs_reorder"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
@@ -423,6 +423,72 @@ def main_kv(args, torch, rw4, gu, dev):
     print(json.dumps(out), flush=True)
 
 
+def main_rrs_reorder(args, torch, rw4, gu, dev):
+    """Rotated Runtime Smooth with the channel reorder on the RRS workload: one step =
+    quantize_act_rrs_reorder (four kernels: channel maxima, their reduction, the order
+    and group scales, the reordered quantizer) + permute_codes of the per-channel weights
+    by that order + w4a4_gemm."""
+    import datagen
+    wl = datagen.make("rrs")
+    M, K, N = wl.M, wl.K, wl.N
+    t = gu.transform_for(wl)
+    x = gu.x_to_device(wl.x, wl.x_dtype)
+    w = torch.from_numpy(wl.w).to(dev)
+    qw, sw = rw4.pack_weight_per_channel(t, w)
+    del w
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    order = torch.empty((K,), dtype=torch.int32, device=dev)
+    ws = torch.empty((int(rw4.lib.rw4_rrs_reorder_workspace_bytes(K)),), dtype=torch.uint8, device=dev)
+    qw_ord = torch.empty_like(qw)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    perm = rw4.prepare_permute_codes(qw, order, out=qw_ord)
+    gemm = rw4.prepare_w4a4_gemm(qa, sa, qw_ord, sw, out=y)
+
+    def q_call(i):
+        rw4.quantize_act_rrs_reorder(t, x, qa=qa, sa=sa, order=order, workspace=ws)
+
+    def step(i):
+        q_call(i)
+        perm()
+        gemm()
+
+    for i in range(args.warmup):
+        step(i)
+    r0, r1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    (q_us, _), (p_us, _), (g_us, _) = (gpu_bound_us(torch, stream, q_call), gpu_bound_us(torch, stream, lambda i: perm()),
+                                       gpu_bound_us(torch, stream, lambda i: gemm()))
+    ops = 2.0 * M * N * K
+    qbytes = M * K * 2 * 2 + M * K // 2 + M * (K // 128) * 4  # X read by both passes, codes and scales written
+    pbytes = 2 * N * K // 2
+    log(f"rrs reorder step {ms_per_step * 1e3:.1f} us: quantize (4 kernels) {q_us:.2f} us, weight permutation "
+        f"{p_us:.2f} us ({pbytes / p_us / 1e3:.0f} GB/s), gemm {g_us:.2f} us ({ops / g_us / 1e6:.0f} TOPS)")
+    out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "config": {"workload": f"rrs_reorder M={M} K={K} N={N}", "transform": f"hadamard{K}",
+                      "act_mode": "rrs with channel reorder", "weights": "per output channel, permuted per call"},
+           "quantize_us": q_us, "permute_us": p_us, "gemm_us": g_us,
+           "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": "gemm_f8p_kernel",
+                        "avg_launch_us": g_us},
+           "permute": {"kernel": "permute_codes_kernel", "avg_launch_us": p_us, "algorithmic_bytes": pbytes,
+                       "gbps": pbytes / p_us / 1e3, "frac_hbm": pbytes / p_us / 1e3 / PEAK_HBM_GBPS},
+           "quantize": {"kernels": "rrs_chanmax + chanmax_reduce + rrs_rank + quant_rrs_order", "avg_us": q_us,
+                        "algorithmic_bytes": qbytes, "gbps": qbytes / q_us / 1e3}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -448,6 +514,8 @@ def main():
         return
     if args.workload == "kv":
         return main_kv(args, torch, rw4, gu, dev)
+    if args.workload == "rrs_reorder":
+        return main_rrs_reorder(args, torch, rw4, gu, dev)
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group

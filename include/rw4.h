@@ -203,6 +203,52 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
 rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, const void* x, rw4_dtype x_dtype,
                                    int64_t M, int64_t ldx, uint8_t* qa, float* sa, void* stream);
 
+/* ---- Rotated Runtime Smooth with the channel reorder --------------------
+ * The Rotated Runtime Smooth page, Figure 4 (1): activations and weights are
+ * reordered by the channel-wise maxima of the activations (Y is a sum over
+ * channels, so the order does not change it); Figure 4 (2): the reordered
+ * channels are grouped by the GEMM block and each group's maximum is its
+ * runtime smoothing scale.  Readings: the maxima are taken over all M tokens
+ * of the call; the order is by decreasing maximum, equal maxima by
+ * increasing channel index; the weights are quantized per output channel
+ * (the page's experimental setup), so reordering them only permutes codes.
+ * One layer call:
+ *   rw4_quantize_act_rrs_reorder(t, x, ..., qa, sa, order, ws)   activations
+ *   rw4_permute_codes(qw, N, K, order, qw_ordered)               weights
+ *   rw4_w4a4_gemm(qa, sa, qw_ordered, sw, ...)                   the product
+ * with qw/sw from rw4_pack_weight_per_channel (offline). */
+
+/* Bytes of device workspace rw4_quantize_act_rrs_reorder needs for K
+ * channels (per-block channel maxima, the maxima, the group scales); 0 for
+ * an invalid K. */
+int64_t rw4_rrs_reorder_workspace_bytes(int64_t K);
+
+/* Transform (a Hadamard transform, any block, plain or signed; K in {512,
+ * 1024, 2048, 4096}, else RW4_ERR_UNSUPPORTED), per-channel maxima of
+ * |x~| over the M tokens, channel order, smoothing by the reordered groups'
+ * maxima, per-token INT4.  Writes qa [M, K/2] in the reordered channel
+ * order, sa [M, K/128] (a_t * s_g of the reordered groups) and order [K]
+ * int32 (order[r] = the channel placed at position r, a permutation).
+ * workspace: rw4_rrs_reorder_workspace_bytes(K) bytes, 16-byte aligned,
+ * owned by the caller, overwritten.  Other arguments as rw4_quantize_act. */
+rw4_status rw4_quantize_act_rrs_reorder(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M,
+                                        int64_t ldx, uint8_t* qa, float* sa, int32_t* order, void* workspace,
+                                        void* stream);
+
+/* pack_weight with one scale per output channel over all K (max / 7 of the
+ * transformed row), stored in every one of the K/128 scale columns of sw.
+ * Hadamard transforms with K in {512, ..., 8192} (else UNSUPPORTED).
+ * Arguments as rw4_pack_weight. */
+rw4_status rw4_pack_weight_per_channel(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
+                                       int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw, void* stream);
+
+/* out[r, j] = code j' = order[j] of row r of q, for rows rows of K codes
+ * (packed as everywhere, K % 128 == 0, K <= 8192); order is a permutation
+ * of [0, K) (device int32 [K]; it is not checked: an index outside
+ * [0, K) is clamped into it).  out must not alias q. */
+rw4_status rw4_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const int32_t* order, uint8_t* out,
+                             void* stream);
+
 /* pack_weight: W~ = R^T W (Hadamard) or D R^T W (Givens) for each of the N
  * output channels, then per-(channel, 128-group) symmetric INT4 and packing
  * (codes in [-7, 7], scale max / 7).  Defined by: the Rotated Runtime Smooth

@@ -24,7 +24,8 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
     "dequantize", "rotate_act", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
-    "prepare_rotate_act", "quantize_act_static",
+    "prepare_rotate_act", "quantize_act_static", "quantize_act_rrs_reorder", "pack_weight_per_channel",
+    "permute_codes", "prepare_permute_codes",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -40,7 +41,8 @@ EXPORTED_SYMBOLS = (
     "rw4_transform_destroy", "rw4_transform_k", "rw4_quantize_act", "rw4_pack_weight",
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
     "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_quantize_act_static", "rw4_status_str",
-    "rw4_version",
+    "rw4_version", "rw4_rrs_reorder_workspace_bytes", "rw4_quantize_act_rrs_reorder", "rw4_pack_weight_per_channel",
+    "rw4_permute_codes",
 )
 
 
@@ -82,8 +84,13 @@ lib.rw4_w4a4_gemm_g.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, ctyp
 lib.rw4_dequantize_g.argtypes = [_p, _p, _i64, _i64, _i32, _p, ctypes.c_int, _i64, _p]
 lib.rw4_rotate_act.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]
 lib.rw4_quantize_act_static.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _p, _p, _p]
+lib.rw4_rrs_reorder_workspace_bytes.argtypes = [_i64]
+lib.rw4_rrs_reorder_workspace_bytes.restype = _i64
+lib.rw4_quantize_act_rrs_reorder.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p]
+lib.rw4_pack_weight_per_channel.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
+lib.rw4_permute_codes.argtypes = [_p, _i64, _i64, _p, _p, _p]
 for _name in EXPORTED_SYMBOLS:
-    if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k"):
+    if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k", "rw4_rrs_reorder_workspace_bytes"):
         getattr(lib, _name).restype = ctypes.c_int
 
 
@@ -300,6 +307,89 @@ def quantize_act_static(t: Transform, x, mode: str = "group128", qa=None, sa=Non
                                        qa.data_ptr(), sa.data_ptr(), _stream(dev)),
            "rw4_quantize_act_static")
     return qa, sa
+
+
+def quantize_act_rrs_reorder(t: Transform, x, qa=None, sa=None, order=None, workspace=None):
+    """Rotated Runtime Smooth with the channel reorder: returns (qa, sa, order).
+
+    qa holds the codes in the reordered channel order; order (int32 [K]) is
+    the permutation to apply to the weights' codes (permute_codes)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    if qa is None:
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    if order is None:
+        order = torch.empty((K,), dtype=torch.int32, device=x.device)
+    nbytes = int(lib.rw4_rrs_reorder_workspace_bytes(K))
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=x.device)
+    _out("qa", qa, (M, K // 2), torch.uint8, dev)
+    _out("sa", sa, (M, K // 128), torch.float32, dev)
+    _out("order", order, (K,), torch.int32, dev)
+    _on_gpu("workspace", workspace, dev)
+    if not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes")
+    _check(lib.rw4_quantize_act_rrs_reorder(t.handle, x.data_ptr(), _dtype_code(x), M, x.stride(0), qa.data_ptr(),
+                                            sa.data_ptr(), order.data_ptr(), workspace.data_ptr(), _stream(dev)),
+           "rw4_quantize_act_rrs_reorder")
+    return qa, sa, order
+
+
+def pack_weight_per_channel(t: Transform, w, layout: str = "kn", qw=None, sw=None):
+    """pack_weight with one scale per output channel (stored in every group column)."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    dev = _on_gpu("w", w)
+    if layout == "kn":
+        K, N = w.shape
+        sk, sn = w.stride(0), w.stride(1)
+    elif layout == "nk":
+        N, K = w.shape
+        sn, sk = w.stride(0), w.stride(1)
+    else:
+        raise ValueError(layout)
+    if K != t.K:
+        raise ValueError(f"w has {K} input channels, the transform {t.K}")
+    if qw is None:
+        qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    if sw is None:
+        sw = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
+    _out("qw", qw, (N, K // 2), torch.uint8, dev)
+    _out("sw", sw, (N, K // 128), torch.float32, dev)
+    _check(lib.rw4_pack_weight_per_channel(t.handle, w.data_ptr(), _dtype_code(w), N, sk, sn, qw.data_ptr(),
+                                           sw.data_ptr(), _stream(dev)),
+           "rw4_pack_weight_per_channel")
+    return qw, sw
+
+
+def permute_codes(q, order, out=None):
+    """out[r, j] = code order[j] of row r of the packed codes q [rows, K/2]."""
+    return prepare_permute_codes(q, order, out)()
+
+
+def prepare_permute_codes(q, order, out=None) -> Call:
+    torch = _torch()
+    rows, Kh = q.shape
+    K = 2 * Kh
+    dev = _on_gpu("q", q)
+    _on_gpu("order", order, dev)
+    if q.dtype != torch.uint8 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous uint8 tensor")
+    if order.shape != (K,) or order.dtype != torch.int32 or not order.is_contiguous():
+        raise ValueError(f"order must be a contiguous int32 tensor of {K} entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _out("out", out, (rows, Kh), torch.uint8, dev)
+    args = (q.data_ptr(), rows, K, order.data_ptr(), out.data_ptr())
+    return Call(lib.rw4_permute_codes, args, dev, "rw4_permute_codes", (q, order), out)
 
 
 def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: int = 128):

@@ -381,6 +381,59 @@ rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, co
   return rw4_quantize_act(t, mode, x, x_dtype, M, ldx, qa, sa, ws, stream);
 }
 
+int64_t rw4_rrs_reorder_workspace_bytes(int64_t K) {
+  if (K <= 0 || K % kGroup) return 0;
+  return rw4::rrs_reorder_workspace_bytes(K);
+}
+
+rw4_status rw4_quantize_act_rrs_reorder(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M,
+                                        int64_t ldx, uint8_t* qa, float* sa, int32_t* order, void* workspace,
+                                        void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0) return RW4_ERR_SHAPE;
+  const int64_t K = t->dev.K;
+  if (t->dev.kind != rw4::TransformKind::Hadamard || !rw4::rrs_reorder_supported(K)) return RW4_ERR_UNSUPPORTED;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (M == 0) return RW4_OK;
+  if (!x || !qa || !sa || !order || !workspace) return RW4_ERR_ARG;
+  if (ldx < K) return RW4_ERR_ARG;
+  const int64_t esz = x_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * esz) % 16 || !aligned16(qa) || !aligned16(sa) || !aligned16(order) ||
+      !aligned16(workspace))
+    return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_quantize_act_rrs_reorder(t->dev, x, x_dtype == RW4_BF16, M, ldx, qa, sa, order,
+                                                       workspace, st));
+}
+
+rw4_status rw4_pack_weight_per_channel(const rw4_transform* t, const void* w, rw4_dtype w_dtype, int64_t N,
+                                       int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw, void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (w_dtype != RW4_F32 && w_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (N < 0) return RW4_ERR_SHAPE;
+  if (t->dev.kind != rw4::TransformKind::Hadamard || !rw4::rowh_supported(t->dev.K)) return RW4_ERR_UNSUPPORTED;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (N == 0) return RW4_OK;
+  if (!w || !qw || !sw) return RW4_ERR_ARG;
+  if (stride_k <= 0 || stride_n <= 0) return RW4_ERR_ARG;
+  const int64_t esz = w_dtype == RW4_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(w) % esz) || !aligned16(qw) || !aligned16(sw)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_pack_weight_per_channel(t->dev, w, w_dtype == RW4_BF16, N, stride_k, stride_n, qw, sw,
+                                                      st));
+}
+
+rw4_status rw4_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const int32_t* order, uint8_t* out,
+                             void* stream) {
+  if (rows < 0 || K <= 0 || K % kGroup || K > 8192) return RW4_ERR_SHAPE;
+  if (rows == 0) return RW4_OK;
+  if (!q || !order || !out || q == out) return RW4_ERR_ARG;
+  if (!aligned16(q) || !aligned16(order) || !aligned16(out)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_permute_codes(q, rows, K, order, out, st));
+}
+
 rw4_status rw4_pack_weight_g(const rw4_transform* t, int32_t group, const void* w, rw4_dtype w_dtype,
                              int64_t N, int64_t stride_k, int64_t stride_n, uint8_t* qw, float* sw,
                              void* stream) {

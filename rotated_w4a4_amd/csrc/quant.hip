@@ -827,6 +827,248 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
 }
 
 // ---------------------------------------------------------------------------
+// Rotated Runtime Smooth with the channel reorder (the Rotated Runtime Smooth
+// page, Figure 4 (1)-(2)): per-channel maxima of |x~| over all rows of the
+// call, channels ordered by decreasing maximum (equal maxima by increasing
+// index), groups of 128 consecutive reordered channels with the group's
+// largest maximum as smoothing scale, then the per-token quantizer on the
+// reordered row.  Row transforms of any Hadamard block (quant_rowh layout:
+// lane l holds channels 512 c + 8 l + e in natural order).
+//   rrs_chanmax      per-block maxima of every channel      -> partial [P][K]
+//   chanmax_reduce   maximum over the P partial rows         -> m [K]
+//   rrs_rank         rank of every channel, group scales     -> order [K], s [K/128]
+//   quant_rrs_order  transform, gather the row in order through LDS, smooth,
+//                    per-token INT4, pack (codes in reordered channel order)
+// ---------------------------------------------------------------------------
+constexpr int kChanmaxBlocks = 256;
+
+template <int E, class Src>
+__global__ __launch_bounds__(256) void rrs_chanmax_kernel(Src src, int64_t M, int log2b, float* __restrict__ partial) {
+  constexpr int K = E * 64;
+  __shared__ float red[K];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  float cmax[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) cmax[e] = 0.0f;
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) cmax[e] = fmaxf(cmax[e], fabsf(v[e]));
+  }
+  // the four waves of the block in turn: wave 0 stores, the others take the maximum
+  for (int t = 0; t < 4; ++t) {
+    if (w == t) {
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = c * 512 + lane * 8 + e;
+          red[j] = t == 0 ? cmax[c * 8 + e] : fmaxf(red[j], cmax[c * 8 + e]);
+        }
+    }
+    __syncthreads();
+  }
+  for (int j = threadIdx.x; j < K; j += blockDim.x) partial[int64_t(blockIdx.x) * K + j] = red[j];
+}
+
+// m[j] = max over the P partial rows (one thread per channel).
+__global__ __launch_bounds__(256) void chanmax_reduce_kernel(const float* __restrict__ partial, int P, int64_t K,
+                                                             float* __restrict__ m) {
+  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  float v = 0.0f;
+  for (int p = 0; p < P; ++p) v = fmaxf(v, partial[int64_t(p) * K + j]);
+  m[j] = v;
+}
+
+// rank(j) = #{i : m_i > m_j} + #{i < j : m_i == m_j}: the position of
+// channel j in decreasing order of the maxima, equal maxima by increasing
+// index (unique ranks, so order is a permutation).  A block takes 16
+// channels; its 16 groups of 16 threads count over 16 slices of the
+// channels, then add up.  The channel of rank 128 g opens group g, and its
+// maximum is the group's smoothing scale.
+__global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__ m, int64_t K,
+                                                       int32_t* __restrict__ order, float* __restrict__ s_g) {
+  extern __shared__ float ms[];  // K maxima, then 256 partial counts
+  int* cnt = reinterpret_cast<int*>(ms + K);
+  for (int64_t i = threadIdx.x; i < K; i += blockDim.x) ms[i] = m[i];
+  __syncthreads();
+  const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const int64_t j = int64_t(blockIdx.x) * 16 + c;
+  const float mj = j < K ? ms[j] : 0.0f;
+  const int64_t slice = K / 16;
+  int n = 0;
+  for (int64_t i = r * slice; i < (r + 1) * slice; ++i) {
+    const float mi = ms[i];
+    n += (mi > mj) || (mi == mj && i < j);
+  }
+  cnt[threadIdx.x] = n;
+  __syncthreads();
+  if (r == 0 && j < K) {
+    int rank = 0;
+    for (int k = 0; k < 16; ++k) rank += cnt[k * 16 + c];
+    order[rank] = int32_t(j);
+    if ((rank & (kGroup - 1)) == 0) s_g[rank / kGroup] = mj;
+  }
+}
+
+// Second pass: one wave per row.  The transformed row goes to the wave's
+// LDS slice in natural channel order and is read back in the given order,
+// so lane l then holds reordered positions 512 c + 8 l + e; their group is
+// 4 c + l / 16, as in quant_rowh.
+template <int E, class Src>
+__global__ __launch_bounds__(256) void quant_rrs_order_kernel(Src src, int64_t M, int log2b,
+                                                              const int32_t* __restrict__ order,
+                                                              const float* __restrict__ smooth,
+                                                              uint8_t* __restrict__ q, float* __restrict__ s,
+                                                              float post_scale) {
+  constexpr int K = E * 64;
+  constexpr int NC = E / 8;
+  constexpr int64_t G = E / 2;
+  __shared__ float rowbuf[4][K];
+  __shared__ int32_t ord[K];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const int sub = lane & 15;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
+  __syncthreads();
+  float inv_s[NC], s_g[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    s_g[c] = smooth[c * 4 + (lane >> 4)];
+    inv_s[c] = safe_inv(s_g[c], 1.0f);
+  }
+  float* buf = rowbuf[w];
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) buf[c * 512 + lane * 8 + e] = v[c * 8 + e];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c * 8 + e] = buf[ord[c * 512 + lane * 8 + e]];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[c * 8 + e] *= inv_s[c];
+        m = fmaxf(m, fabsf(v[c * 8 + e]));
+      }
+    m = max_x<1>(m);
+    m = max_x<2>(m);
+    m = max_x<4>(m);
+    m = max_x<8>(m);
+    m = max_x<16>(m);
+    m = max_x<32>(m);
+    const float a_t = m * (1.0f / 7.0f);
+    uint32_t* qrow = reinterpret_cast<uint32_t*>(q + row * (G * 64));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t b[8];
+      encode<8>(&v[c * 8], m, b);
+      qrow[c * 64 + lane] = pack8_bits(b);
+      if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
+    }
+  }
+}
+
+// Per-output-channel weights: the row transform, then one symmetric INT4
+// scale over the whole transformed row (max / 7), stored in every group
+// column (the Rotated Runtime Smooth experimental setup quantizes weights
+// per channel; a channel permutation then only permutes the codes).
+template <int E, class Src>
+__global__ __launch_bounds__(256) void quant_row_perchannel_kernel(Src src, int64_t M, int log2b,
+                                                                   uint8_t* __restrict__ q, float* __restrict__ s,
+                                                                   float post_scale) {
+  constexpr int NC = E / 8;
+  constexpr int64_t G = E / 2;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const int sub = lane & 15;
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[E];
+    load_row<E>(src, row, lane, v);
+    fwht_row<E>(v, lane, log2b);
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = max_x<1>(m);
+    m = max_x<2>(m);
+    m = max_x<4>(m);
+    m = max_x<8>(m);
+    m = max_x<16>(m);
+    m = max_x<32>(m);
+    uint32_t* qrow = reinterpret_cast<uint32_t*>(q + row * (G * 64));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t b[8];
+      encode<8>(&v[c * 8], m, b);
+      qrow[c * 64 + lane] = pack8_bits(b);
+      if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
+    }
+  }
+}
+
+// Codes of every row taken in channel order: out[r, j] = code(q[r], order[j]).
+// A block walks rows with the order in LDS; each row's stored words are
+// staged in LDS, every thread builds whole output words (8 codes).  The
+// stored form puts the sign of code e in bit 3 of nibble (e + 1) mod 8 of its
+// word.
+__global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t K,
+                                                            const int32_t* __restrict__ order,
+                                                            uint8_t* __restrict__ out) {
+  extern __shared__ uint32_t pc_smem[];  // K order entries, then K / 8 stored words of a row
+  int32_t* ord = reinterpret_cast<int32_t*>(pc_smem);
+  uint32_t* words = pc_smem + K;
+  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
+  const int64_t W = K / 8;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    __syncthreads();  // order staged / the previous row's words consumed
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q + row * (K / 2));
+    for (int64_t i = threadIdx.x; i < W; i += blockDim.x) words[i] = src[i];
+    __syncthreads();
+    uint32_t* dst = reinterpret_cast<uint32_t*>(out + row * (K / 2));
+    for (int64_t i = threadIdx.x; i < W; i += blockDim.x) {
+      int code[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int32_t k = int32_t(min(uint32_t(ord[i * 8 + e]), uint32_t(K - 1)));  // clamped into the row
+        const uint32_t wd = words[k >> 3];
+        const int n = k & 7;
+        const int mag = int((wd >> (4 * n)) & 7u);
+        const int neg = int((wd >> (4 * ((n + 1) & 7) + 3)) & 1u);
+        code[e] = neg ? -mag : mag;
+      }
+      uint32_t o = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mag = uint32_t(code[e] < 0 ? -code[e] : code[e]);
+        const uint32_t prev_neg = code[(e + 7) & 7] < 0 ? 8u : 0u;
+        o |= (mag | prev_neg) << (4 * e);
+      }
+      dst[i] = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Rotation without quantization: x~ = x R (Hadamard, optionally signed) or
 // x R D^-1 (Givens), written as fp32 or bf16 (round to nearest even).  The
 // query side of an INT4 KV cache: keys are stored rotated and quantized, the
@@ -1106,6 +1348,102 @@ hipError_t launch_rotate_src(const TransformDev& t, const Src& src, int64_t M, v
 }
 
 }  // namespace
+
+int64_t rrs_reorder_workspace_bytes(int64_t K) {
+  return (int64_t(kChanmaxBlocks) + 1) * K * 4 + (K / kGroup) * 4;
+}
+
+namespace {
+
+template <class Src>
+hipError_t launch_rrs_reorder_src(const Src& src, int64_t K, int log2b, int64_t M, uint8_t* q, float* s,
+                                  int32_t* order, float* ws, float post, hipStream_t st) {
+  float* partial = ws;
+  float* m = ws + int64_t(kChanmaxBlocks) * K;
+  float* smooth = m + K;
+  const int grid = grid_for_waves(M, 256 * 16);
+  const int rank_lds = int(K * 4 + 256 * 4);
+  auto run = [&](auto e_const) {
+    constexpr int E = decltype(e_const)::value;
+    hipLaunchKernelGGL((rrs_chanmax_kernel<E, Src>), dim3(kChanmaxBlocks), dim3(256), 0, st, src, M, log2b, partial);
+    hipLaunchKernelGGL(chanmax_reduce_kernel, dim3(unsigned((K + 255) / 256)), dim3(256), 0, st,
+                       (const float*)partial, kChanmaxBlocks, K, m);
+    hipLaunchKernelGGL(rrs_rank_kernel, dim3(unsigned(K / 16)), dim3(256), rank_lds, st, (const float*)m, K, order,
+                       smooth);
+    hipLaunchKernelGGL((quant_rrs_order_kernel<E, Src>), dim3(grid), dim3(256), 0, st, src, M, log2b,
+                       (const int32_t*)order, (const float*)smooth, q, s, post);
+    return hipGetLastError();
+  };
+  switch (K) {
+    case 512: return run(std::integral_constant<int, 8>{});
+    case 1024: return run(std::integral_constant<int, 16>{});
+    case 2048: return run(std::integral_constant<int, 32>{});
+    case 4096: return run(std::integral_constant<int, 64>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class Src>
+hipError_t launch_perchannel_src(const Src& src, int64_t K, int log2b, int64_t N, uint8_t* q, float* s, float post,
+                                 hipStream_t st) {
+  const int grid = grid_for_waves(N, 256 * 16);
+  auto run = [&](auto e_const) {
+    constexpr int E = decltype(e_const)::value;
+    hipLaunchKernelGGL((quant_row_perchannel_kernel<E, Src>), dim3(grid), dim3(256), 0, st, src, N, log2b, q, s, post);
+    return hipGetLastError();
+  };
+  switch (K) {
+    case 512: return run(std::integral_constant<int, 8>{});
+    case 1024: return run(std::integral_constant<int, 16>{});
+    case 2048: return run(std::integral_constant<int, 32>{});
+    case 4096: return run(std::integral_constant<int, 64>{});
+    case 8192: return run(std::integral_constant<int, 128>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool rrs_reorder_supported(int64_t K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
+
+hipError_t launch_quantize_act_rrs_reorder(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
+                                           uint8_t* q, float* s, int32_t* order, void* workspace, hipStream_t st) {
+  int log2b = 0;
+  while ((int64_t(1) << log2b) < t.block) ++log2b;
+  const float post = 1.0f / sqrtf(float(t.block));  // the per-token scale a_t carries the 1/7
+  float* ws = static_cast<float*>(workspace);
+  if (t.sign_mask) {
+    if (bf16)
+      return launch_rrs_reorder_src(SignedSrc<RowSrc<true>>{{x, ldx}, t.sign_mask}, t.K, log2b, M, q, s, order, ws,
+                                    post, st);
+    return launch_rrs_reorder_src(SignedSrc<RowSrc<false>>{{x, ldx}, t.sign_mask}, t.K, log2b, M, q, s, order, ws,
+                                  post, st);
+  }
+  if (bf16) return launch_rrs_reorder_src(RowSrc<true>{x, ldx}, t.K, log2b, M, q, s, order, ws, post, st);
+  return launch_rrs_reorder_src(RowSrc<false>{x, ldx}, t.K, log2b, M, q, s, order, ws, post, st);
+}
+
+hipError_t launch_pack_weight_per_channel(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
+                                          int64_t sn, uint8_t* q, float* s, hipStream_t st) {
+  int log2b = 0;
+  while ((int64_t(1) << log2b) < t.block) ++log2b;
+  const float post = (1.0f / 7.0f) / sqrtf(float(t.block));
+  if (t.sign_mask) {
+    if (bf16)
+      return launch_perchannel_src(SignedSrc<StridedSrc<true>>{{w, sk, sn}, t.sign_mask}, t.K, log2b, N, q, s, post, st);
+    return launch_perchannel_src(SignedSrc<StridedSrc<false>>{{w, sk, sn}, t.sign_mask}, t.K, log2b, N, q, s, post, st);
+  }
+  if (bf16) return launch_perchannel_src(StridedSrc<true>{w, sk, sn}, t.K, log2b, N, q, s, post, st);
+  return launch_perchannel_src(StridedSrc<false>{w, sk, sn}, t.K, log2b, N, q, s, post, st);
+}
+
+hipError_t launch_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const int32_t* order, uint8_t* out,
+                                hipStream_t st) {
+  const int64_t grid = rows < 1024 ? rows : 1024;
+  const int lds = int(K * 4 + (K / 8) * 4);
+  hipLaunchKernelGGL(permute_codes_kernel, dim3(unsigned(grid)), dim3(256), lds, st, q, rows, K, order, out);
+  return hipGetLastError();
+}
 
 // Rotation without quantization of row-major activations X [M, K].
 hipError_t launch_rotate_act(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx, void* out,

@@ -36,6 +36,17 @@ hipError_t launch_pack_weight(const TransformDev& t, const void* w, bool bf16, i
 hipError_t launch_rotate_act(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st);
 
+// Rotated Runtime Smooth with the channel reorder (Hadamard transforms, K in
+// {512, 1024, 2048, 4096}); workspace of rrs_reorder_workspace_bytes(K).
+bool rrs_reorder_supported(int64_t K);
+int64_t rrs_reorder_workspace_bytes(int64_t K);
+hipError_t launch_quantize_act_rrs_reorder(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
+                                           uint8_t* q, float* s, int32_t* order, void* workspace, hipStream_t st);
+hipError_t launch_pack_weight_per_channel(const TransformDev& t, const void* w, bool bf16, int64_t N, int64_t sk,
+                                          int64_t sn, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const int32_t* order, uint8_t* out,
+                                hipStream_t st);
+
 hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, int group, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st);
 

@@ -341,3 +341,31 @@ def test_every_entry_point_declares_its_argument_types():
         if n in ("rw4_version",):
             continue
         assert getattr(lib, n).argtypes is not None, n
+
+
+def test_reorder_entry_points_validation():
+    assert lib.rw4_rrs_reorder_workspace_bytes(100) == 0
+    assert lib.rw4_rrs_reorder_workspace_bytes(4096) == (256 + 1) * 4096 * 4 + 32 * 4
+    f = lib.rw4_quantize_act_rrs_reorder
+    assert f(None, FAKE, 1, 4, 4096, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    st, h = _had(8192, 8192)
+    assert st == OK
+    try:  # K = 8192 is beyond the reorder kernels
+        assert f(h, FAKE, 1, 4, 8192, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+    finally:
+        lib.rw4_transform_destroy(h)
+    st, h = _had(4096, 4096)
+    try:
+        assert f(h, FAKE, 1, 0, 4096, None, None, None, None, None) == OK      # empty
+        assert f(h, FAKE, 1, 4, 4096, FAKE, FAKE, FAKE, None, None) == ARG     # no workspace
+        assert f(h, FAKE, 1, 4, 4096, FAKE, FAKE, None, FAKE, None) == ARG     # no order
+        assert f(h, FAKE, 1, -1, 4096, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+        assert lib.rw4_pack_weight_per_channel(h, FAKE, 1, 4, 0, 1, FAKE, FAKE, None) == ARG  # stride 0
+    finally:
+        lib.rw4_transform_destroy(h)
+    p = lib.rw4_permute_codes
+    assert p(FAKE, 4, 100, FAKE, FAKE + 64, None) == SHAPE
+    assert p(FAKE, 4, 16384, FAKE, FAKE + 64, None) == SHAPE
+    assert p(FAKE, 0, 128, None, None, None) == OK
+    assert p(FAKE, 4, 128, FAKE, FAKE, None) == ARG   # in place
+    assert p(FAKE, 4, 128, None, FAKE + 64, None) == ARG
