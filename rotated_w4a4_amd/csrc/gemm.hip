@@ -561,8 +561,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 // fragment reads are then ordinary loads that it schedules itself, issued
 // a K-half (or a group) ahead of the MFMAs that consume them, with partial
 // lgkmcnt waits (the asm reads of gemm_f8_kernel wait for all of their own
-// results at once).  Bit-identical results; measured 8-10 % faster at
-// 4096 x 14336 x 4096 and 8192 x 4096 x 11008.
+// results at once).  Bit-identical results; the pipelining measured 8-10 %
+// faster at 4096 x 14336 x 4096 and 8192 x 4096 x 11008, and the wave-
+// priority alternation below a further 8-19 %.
 // ---------------------------------------------------------------------------
 constexpr int kStageTileBytes = 2 * kGroupBytes;        // A and B tiles of two groups
 constexpr int kStageSplitBytes = 2 * kSplitGroupBytes;  // their split scale operands
@@ -709,12 +710,30 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
   // wave finished reading them before the barrier); compute the two groups
   // with each K-half's fragments read one step ahead; split the scales of
   // stage s + 1.  Loads past the last group are clamped and never read.
-  put_split(sA, 0, sc_load(0));
-  put_split(sA, 1, sc_load(1));
+  // the first stage's DMA goes out before the wait for its scales, so the
+  // two memory latencies overlap
   issue(tA, 0, 0);
   issue(tA, 1, 1);
+  {
+    const float x0 = sc_load(0), x1 = sc_load(1);
+    put_split(sA, 0, x0);
+    put_split(sA, 1, x1);
+  }
   const int64_t S = (G + 1) / 2;
+  // Wave priority alternates stage by stage, opposite for odd and even
+  // blocks.  Two blocks share a CU, and the arbiter otherwise lets the
+  // older block's waves win: it finished ~7.6 us before the younger one at
+  // 2048 x 4096 x 4096 (per-block timestamps), leaving one wave per SIMD for
+  // the tail.  With the alternation the pair ends ~1.2 us apart.  Measured
+  // over rotating 512 MiB buffer sets, on two boxes: 4096 x 14336 x 4096
+  // -13 % and -19 %, 8192 x 4096 x 11008 -8 % and -10 %, 2048 x 4096 x 4096
+  // -3 %.  Toggling every group instead of every stage was 20-40 % slower.
+  const int prio_phase = int(blockIdx.x & 1);
   auto stage = [&](uint8_t* Tc, uint8_t* Sc, uint8_t* Tn, uint8_t* Sn, int64_t s) {
+    if (((s + prio_phase) & 1) != 0)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(0);
     wait_vm_barrier<0>();
     const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
     issue(Tn, 0, 2 * s + 2);
@@ -743,6 +762,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     if (s + 1 >= S) break;
     stage(tB, sB, tA, sA, s + 1);
   }
+  __builtin_amdgcn_s_setprio(0);
   // drain the trailing DMA before the stage arrays are reused for the output
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
   asm volatile("s_barrier" ::: "memory");
