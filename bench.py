@@ -160,7 +160,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
-                             "decode128", "decode256", "tiny", "kv", "rrs_reorder"])
+                             "decode128", "decode256", "tiny", "kv", "rrs_reorder", "fused1", "fused2", "fused4",
+                             "fused8", "fused16"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
@@ -179,6 +180,7 @@ KERNEL_SOURCES = {
     "gemm_f8_kernel": ["gemm.hip", "rw4_device.h"],
     "gemm_f8p_kernel": ["gemm.hip", "rw4_device.h"],
     "gemm_small_kernel": ["gemm.hip", "rw4_device.h"],
+    "decode_fused_kernel": ["gemm.hip", "rw4_device.h"],
     "quant_h128_act_kernel": ["quant.hip", "rw4_device.h"],
     "quant_h128_kernel": ["quant.hip", "rw4_device.h"],
     "quant_rrs_full_kernel": ["quant.hip", "rw4_device.h"],
@@ -489,6 +491,63 @@ def main_rrs_reorder(args, torch, rw4, gu, dev):
     print(json.dumps(out), flush=True)
 
 
+def main_decode_fused(args, torch, rw4, gu, dev):
+    """One decode step in one launch (decode_fused: quantize inside the small-M GEMM) on the
+    decode shape with the block-128 Hadamard, M = 1..16 tokens, against the two launches
+    (quantize_act + w4a4_gemm) it replaces."""
+    import datagen
+    M = int(args.workload[len("fused"):])
+    wl = datagen.make("decode", M=M)
+    K, N = wl.K, wl.N
+    t = rw4.Transform.hadamard(K, 128)
+    x = gu.x_to_device(wl.x, wl.x_dtype)
+    qw0, sw0 = rw4.pack_weight(t, torch.from_numpy(wl.w).to(dev))
+    nsets = max(2, math.ceil(MALL_FLUSH_BYTES / (N * K // 2 + N * K // 32)))
+    sets = [(qw0.clone(), sw0.clone(), torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    fused = [rw4.prepare_decode_fused(t, x, q, s, out=y) for q, s, y in sets]
+    qc = rw4.prepare_quantize_act(t, x, qa=qa, sa=sa)
+    gc = [rw4.prepare_w4a4_gemm(qa, sa, q, s, out=y) for q, s, y in sets]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        fused[i % nsets]()
+
+    def two(i):
+        qc()
+        gc[i % nsets]()
+
+    for i in range(args.warmup):
+        step(i)
+        two(i)
+    r0, r1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    (f_us, f_ok), (t_us, t_ok) = gpu_bound_us(torch, stream, step, reps=40), gpu_bound_us(torch, stream, two, reps=40)
+    ops = 2.0 * M * N * K
+    hbm = M * K * 2 + N * K // 2 + N * (K // 128) * 4 + M * N * 2  # x, weights, scales, y
+    log(f"decode_fused M={M} K={K} N={N}: {f_us:.2f} us per step back to back (host ahead {f_ok}); "
+        f"quantize_act + w4a4_gemm {t_us:.2f} us (host ahead {t_ok})")
+    out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "config": {"workload": f"decode_fused M={M} K={K} N={N}", "transform": "hadamard128",
+                      "act_mode": "group128"},
+           "fused_us": f_us, "two_launch_us": t_us,
+           "roofline": {"bound": "hbm", "achieved": hbm / f_us / 1e3, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": hbm / f_us / 1e3 / PEAK_HBM_GBPS, "traffic": None, "kernel": "decode_fused_kernel",
+                        "avg_launch_us": f_us, "algorithmic_bytes": hbm}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -516,6 +575,8 @@ def main():
         return main_kv(args, torch, rw4, gu, dev)
     if args.workload == "rrs_reorder":
         return main_rrs_reorder(args, torch, rw4, gu, dev)
+    if args.workload.startswith("fused"):
+        return main_decode_fused(args, torch, rw4, gu, dev)
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group

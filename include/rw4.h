@@ -203,6 +203,24 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
 rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, const void* x, rw4_dtype x_dtype,
                                    int64_t M, int64_t ldx, uint8_t* qa, float* sa, void* stream);
 
+/* ---- One decode step in one launch ---------------------------------------
+ * y [M, N] = w4a4_gemm(quantize_act(t, x), qw, sw) for a decode-sized step
+ * (1 <= M <= 16 tokens) in one kernel launch (the independent-rotation
+ * article, section 3.2: rotate, scale and quantize in one kernel; the
+ * QuIP#/QTIP page, section 6.1: precomputed fused kernels against launch
+ * latency).  Each wave transforms and quantizes exactly the 128-channel
+ * slices its own MFMAs consume; the codes never reach memory and nothing is
+ * allocated.  Transform: the block-128 Hadamard, with or without random
+ * signs (others: RW4_ERR_UNSUPPORTED; the Givens rotation, done in every
+ * block, costs more than the launch it saves).  x as for rw4_quantize_act
+ * (M <= 16, else RW4_ERR_SHAPE); qw/sw and y as for rw4_w4a4_gemm (group
+ * 128).  The codes, scales and products are those of rw4_quantize_act and
+ * rw4_w4a4_gemm, summed in the same order, so y equals those two calls in a
+ * row. */
+rw4_status rw4_decode_fused(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                            const uint8_t* qw, const float* sw, int64_t N, void* y, rw4_dtype y_dtype, int64_t ldy,
+                            void* stream);
+
 /* ---- Rotated Runtime Smooth with the channel reorder --------------------
  * The Rotated Runtime Smooth page, Figure 4 (1): activations and weights are
  * reordered by the channel-wise maxima of the activations (Y is a sum over

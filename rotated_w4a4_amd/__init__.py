@@ -25,7 +25,7 @@ __all__ = [
     "LIB_PATH", "lib", "RW4Error", "Transform", "quantize_act", "pack_weight", "w4a4_gemm",
     "dequantize", "rotate_act", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
     "prepare_rotate_act", "quantize_act_static", "quantize_act_rrs_reorder", "pack_weight_per_channel",
-    "permute_codes", "prepare_permute_codes",
+    "permute_codes", "prepare_permute_codes", "decode_fused", "prepare_decode_fused",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
     "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_quantize_act_static", "rw4_status_str",
     "rw4_version", "rw4_rrs_reorder_workspace_bytes", "rw4_quantize_act_rrs_reorder", "rw4_pack_weight_per_channel",
-    "rw4_permute_codes",
+    "rw4_permute_codes", "rw4_decode_fused",
 )
 
 
@@ -89,6 +89,7 @@ lib.rw4_rrs_reorder_workspace_bytes.restype = _i64
 lib.rw4_quantize_act_rrs_reorder.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p]
 lib.rw4_pack_weight_per_channel.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_permute_codes.argtypes = [_p, _i64, _i64, _p, _p, _p]
+lib.rw4_decode_fused.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, ctypes.c_int, _i64, _p]
 for _name in EXPORTED_SYMBOLS:
     if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k", "rw4_rrs_reorder_workspace_bytes"):
         getattr(lib, _name).restype = ctypes.c_int
@@ -390,6 +391,38 @@ def prepare_permute_codes(q, order, out=None) -> Call:
     _out("out", out, (rows, Kh), torch.uint8, dev)
     args = (q.data_ptr(), rows, K, order.data_ptr(), out.data_ptr())
     return Call(lib.rw4_permute_codes, args, dev, "rw4_permute_codes", (q, order), out)
+
+
+def decode_fused(t: Transform, x, qw, sw, out_dtype=None, out=None):
+    """One decode step in one launch: y = w4a4_gemm(quantize_act(t, x), qw, sw), 1..16 rows."""
+    return prepare_decode_fused(t, x, qw, sw, out_dtype, out)()
+
+
+def prepare_decode_fused(t: Transform, x, qw, sw, out_dtype=None, out=None) -> Call:
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    N = qw.shape[0]
+    for name, tns, dt in (("qw", qw, torch.uint8), ("sw", sw, torch.float32)):
+        _on_gpu(name, tns, dev)
+        if tns.dtype != dt or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if qw.shape != (N, K // 2) or sw.shape != (N, K // 128):
+        raise ValueError("weight shapes do not match K (groups of 128)")
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
+    args = (t.handle, x.data_ptr(), _dtype_code(x), M, x.stride(0), qw.data_ptr(), sw.data_ptr(), N,
+            out.data_ptr(), _dtype_code(out), out.stride(0))
+    return Call(lib.rw4_decode_fused, args, dev, "rw4_decode_fused", (t, x, qw, sw), out)
 
 
 def pack_weight(t: Transform, w, layout: str = "kn", qw=None, sw=None, group: int = 128):

@@ -381,6 +381,30 @@ rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, co
   return rw4_quantize_act(t, mode, x, x_dtype, M, ldx, qa, sa, ws, stream);
 }
 
+rw4_status rw4_decode_fused(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                            const uint8_t* qw, const float* sw, int64_t N, void* y, rw4_dtype y_dtype, int64_t ldy,
+                            void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || M > 16 || N < 0) return RW4_ERR_SHAPE;
+  if (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128) return RW4_ERR_UNSUPPORTED;
+  const int64_t K = t->dev.K;
+  if (K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (M == 0 || N == 0) return RW4_OK;
+  if (!x || !qw || !sw || !y) return RW4_ERR_ARG;
+  if (ldx < K || ldy < N) return RW4_ERR_ARG;
+  const int64_t esz = x_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * esz) % 16 || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return RW4_ERR_ARG;
+  // the kernel addresses x with 32-bit buffer offsets
+  if (((M - 1) * ldx + K) * esz > 0x7FFFFFFF) return RW4_ERR_SHAPE;
+  const float post = (1.0f / 7.0f) / sqrtf(128.0f);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_decode_fused(x, x_dtype == RW4_BF16, ldx, t->dev.sign_mask, post, qw, sw, M, N, K, y,
+                                           y_dtype == RW4_BF16, ldy, st));
+}
+
 int64_t rw4_rrs_reorder_workspace_bytes(int64_t K) {
   if (K <= 0 || K % kGroup) return 0;
   return rw4::rrs_reorder_workspace_bytes(K);

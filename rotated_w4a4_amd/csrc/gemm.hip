@@ -1058,6 +1058,275 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode_fused_kernel: quantize_act + w4a4_gemm of a decode-sized step
+// (M <= 16 rows, block-128 Hadamard, 128-wide groups) in one launch (the
+// independent-rotation article, section 3.2, fuses rotate, scale and
+// quantize into one kernel; the QuIP#/QTIP page, section 6.1, precomputes
+// fused kernels against launch latency).  It is gemm_small_kernel (MT = 1)
+// with the activation side produced in place: in every K-iteration, each
+// wave transforms and quantizes the M rows of exactly the two 128-channel
+// slices its own MFMAs consume, straight into its part of the LDS A tile
+// and scale column (no other wave reads them), while the block's weights
+// stream in.  A pass of the quantizer takes four (slice, row) pairs, one
+// per 16-lane DPP row, so a single row costs one pass for both slices.
+// The activations of the next iteration are loaded during the current one.
+// The transform and encoder are quant_h128_act's and the products and their
+// order gemm_small_kernel's, so y equals quantize_act followed by
+// w4a4_gemm.  PS: quantizer passes (2 M <= 4 PS); SG: random signs.
+// ---------------------------------------------------------------------------
+template <bool XBF16, int PS, bool SG>
+struct FusedX {
+  static constexpr int XW = XBF16 ? 1 : 2;  // 16-byte words per lane and pass
+  v4u x[PS][XW];                            // pass p: pair 4 p + lane / 16, channels 8 (lane % 16) ..
+  v4u sm[SG ? 2 : 1][2];                    // random signs of those channels in slices 0 and 1
+};
+
+template <bool BF16, int CT, bool XBF16, int PS, bool SG>
+__global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
+    const void* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ sign_mask, float post,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw, int64_t M, int64_t N, int64_t K,
+    void* __restrict__ y, int64_t ldy) {
+  constexpr int MT = 1, GSZ = 128;
+  using C = SmallCfg<GSZ, MT, CT>;
+  using Stage = SmallStage<GSZ, MT, CT>;
+  using X = FusedX<XBF16, PS, SG>;
+  static_assert(C::NS == 2, "two slices per wave and iteration");
+  constexpr int ES = XBF16 ? 2 : 4;
+  __shared__ __align__(16) uint8_t lds[C::BYTES];
+  v4u* const As = reinterpret_cast<v4u*>(lds);
+  uint8_t* const Ab = lds;
+  float* const saT = reinterpret_cast<float*>(lds + C::SA_OFF);
+  float* const swT = reinterpret_cast<float*>(lds + C::SW_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int am = lane & 15;
+  const int part = lane >> 4;
+  const int sub = lane & 15;
+  const int64_t SL = K / kGroup;
+  const int64_t GS = SL;
+  const int64_t rowbytes = K / 2;
+  const int64_t n0 = int64_t(blockIdx.x) * 16 * CT;
+  const int64_t nrows = N - n0 < 16 * CT ? N - n0 : 16 * CT;
+  const int64_t NI = (SL + C::GB - 1) / C::GB;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + n0 * rowbytes, nrows * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw + n0 * GS, nrows * GS * 4);
+  // rows 0..M-1 of pitch ldx (the host checks the range < 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, ((M - 1) * ldx + K) * ES);
+  const __amdgpu_buffer_rsrc_t rsm = make_rsrc(sign_mask, SG ? K * 4 : 0);
+
+  // the weight side of iteration it: weights and their scales
+  auto issue_b = [&](Stage& S, int64_t it) __attribute__((always_inline)) {
+    const int64_t s0 = it * C::GB;
+#pragma unroll
+    for (int j = 0; j < C::SWR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      const int64_t col = s0 + idx % C::CW;
+      const bool ok = idx < C::SWE && col < GS;
+      S.sw[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsw, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
+    }
+#pragma unroll
+    for (int ns = 0; ns < C::NS; ++ns) {
+      const int64_t sl = s0 + wave * C::NS + ns;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        S.b[ct][ns] = __builtin_bit_cast(
+            v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                     rb, int(sl < SL ? uint32_t((ct * 16 + am) * rowbytes + sl * 64 + part * 16) : kNoRead), 0, 0));
+    }
+  };
+  auto store_b = [&](const Stage& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < C::SWR; ++j) {
+      const int idx = j * kSmallThreads + tid;
+      swT[idx < C::SWE ? (idx % C::CW) * (16 * CT) + idx / C::CW : idx] = S.sw[j];
+    }
+  };
+
+  // the activation side of iteration it for this wave: pair q = 4 p + part
+  // of pass p is (slice 2 wave + q % 2, row q / 2); rows past M read zeros
+  // (past the buffer range), slices past K too
+  X xs;
+  auto issue_x = [&](int64_t it) __attribute__((always_inline)) {
+    const int64_t g0 = it * C::GB + wave * C::NS;
+#pragma unroll
+    for (int p = 0; p < PS; ++p) {
+      const int q = 4 * p + part;
+      const int64_t g = g0 + (q & 1);
+      const int64_t row = q >> 1;
+      const uint32_t off = g < SL && row < M ? uint32_t((row * ldx + g * kGroup + sub * 8) * ES) : kNoRead;
+#pragma unroll
+      for (int i = 0; i < X::XW; ++i)
+        xs.x[p][i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rx, int(off + 16 * i), 0, 0));
+    }
+    if constexpr (SG) {
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns) {
+        const int64_t g = g0 + ns;
+        const uint32_t off = g < SL ? uint32_t((g * kGroup + sub * 8) * 4) : kNoRead;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          xs.sm[ns][i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsm, int(off + 16 * i), 0, 0));
+      }
+    }
+  };
+
+  const int word = h128_lane_word(sub);
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  const float flip = parity_sign(lane & 15);
+  auto quantize = [&](int64_t it) __attribute__((always_inline)) {
+    const int64_t g0 = it * C::GB + wave * C::NS;
+    // slices past K: zero codes and scales (gemm_small_kernel's loads read zeros there)
+#pragma unroll
+    for (int ns = 0; ns < C::NS; ++ns) {
+      if (g0 + ns >= SL) {
+        const int gl = wave * C::NS + ns;
+        for (int64_t m = 0; m < M; ++m) Ab[gl * 64 + m * (C::AROW + 1) * 16 + lane] = 0;
+        if (lane < 16) saT[gl * 16 + lane] = 0.0f;
+      }
+    }
+    auto load_v = [&](int p, float (&v)[8]) __attribute__((always_inline)) {
+      if constexpr (XBF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf16_lo(xs.x[p][0][e]);
+          v[2 * e + 1] = bf16_hi(xs.x[p][0][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(xs.x[p][e >> 2][e & 3]);
+      }
+      if constexpr (SG) {
+        const int ns = (4 * p + part) & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (ns ? xs.sm[1][e >> 2][e & 3] : xs.sm[0][e >> 2][e & 3]));
+      }
+      fwht8(v);
+    };
+    auto finish = [&](int p, float (&v)[8], float mx) __attribute__((always_inline)) {
+      const int q = 4 * p + part;
+      const int ns = q & 1;
+      const int64_t m = q >> 1;
+      const int gl = wave * C::NS + ns;
+      const uint32_t packed = encode8_rcp(v, mx, flip);
+      if (m < M && g0 + ns < SL) {
+        *reinterpret_cast<uint32_t*>(Ab + gl * 64 + m * (C::AROW + 1) * 16 + word * 4) = packed;
+        if (sub == 0) saT[gl * 16 + m] = mx * post;
+      }
+    };
+    auto absmax8 = [](const float (&v)[8]) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+      return mx;
+    };
+#pragma unroll
+    for (int p = 0; p < PS; ++p) {
+      if (2 * M <= 4 * p) break;
+      float v[8];
+      load_v(p, v);
+      lane_stages_dpp(v, c1, c2, c7, c8);
+      finish(p, v, row16_max_dpp(absmax8(v)));
+    }
+  };
+
+  float yv[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yv[ct][r] = 0.0f;
+  auto compute = [&](const Stage& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ns = 0; ns < C::NS; ++ns) {
+      const int gl = wave * C::NS + ns;
+      v8i b[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) b[ct] = f8_operand(S.b[ct][ns]);
+      const v8i a = f8_operand(As[am * (C::AROW + 1) + gl * 4 + part]);
+      const v4f s4 = *reinterpret_cast<const v4f*>(saT + gl * 16 + part * 4);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const v4f acc =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[ct], v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+        const float swv = swT[gl * (16 * CT) + ct * 16 + am];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yv[ct][r] = fmaf(acc[r], s4[r] * swv, yv[ct][r]);
+      }
+    }
+  };
+  // one iteration: the next weights are requested, this iteration's
+  // activations (loaded one iteration ago) are quantized into LDS, the next
+  // activations requested, then the MFMAs
+  auto step = [&](Stage& cur, Stage& nxt, int64_t it) __attribute__((always_inline)) {
+    issue_b(nxt, it + 1);
+    quantize(it);
+    issue_x(it + 1);
+    store_b(cur);
+    __syncthreads();
+    compute(cur);
+    __syncthreads();  // LDS free for the next iteration
+  };
+  Stage s0, s1;
+  issue_x(0);
+  issue_b(s0, 0);
+  for (int64_t it = 0; it < NI; it += 2) {
+    step(s0, s1, it);
+    if (it + 1 >= NI) break;
+    step(s1, s0, it + 1);
+  }
+  float* const red = reinterpret_cast<float*>(lds);  // [wave][tile][lane][4]
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    *reinterpret_cast<v4f*>(red + ((wave * CT + ct) * 64 + lane) * 4) = v4f{yv[ct][0], yv[ct][1], yv[ct][2], yv[ct][3]};
+  __syncthreads();
+  if (wave < CT) {  // wave t adds up output tile t over the waves
+    const int ct = wave;
+    v4f v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) v += *reinterpret_cast<const v4f*>(red + ((w * CT + ct) * 64 + lane) * 4);
+    const int64_t bn = n0 + ct * 16 + am;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = part * 4 + r;
+      if (m < M && bn < N) store_y<BF16>(y, ldy, m, bn, v[r]);
+    }
+  }
+}
+
+hipError_t launch_decode_fused(const void* x, bool x_bf16, int64_t ldx, const uint32_t* sign_mask, float post,
+                               const uint8_t* qw, const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                               bool y_bf16, int64_t ldy, hipStream_t st) {
+  const bool ct2 = N > 12288;  // the channel tiling of gemm_small_kernel for M <= 16
+  const int64_t blocks = (N + (ct2 ? 31 : 15)) / (ct2 ? 32 : 16);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto run = [&](auto yb, auto ct, auto xb, auto mp, auto sg) {
+    hipLaunchKernelGGL((decode_fused_kernel<decltype(yb)::value, decltype(ct)::value, decltype(xb)::value,
+                                            decltype(mp)::value, decltype(sg)::value>),
+                       dim3(unsigned(blocks)), dim3(kSmallThreads), 0, st, x, ldx, sign_mask, post, qw, sw, M, N, K,
+                       y, ldy);
+    return hipGetLastError();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto by_sg = [&](auto yb, auto ct, auto xb, auto mp) { return sign_mask ? run(yb, ct, xb, mp, T{}) : run(yb, ct, xb, mp, F{}); };
+  auto by_mp = [&](auto yb, auto ct, auto xb) {
+    if (M <= 2) return by_sg(yb, ct, xb, std::integral_constant<int, 1>{});
+    if (M <= 4) return by_sg(yb, ct, xb, std::integral_constant<int, 2>{});
+    if (M <= 8) return by_sg(yb, ct, xb, std::integral_constant<int, 4>{});
+    return by_sg(yb, ct, xb, std::integral_constant<int, 8>{});
+  };
+  auto by_x = [&](auto yb, auto ct) { return x_bf16 ? by_mp(yb, ct, T{}) : by_mp(yb, ct, F{}); };
+  auto by_ct = [&](auto yb) {
+    return ct2 ? by_x(yb, std::integral_constant<int, 2>{}) : by_x(yb, std::integral_constant<int, 1>{});
+  };
+  return y_bf16 ? by_ct(T{}) : by_ct(F{});
+}
+
 // Which kernel runs a product.  The tiled kernel gives one 128 x 128 tile per
 // block; below about one block per CU its time is one block's K loop (about
 // 30 us at K = 4096 for any M up to 1024 at N = 4096, measured), while the

@@ -246,4 +246,85 @@ __device__ __forceinline__ void encode(float v[N], float m, uint32_t b[N], float
   for (int e = 0; e < N; ++e) b[e] = rne_code_bits(v[e], inv);
 }
 
+// ---------------------------------------------------------------------------
+// Lane stages of the block-128 activation quantizers (16 lanes x 8 values
+// per group).  The four lane stages run along lane masks 1, 2, 7 and 8,
+// each one DPP move (quad_perm, row_half_mirror, row_ror:8) fused into a
+// v_fmac_f32: x += c_k * x[lane ^ m_k] with c_k = (-1)^parity(lane & t_k)
+// for the dual functionals t = (5, 6, 4, 8) (parity(m_j & t_k) = [j == k]).
+// The product of these stages is the Walsh-Hadamard transform of the
+// 16-lane index up to a signed permutation: lane l ends with
+// (-1)^popcount(l) times the outputs of Sylvester lane f(l), where f is
+// GF(2)-linear with f(1) = 5, f(2) = 6, f(4) = 7, f(8) = 8.  The sign is
+// undone in the encoder (the absolute maximum is unchanged) and the packed
+// word is stored at word f(l) of the group.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int h128_lane_word(int l) {
+  return ((l & 1) ? 5 : 0) ^ ((l & 2) ? 6 : 0) ^ ((l & 4) ? 7 : 0) ^ (l & 8);
+}
+__device__ __forceinline__ float parity_sign(int x) { return (__builtin_popcount(x) & 1) ? -1.0f : 1.0f; }
+
+// The four lane stages on 8 values (asm: the compiler does not fuse the DPP
+// move into the multiply-add).  Each DPP read follows the write of its
+// register by at least 2 wait states: s_nop 1 at entry, then 8 independent
+// instructions between the stages of one value.
+__device__ __forceinline__ void lane_stages_dpp(float (&v)[8], float c1, float c2, float c7, float c8) {
+#define RW4_STAGE(CTRL, C)                                            \
+  "v_fmac_f32_dpp %0, %0, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %1, %1, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %2, %2, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %3, %3, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %4, %4, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %5, %5, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %6, %6, " C " " CTRL " row_mask:0xf bank_mask:0xf\n" \
+  "v_fmac_f32_dpp %7, %7, " C " " CTRL " row_mask:0xf bank_mask:0xf\n"
+  asm volatile("s_nop 1\n"
+               RW4_STAGE("quad_perm:[1,0,3,2]", "%8")
+               RW4_STAGE("quad_perm:[2,3,0,1]", "%9")
+               RW4_STAGE("row_half_mirror", "%10")
+               RW4_STAGE("row_ror:8", "%11")
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7])
+               : "v"(c1), "v"(c2), "v"(c7), "v"(c8));
+#undef RW4_STAGE
+}
+// Maximum over the 16 lanes of a DPP row (lane masks 1, 2, 7, 8 span them).
+__device__ __forceinline__ float row16_max_dpp(float m) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      : "+v"(m));
+  return m;
+}
+
+// Packed word of 8 values whose group maximum is m, for the activation
+// quantizers of the lane-stage layout.  Groups whose maximum is below
+// 2^-100 are lifted by 2^64 (exact) so that 7 / m stays finite; rare, so
+// the whole wave branches around it.  7 / m is the hardware reciprocal of
+// m / 7: a few ulp from the rounded quotient, which moves v * 7 / m by
+// ~1e-6 of a code step at most.  (The reciprocal flushes subnormal
+// results, so it is taken of m / 7, whose reciprocal is normal for every
+// finite m >= 2^-100; 1 / m is not, for m above 2^126.)
+__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float flip) {
+  float mm = m;
+  if (__builtin_amdgcn_ballot_w64(m > 0.0f && m < kTinyMax) != 0) {
+    if (m > 0.0f && m < kTinyMax) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
+      mm = m * kTinyLift;
+    }
+  }
+  const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 7.0f)) : 0.0f;
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
+  return pack8_bits(b);
+}
+
 }  // namespace rw4

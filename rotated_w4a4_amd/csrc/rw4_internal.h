@@ -50,6 +50,13 @@ hipError_t launch_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const
 hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K, int group, void* out,
                              bool out_bf16, int64_t ldo, hipStream_t st);
 
+// One decode step (M <= 16, block-128 Hadamard with optional signs,
+// 128-wide groups) in one launch: every wave quantizes the activation
+// slices it consumes, then multiplies them.
+hipError_t launch_decode_fused(const void* x, bool x_bf16, int64_t ldx, const uint32_t* sign_mask, float post,
+                               const uint8_t* qw, const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                               bool y_bf16, int64_t ldy, hipStream_t st);
+
 hipError_t launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, bool y_bf16, int64_t ldy,
                        hipStream_t st);

@@ -369,3 +369,34 @@ def test_reorder_entry_points_validation():
     assert p(FAKE, 0, 128, None, None, None) == OK
     assert p(FAKE, 4, 128, FAKE, FAKE, None) == ARG   # in place
     assert p(FAKE, 4, 128, None, FAKE + 64, None) == ARG
+
+
+def test_decode_fused_validation():
+    """decode_fused: at most 16 rows, block-128 Hadamard or Givens, the
+    checks of quantize_act and w4a4_gemm, all before any device work."""
+    f = lib.rw4_decode_fused
+    assert f(None, FAKE, 1, 4, 256, FAKE, FAKE, 64, FAKE, 1, 64, None) == ARG       # no transform
+    st, h = _had(256, 128)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 7, 4, 256, FAKE, FAKE, 64, FAKE, 1, 64, None) == ARG      # unknown x dtype
+        assert f(h, FAKE, 1, 4, 256, FAKE, FAKE, 64, FAKE, 9, 64, None) == ARG      # unknown y dtype
+        assert f(h, FAKE, 1, 17, 256, FAKE, FAKE, 64, FAKE, 1, 64, None) == SHAPE   # more than 16 rows
+        assert f(h, FAKE, 1, -1, 256, FAKE, FAKE, 64, FAKE, 1, 64, None) == SHAPE
+        assert f(h, FAKE, 1, 4, 256, FAKE, FAKE, -1, FAKE, 1, 64, None) == SHAPE
+        assert f(h, None, 1, 0, 256, None, None, 64, None, 1, 64, None) == OK       # empty
+        assert f(h, None, 1, 4, 256, None, None, 0, None, 1, 0, None) == OK         # no outputs
+        assert f(h, None, 1, 4, 256, FAKE, FAKE, 64, FAKE, 1, 64, None) == ARG      # null x
+        assert f(h, FAKE, 1, 4, 256, FAKE, None, 64, FAKE, 1, 64, None) == ARG      # null scales
+        assert f(h, FAKE, 1, 4, 200, FAKE, FAKE, 64, FAKE, 1, 64, None) == ARG      # ldx < K
+        assert f(h, FAKE, 1, 4, 256, FAKE, FAKE, 64, FAKE, 1, 32, None) == ARG      # ldy < N
+        assert f(h, FAKE, 1, 4, 260, FAKE, FAKE, 64, FAKE, 1, 64, None) == ARG      # row pitch not 16-byte aligned
+        assert f(h, FAKE, 1, 4, 256, FAKE + 4, FAKE, 64, FAKE, 1, 64, None) == ARG  # misaligned weights
+    finally:
+        lib.rw4_transform_destroy(h)
+    st, h = _had(512, 256)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 1, 4, 512, FAKE, FAKE, 64, FAKE, 1, 64, None) == UNSUP    # block 256
+    finally:
+        lib.rw4_transform_destroy(h)
