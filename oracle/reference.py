@@ -46,7 +46,11 @@ reason in the design notes):
     range the packed form holds;
   * packed INT4 (the pages fix no layout): sign-magnitude nibbles, 8 codes
     per little-endian 32-bit word; nibble e (byte e // 2, low nibble for
-    even e) holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 8) in bit 3.
+    even e) holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 8) in bit 3;
+  * asymmetric (s, z) groups ([Paro] section 2.3; the [RRS] symbol table's
+    q = round(x * scale) + offset): min/max round-to-nearest with zero kept
+    inside the range, unsigned codes 0..15 with an integer zero point,
+    packed as plain nibbles (code 2b in the low nibble of byte b).
 
 Shapes: X [M, K] (tokens x input channels), W [K, N], Y = X W [M, N];
 group size g = 128, G = K / g.
@@ -60,6 +64,7 @@ import numpy as np
 GROUP = 128
 QMAX = 7      # 2^(4-1) - 1
 QMIN = -QMAX  # symmetric: max / 7 never gives -8
+UMAX = 15     # 2^4 - 1: asymmetric (affine) codes 0..15
 
 __all__ = [
     "GROUP", "QMAX", "QMIN",
@@ -68,6 +73,8 @@ __all__ = [
     "act_transform_blocks", "weight_transform_blocks",
     "transform_act", "transform_weight",
     "quantize_groups", "quantize_rrs", "rrs_channel_order", "quantize_per_channel", "permute_codes",
+    "quantize_groups_asym", "UMAX", "pack_uint4", "unpack_uint4", "dequantize_asym", "weight_code_sums",
+    "w4a4_gemm_asym",
     "pack_int4", "unpack_int4",
     "group_accumulators", "dequant_gemm",
     "round_bf16", "round_output", "dequantize", "round_dequant_output",
@@ -240,6 +247,50 @@ def quantize_groups(xt: np.ndarray, g: int = GROUP):
     return codes.reshape(R, K), scale, ratio.reshape(R, K)
 
 
+def quantize_groups_asym(xt: np.ndarray, g: int = GROUP):
+    """Per-(row, group) asymmetric (affine) INT4 with a shared (s, z) per group.
+
+    [Paro] section 2.3: each group of 128 channels shares its quantization
+    parameters (s, z); the [RRS] symbol table: q = round(x * scale) + offset,
+    scale and offset fixed by the bit width and the value range.  Reading
+    (min/max round-to-nearest, zero kept inside the range so that it is
+    represented exactly):
+
+      lo = min(0, min_k x_k),  hi = max(0, max_k x_k)
+      s  = (hi - lo) / 15
+      z  = rne(-lo / s)                      (an integer in [0, 15])
+      q  = clamp(rne(x / s) + z, 0, 15)      x_hat = s (q - z)
+
+    A group of zeros gets s = 0, z = 0 and codes 0.  Returns (codes uint8
+    [R, K], s float64 [R, G], z int64 [R, G], ratio float64 [R, K] = x / s,
+    zratio float64 [R, G] = -lo / s), the last two for recognising rounding
+    ties in the tests.
+    """
+    xt = np.asarray(xt, dtype=np.float64)
+    R, K = xt.shape
+    if K % g:
+        raise ValueError("K must be a multiple of the group size")
+    Gn = K // g
+    xg = xt.reshape(R, Gn, g)
+    lo = np.minimum(xg.min(axis=2), 0.0)
+    hi = np.maximum(xg.max(axis=2), 0.0)
+    s = (hi - lo) / UMAX
+    safe = np.where(s > 0, s, 1.0)
+    zratio = np.where(s > 0, -lo / safe, 0.0)
+    z = np.rint(zratio).astype(np.int64)
+    ratio = np.where(s[:, :, None] > 0, xg / safe[:, :, None], 0.0)
+    codes = np.clip(np.rint(ratio) + z[:, :, None], 0, UMAX)
+    codes = np.where(s[:, :, None] > 0, codes, 0).astype(np.uint8)
+    return codes.reshape(R, K), s, z, ratio.reshape(R, K), zratio
+
+
+def dequantize_asym(codes: np.ndarray, s: np.ndarray, z: np.ndarray, g: int = GROUP) -> np.ndarray:
+    """x_hat[r, k] = s[r, k // g] * (codes[r, k] - z[r, k // g]) (float64)."""
+    c = np.asarray(codes, dtype=np.float64)
+    return (c - np.repeat(np.asarray(z, dtype=np.float64), g, axis=1)) * np.repeat(
+        np.asarray(s, dtype=np.float64), g, axis=1)
+
+
 def quantize_rrs(xt: np.ndarray, g: int = GROUP, quantizer=None):
     """Rotated Runtime Smooth activation quantizer on already-rotated values.
 
@@ -348,6 +399,27 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return codes.reshape(nib.shape).astype(np.int8)
 
 
+def pack_uint4(codes: np.ndarray) -> np.ndarray:
+    """[R, K] unsigned codes 0..15 -> [R, K/2] bytes: code 2b in the low nibble
+    of byte b, code 2b + 1 in the high nibble (the asymmetric form)."""
+    c = np.asarray(codes)
+    if c.shape[-1] % 2:
+        raise ValueError("row length must be even")
+    if c.min(initial=0) < 0 or c.max(initial=0) > UMAX:
+        raise ValueError("code out of the unsigned INT4 range [0, 15]")
+    c = c.astype(np.int64)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_uint4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_uint4: uint8 codes [R, 2 * bytes]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
 # --------------------------------------------------------------------------
 # GEMM
 # --------------------------------------------------------------------------
@@ -389,6 +461,26 @@ def dequant_gemm(qa: np.ndarray, sa: np.ndarray, qw: np.ndarray, sw: np.ndarray,
         acc = qa[:, sl] @ qw[:, sl].T
         Y += (sa[:, gi][:, None] * sw[:, gi][None, :]) * acc
     return Y
+
+
+def weight_code_sums(qw_packed, g: int = GROUP) -> np.ndarray:
+    """cw[n, gamma] = sum over k in group gamma of the weight codes (int64), the
+    per-group totals an asymmetric activation's zero point multiplies."""
+    c = unpack_int4(qw_packed).astype(np.int64)
+    N, K = c.shape
+    return c.reshape(N, K // g, g).sum(axis=2)
+
+
+def w4a4_gemm_asym(qa_packed, sa, za, qw_packed, sw, out_dtype: str = "f32") -> np.ndarray:
+    """Oracle of the GEMM with asymmetric activations: the activation codes are
+    centred by their group's zero point, then the symmetric GEMM's definition:
+    Y[m, n] = sum over gamma of sa[m, gamma] * sw[n, gamma] * sum over k in gamma
+    of (qa[m, k] - za[m, gamma]) * qw[n, k], in exact integers and float64."""
+    qa = unpack_uint4(qa_packed).astype(np.int64)
+    g = qa.shape[1] // np.asarray(sa).shape[1]
+    centred = qa - np.repeat(np.asarray(za, dtype=np.int64), g, axis=1)
+    Y = dequant_gemm(centred, sa, unpack_int4(qw_packed), sw, g)
+    return round_output(Y, out_dtype)
 
 
 def round_bf16(y: np.ndarray) -> np.ndarray:
@@ -444,7 +536,9 @@ def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GRO
     """Oracle of quantize_act: transform, then per-group or RRS per-token INT4.
 
     ``g`` is the quantization group ([Paro] section 2.3 uses 128; other
-    group sizes are a knob of the same quantizer).  Mode "rrs_reorder" is
+    group sizes are a knob of the same quantizer).  Mode "group128_asym" is
+    the asymmetric (s, z) quantizer (quantize_groups_asym; the dict also
+    holds za and zratio, qa holds plain unsigned nibbles).  Mode "rrs_reorder" is
     Rotated Runtime Smooth with the channel reorder of [RRS] Figure 4 (1):
     the transformed channels are permuted by ``order`` (default: the
     rrs_channel_order of this call's activations) before grouping, and the
@@ -455,6 +549,10 @@ def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GRO
     """
     xt = transform_act(X, spec)
     m = None
+    if mode == "group128_asym":
+        codes, sa, za, ratio, zratio = quantize_groups_asym(xt, g)
+        return {"qa": pack_uint4(codes), "sa": sa, "za": za, "codes": codes, "ratio": ratio, "zratio": zratio,
+                "xt": xt, "s": None, "order": None, "m": None}
     if mode == "group128":
         codes, sa, ratio = quantize_groups(xt, g)
         s = None
