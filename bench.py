@@ -161,7 +161,7 @@ def parse():
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
                              "decode128", "decode256", "tiny", "kv", "rrs_reorder", "fused1", "fused2", "fused4",
-                             "fused8", "fused16"])
+                             "fused8", "fused16", "q_proj_asym", "down_proj_asym", "decode16_asym"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
@@ -548,6 +548,71 @@ def main_decode_fused(args, torch, rw4, gu, dev):
     print(json.dumps(out), flush=True)
 
 
+def main_asym(args, torch, rw4, gu, dev):
+    """Asymmetric (s, z) activations on a block-128 Hadamard workload: one step =
+    quantize_act_asym + w4a4_gemm_asym (weights and their code sums packed offline),
+    beside the symmetric step on the same data."""
+    base = args.workload[:-len("_asym")]
+    wl = workload(base)
+    M, K, N = wl.M, wl.K, wl.N
+    G = K // 128
+    t = rw4.Transform.hadamard(K, 128)
+    x0 = gu.x_to_device(wl.x, wl.x_dtype)
+    qw0, sw0 = rw4.pack_weight(t, torch.from_numpy(wl.w).to(dev))
+    cw0 = rw4.weight_code_sums(qw0)
+    set_bytes = M * K * 2 + M * K // 2 + 2 * M * G * 4 + N * K // 2 + 2 * N * G * 4 + M * N * 2
+    nsets = max(2, math.ceil(MALL_FLUSH_BYTES / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(x=x0.clone(), qa=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                         sa=torch.empty((M, G), dtype=torch.float32, device=dev),
+                         za=torch.empty((M, G), dtype=torch.float32, device=dev),
+                         qw=qw0.clone(), sw=sw0.clone(), cw=cw0.clone(),
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    qc = [rw4.prepare_quantize_act_asym(t, s["x"], qa=s["qa"], sa=s["sa"], za=s["za"]) for s in sets]
+    gc = [rw4.prepare_w4a4_gemm_asym(s["qa"], s["sa"], s["za"], s["qw"], s["sw"], s["cw"], out=s["y"]) for s in sets]
+    qs = [rw4.prepare_quantize_act(t, s["x"], qa=s["qa"], sa=s["sa"]) for s in sets]
+    gs = [rw4.prepare_w4a4_gemm(s["qa"], s["sa"], s["qw"], s["sw"], out=s["y"]) for s in sets]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        qc[i % nsets]()
+        gc[i % nsets]()
+
+    for i in range(args.warmup):
+        step(i)
+    r0, r1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    (q_us, _), (g_us, _) = (gpu_bound_us(torch, stream, lambda i: qc[i % nsets]()),
+                            gpu_bound_us(torch, stream, lambda i: gc[i % nsets]()))
+    (qs_us, _), (gs_us, _) = (gpu_bound_us(torch, stream, lambda i: qs[i % nsets]()),
+                              gpu_bound_us(torch, stream, lambda i: gs[i % nsets]()))
+    ops = 2.0 * M * N * K
+    qbytes = M * K * 2 + M * K // 2 + 2 * M * G * 4
+    gk = gemm_kernel_for(M, N)
+    log(f"{args.workload} M={M} K={K} N={N}: step {ms_per_step * 1e3:.1f} us; asymmetric quantize {q_us:.2f} us, "
+        f"gemm {g_us:.2f} us ({ops / g_us / 1e6:.0f} TOPS); symmetric quantize {qs_us:.2f} us, gemm {gs_us:.2f} us")
+    out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
+                      "act_mode": "group128 asymmetric (s, z)"},
+           "quantize_us": q_us, "gemm_us": g_us, "symmetric_quantize_us": qs_us, "symmetric_gemm_us": gs_us,
+           "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": gk, "avg_launch_us": g_us},
+           "quantize": {"kernel": "quant_h128_act_kernel (asymmetric)", "avg_us": q_us, "algorithmic_bytes": qbytes,
+                        "gbps": qbytes / q_us / 1e3, "frac_hbm": qbytes / q_us / 1e3 / PEAK_HBM_GBPS}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -577,6 +642,8 @@ def main():
         return main_rrs_reorder(args, torch, rw4, gu, dev)
     if args.workload.startswith("fused"):
         return main_decode_fused(args, torch, rw4, gu, dev)
+    if args.workload.endswith("_asym"):
+        return main_asym(args, torch, rw4, gu, dev)
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group

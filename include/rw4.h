@@ -203,6 +203,43 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
 rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, const void* x, rw4_dtype x_dtype,
                                    int64_t M, int64_t ldx, uint8_t* qa, float* sa, void* stream);
 
+/* ---- Asymmetric (s, z) activation groups ---------------------------------
+ * The independent-rotation article, section 2.3: a group of 128 channels
+ * shares its quantization parameters (s, z); the Rotated Runtime Smooth
+ * page's symbol table: q = round(x * scale) + offset.  Reading: min/max
+ * round-to-nearest with zero kept inside the range.  Per (row, group g) of
+ * the transformed row x~ (block-128 Hadamard only):
+ *   lo = min(0, min x~), hi = max(0, max x~), s = (hi - lo) / 15,
+ *   z = rne(-lo / s), q = clamp(rne(x~ / s) + z, 0, 15);  x~ ~ s (q - z).
+ * qa [M][K/2]: plain nibbles, code 2b in the low nibble of byte b (NOT the
+ * sign-magnitude form of rw4_quantize_act); sa [M][K/128] fp32 scales s;
+ * za [M][K/128] fp32 zero points (integers 0..15).  A group of zeros gets
+ * s = 0, z = 0 and codes 0.  Arguments and errors otherwise as
+ * rw4_quantize_act; other transforms: RW4_ERR_UNSUPPORTED. */
+rw4_status rw4_quantize_act_asym(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                                 uint8_t* qa, float* sa, float* za, void* stream);
+
+/* cw [N][K/128] fp32 = the sum of the 128 codes of each group of the packed
+ * weight rows qw [N][K/2] (rw4_pack_weight's form): what an asymmetric
+ * activation's zero point multiplies.  Offline, with the weight pack.
+ * K a multiple of 128, else RW4_ERR_SHAPE. */
+rw4_status rw4_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, void* stream);
+
+/* y [M][N] = sum over g of sa[m,g] sw[n,g] sum over k in g of
+ * (qa[m,k] - za[m,g]) qw[n,k], for the asymmetric activations above and
+ * symmetric weights (groups of 128).  Computed as the integer products
+ * minus za cw, exact, then the fp32 epilogue of rw4_w4a4_gemm; y fp32 or
+ * bf16 (round to nearest even), ld ldy >= N.  Errors as rw4_w4a4_gemm. */
+rw4_status rw4_w4a4_gemm_asym(const uint8_t* qa, const float* sa, const float* za, const uint8_t* qw,
+                              const float* sw, const float* cw, int64_t M, int64_t N, int64_t K, void* y,
+                              rw4_dtype y_dtype, int64_t ldy, void* stream);
+
+/* out [M][K] = s (q - z) from the asymmetric form (the KV-cache read-back of
+ * asymmetric groups), rounded once to fp32, then to bf16 when asked.
+ * ldo >= K elements, 16-byte aligned rows.  Errors as rw4_dequantize. */
+rw4_status rw4_dequantize_asym(const uint8_t* q, const float* s, const float* z, int64_t M, int64_t K, void* out,
+                               rw4_dtype out_dtype, int64_t ldo, void* stream);
+
 /* ---- One decode step in one launch ---------------------------------------
  * y [M, N] = w4a4_gemm(quantize_act(t, x), qw, sw) for a decode-sized step
  * (1 <= M <= 16 tokens) in one kernel launch (the independent-rotation

@@ -26,6 +26,8 @@ __all__ = [
     "dequantize", "rotate_act", "Call", "prepare_quantize_act", "prepare_w4a4_gemm", "prepare_dequantize",
     "prepare_rotate_act", "quantize_act_static", "quantize_act_rrs_reorder", "pack_weight_per_channel",
     "permute_codes", "prepare_permute_codes", "decode_fused", "prepare_decode_fused",
+    "quantize_act_asym", "prepare_quantize_act_asym", "weight_code_sums", "w4a4_gemm_asym", "prepare_w4a4_gemm_asym",
+    "dequantize_asym",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -42,7 +44,8 @@ EXPORTED_SYMBOLS = (
     "rw4_dequantize", "rw4_w4a4_gemm", "rw4_quantize_act_g", "rw4_pack_weight_g",
     "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_quantize_act_static", "rw4_status_str",
     "rw4_version", "rw4_rrs_reorder_workspace_bytes", "rw4_quantize_act_rrs_reorder", "rw4_pack_weight_per_channel",
-    "rw4_permute_codes", "rw4_decode_fused",
+    "rw4_permute_codes", "rw4_decode_fused", "rw4_quantize_act_asym", "rw4_weight_code_sums", "rw4_w4a4_gemm_asym",
+    "rw4_dequantize_asym",
 )
 
 
@@ -90,6 +93,10 @@ lib.rw4_quantize_act_rrs_reorder.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _
 lib.rw4_pack_weight_per_channel.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
 lib.rw4_permute_codes.argtypes = [_p, _i64, _i64, _p, _p, _p]
 lib.rw4_decode_fused.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, ctypes.c_int, _i64, _p]
+lib.rw4_quantize_act_asym.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
+lib.rw4_weight_code_sums.argtypes = [_p, _i64, _i64, _p, _p]
+lib.rw4_w4a4_gemm_asym.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+lib.rw4_dequantize_asym.argtypes = [_p, _p, _p, _i64, _i64, _p, ctypes.c_int, _i64, _p]
 for _name in EXPORTED_SYMBOLS:
     if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k", "rw4_rrs_reorder_workspace_bytes"):
         getattr(lib, _name).restype = ctypes.c_int
@@ -523,6 +530,101 @@ def prepare_dequantize(q, s, out_dtype=None, out=None) -> Call:
         raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
     args = (q.data_ptr(), s.data_ptr(), M, K, group, out.data_ptr(), _dtype_code(out), out.stride(0))
     return Call(lib.rw4_dequantize_g, args, dev, "rw4_dequantize", (q, s), out)
+
+
+def quantize_act_asym(t: Transform, x, qa=None, sa=None, za=None):
+    """Transform + asymmetric (s, z) INT4 in groups of 128 (block-128 Hadamard).
+
+    Returns (qa uint8 [M, K/2] plain nibbles, sa fp32 [M, K/128], za fp32 [M, K/128])."""
+    return prepare_quantize_act_asym(t, x, qa, sa, za)()
+
+
+def prepare_quantize_act_asym(t: Transform, x, qa=None, sa=None, za=None) -> Call:
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    G = K // 128
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if qa is None else qa
+    sa = torch.empty((M, G), dtype=torch.float32, device=x.device) if sa is None else sa
+    za = torch.empty((M, G), dtype=torch.float32, device=x.device) if za is None else za
+    _out("qa", qa, (M, K // 2), torch.uint8, dev)
+    _out("sa", sa, (M, G), torch.float32, dev)
+    _out("za", za, (M, G), torch.float32, dev)
+    args = (t.handle, x.data_ptr(), _dtype_code(x), M, x.stride(0), qa.data_ptr(), sa.data_ptr(), za.data_ptr())
+    return Call(lib.rw4_quantize_act_asym, args, dev, "rw4_quantize_act_asym", (t, x), (qa, sa, za))
+
+
+def weight_code_sums(qw, cw=None):
+    """cw fp32 [N, K/128]: the sum of every 128-group of codes of the packed weights qw."""
+    torch = _torch()
+    N, Kh = qw.shape
+    K = Kh * 2
+    dev = _on_gpu("qw", qw)
+    if qw.dtype != torch.uint8 or not qw.is_contiguous():
+        raise ValueError("qw must be a contiguous uint8 tensor")
+    cw = torch.empty((N, K // 128), dtype=torch.float32, device=qw.device) if cw is None else cw
+    _out("cw", cw, (N, K // 128), torch.float32, dev)
+    return Call(lib.rw4_weight_code_sums, (qw.data_ptr(), N, K, cw.data_ptr()), dev, "rw4_weight_code_sums",
+                (qw,), cw)()
+
+
+def w4a4_gemm_asym(qa, sa, za, qw, sw, cw, out_dtype=None, out=None):
+    """Y [M, N] from asymmetric activations (qa, sa, za) and weights (qw, sw) with their code sums cw."""
+    return prepare_w4a4_gemm_asym(qa, sa, za, qw, sw, cw, out_dtype, out)()
+
+
+def prepare_w4a4_gemm_asym(qa, sa, za, qw, sw, cw, out_dtype=None, out=None) -> Call:
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    M, Kh = qa.shape
+    N = qw.shape[0]
+    K = Kh * 2
+    G = K // 128
+    if K % 128 or qw.shape[1] != Kh or sa.shape != (M, G) or za.shape != (M, G) or sw.shape != (N, G) \
+            or cw.shape != (N, G):
+        raise ValueError("operand shapes do not match (groups of 128)")
+    dev = _on_gpu("qa", qa)
+    u8, f32 = torch.uint8, torch.float32
+    for name, tns, dt in (("qa", qa, u8), ("sa", sa, f32), ("za", za, f32), ("qw", qw, u8), ("sw", sw, f32),
+                          ("cw", cw, f32)):
+        _on_gpu(name, tns, dev)
+        if tns.dtype != dt or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
+    args = (qa.data_ptr(), sa.data_ptr(), za.data_ptr(), qw.data_ptr(), sw.data_ptr(), cw.data_ptr(), M, N, K,
+            out.data_ptr(), _dtype_code(out), out.stride(0))
+    return Call(lib.rw4_w4a4_gemm_asym, args, dev, "rw4_w4a4_gemm_asym", (qa, sa, za, qw, sw, cw), out)
+
+
+def dequantize_asym(q, s, z, out_dtype=None, out=None):
+    """x_hat [M, K] = s * (q - z) from the asymmetric form (groups of 128), fp32 or bf16."""
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    M, Kh = q.shape
+    K = Kh * 2
+    if K % 128 or s.shape != (M, K // 128) or z.shape != (M, K // 128):
+        raise ValueError("scale / zero-point shapes do not match the codes")
+    dev = _on_gpu("q", q)
+    for name, tns, dt in (("q", q, torch.uint8), ("s", s, torch.float32), ("z", z, torch.float32)):
+        _on_gpu(name, tns, dev)
+        if tns.dtype != dt or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    out = torch.empty((M, K), dtype=out_dtype, device=q.device) if out is None else out
+    _on_gpu("out", out, dev)
+    if out.dim() != 2 or out.shape != (M, K) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
+    args = (q.data_ptr(), s.data_ptr(), z.data_ptr(), M, K, out.data_ptr(), _dtype_code(out), out.stride(0))
+    return Call(lib.rw4_dequantize_asym, args, dev, "rw4_dequantize_asym", (q, s, z), out)()
 
 
 def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):

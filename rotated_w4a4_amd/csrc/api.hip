@@ -348,6 +348,59 @@ rw4_status rw4_quantize_act(const rw4_transform* t, rw4_act_mode mode, const voi
   return rw4_quantize_act_g(t, mode, 128, x, x_dtype, M, ldx, qa, sa, workspace, stream);
 }
 
+rw4_status rw4_quantize_act_asym(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                                 uint8_t* qa, float* sa, float* za, void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0) return RW4_ERR_SHAPE;
+  if (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128) return RW4_ERR_UNSUPPORTED;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (M == 0) return RW4_OK;
+  if (!x || !qa || !sa || !za) return RW4_ERR_ARG;
+  const int64_t K = t->dev.K;
+  if (ldx < K) return RW4_ERR_ARG;
+  const int64_t esz = x_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * esz) % 16 || !aligned16(qa) || !aligned16(sa) || !aligned16(za)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_quantize_act_asym(t->dev, x, x_dtype == RW4_BF16, M, ldx, qa, sa, za, st));
+}
+
+rw4_status rw4_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, void* stream) {
+  if (N < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
+  if (N == 0) return RW4_OK;
+  if (!qw || !cw) return RW4_ERR_ARG;
+  if (!aligned16(qw) || !aligned16(cw)) return RW4_ERR_ARG;
+  return from_hip(rw4::launch_weight_code_sums(qw, N, K, cw, static_cast<hipStream_t>(stream)));
+}
+
+rw4_status rw4_w4a4_gemm_asym(const uint8_t* qa, const float* sa, const float* za, const uint8_t* qw,
+                              const float* sw, const float* cw, int64_t M, int64_t N, int64_t K, void* y,
+                              rw4_dtype y_dtype, int64_t ldy, void* stream) {
+  if (y_dtype != RW4_F32 && y_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
+  if (M == 0 || N == 0) return RW4_OK;
+  if (!qa || !sa || !za || !qw || !sw || !cw || !y) return RW4_ERR_ARG;
+  if (ldy < N) return RW4_ERR_ARG;
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(sa) || !aligned16(sw) || !aligned16(za) || !aligned16(cw) ||
+      !aligned16(y))
+    return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_gemm_asym(qa, sa, za, qw, sw, cw, M, N, K, y, y_dtype == RW4_BF16, ldy, st));
+}
+
+rw4_status rw4_dequantize_asym(const uint8_t* q, const float* s, const float* z, int64_t M, int64_t K, void* out,
+                               rw4_dtype out_dtype, int64_t ldo, void* stream) {
+  if (out_dtype != RW4_F32 && out_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || K <= 0 || K % kGroup) return RW4_ERR_SHAPE;
+  if (M == 0) return RW4_OK;
+  if (!q || !s || !z || !out) return RW4_ERR_ARG;
+  if (ldo < K) return RW4_ERR_ARG;
+  const int64_t esz = out_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(z) || !aligned16(out) || (ldo * esz) % 16) return RW4_ERR_ARG;
+  return from_hip(rw4::launch_dequantize_asym(q, s, z, M, K, out, out_dtype == RW4_BF16, ldo,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 rw4_status rw4_rotate_act(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
                           void* out, rw4_dtype out_dtype, int64_t ldo, void* stream) {
   if (!t) return RW4_ERR_ARG;

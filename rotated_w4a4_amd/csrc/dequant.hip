@@ -85,4 +85,86 @@ hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Asymmetric codes (plain nibbles, groups of 128): x_hat = s (q - z), with
+// q - z an exact small integer, so the product is rounded once to fp32 (then
+// to bf16 when asked).  One lane per stored word, as dequant_kernel.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_asym_kernel(const uint8_t* __restrict__ q,
+                                                           const float* __restrict__ s,
+                                                           const float* __restrict__ z, int64_t row0, int64_t K,
+                                                           void* __restrict__ out, int64_t ldo) {
+  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= K / 8) return;
+  const int64_t row = row0 + blockIdx.y;
+  const uint32_t w = reinterpret_cast<const uint32_t*>(q + row * (K / 2))[j];
+  const int64_t gi = row * (K / kGroup) + (j * 8) / kGroup;
+  const float sc = s[gi], zp = z[gi];
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float((w >> (4 * e)) & 15u) - zp) * sc;
+  if constexpr (BF16) {
+    __bf16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<__bf16>(v[i]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(out) + row * ldo + j * 8) =
+        *reinterpret_cast<const uint4*>(h);
+  } else {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * ldo + j * 8);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+hipError_t launch_dequantize_asym(const uint8_t* q, const float* s, const float* z, int64_t M, int64_t K, void* out,
+                                  bool out_bf16, int64_t ldo, hipStream_t st) {
+  const int64_t words = K / 8;
+  const int bd = words >= 256 ? 256 : int((words + 63) / 64 * 64);
+  const int64_t bx = (words + bd - 1) / bd;
+  if (bx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  constexpr int64_t kMaxRows = 65535;
+  for (int64_t r0 = 0; r0 < M; r0 += kMaxRows) {
+    const int64_t rows = M - r0 < kMaxRows ? M - r0 : kMaxRows;
+    const dim3 grid{unsigned(bx), unsigned(rows), 1u};
+    if (out_bf16)
+      hipLaunchKernelGGL((dequant_asym_kernel<true>), grid, dim3(bd), 0, st, q, s, z, r0, K, out, ldo);
+    else
+      hipLaunchKernelGGL((dequant_asym_kernel<false>), grid, dim3(bd), 0, st, q, s, z, r0, K, out, ldo);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Code sums of packed (sign-magnitude) weight rows per 128-group: the totals
+// an asymmetric activation's zero point multiplies.  One lane per (row,
+// group); offline, with the weight pack.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __restrict__ qw, int64_t N, int64_t G,
+                                                               float* __restrict__ cw) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= N * G) return;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(qw + i * 64);  // row n = i / G, group i % G
+  int sum = 0;
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t ev = w[k] & 0x87878787u, od = __builtin_amdgcn_alignbit(w[k], w[k], 4) & 0x87878787u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t e = (ev >> (8 * b)) & 0xFFu, o = (od >> (8 * b)) & 0xFFu;
+      sum += (e & 0x80u ? -int(e & 7u) : int(e & 7u)) + (o & 0x80u ? -int(o & 7u) : int(o & 7u));
+    }
+  }
+  cw[i] = float(sum);
+}
+
+hipError_t launch_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, hipStream_t st) {
+  const int64_t n = N * (K / kGroup);
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(weight_code_sums_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, qw, N, K / kGroup, cw);
+  return hipGetLastError();
+}
+
 }  // namespace rw4

@@ -62,6 +62,16 @@ __device__ __forceinline__ v8i f8_operand(v4u w) {
              int(f8_even(w[2])), int(f8_odd(w[2])), int(f8_even(w[3])), int(f8_odd(w[3]))};
 }
 
+// 4 words of plain unsigned nibbles (asymmetric codes 0..15) -> the FP8
+// operand in the same code order as f8_operand.  The E4M3 byte of u * 2^-9
+// is u itself for every u in 0..15 (subnormals 0..7, exponent field 1 for
+// 8..15), so the bytes are the nibbles.
+__device__ __forceinline__ v8i f8u_operand(v4u w) {
+  return v8i{int(w[0] & 0x0F0F0F0Fu), int((w[0] >> 4) & 0x0F0F0F0Fu), int(w[1] & 0x0F0F0F0Fu),
+             int((w[1] >> 4) & 0x0F0F0F0Fu), int(w[2] & 0x0F0F0F0Fu), int((w[2] >> 4) & 0x0F0F0F0Fu),
+             int(w[3] & 0x0F0F0F0Fu), int((w[3] >> 4) & 0x0F0F0F0Fu)};
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -568,13 +578,20 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 constexpr int kStageTileBytes = 2 * kGroupBytes;        // A and B tiles of two groups
 constexpr int kStageSplitBytes = 2 * kSplitGroupBytes;  // their split scale operands
 
-template <bool BF16>
+// ASYM: plain-nibble activation codes with zero points za [M][G] and the
+// weight code sums cw [N][G]: every group's accumulators start at
+// -za cw (exact integers, from a bf16 MFMA on the spare K slots 6 and 7 of
+// the split scale operands: -za twice against cw split into two bf16
+// parts), then the integer products add to them.
+template <bool BF16, bool ASYM = false>
 __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restrict__ qa,
                                                           const float* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw,
                                                           const float* __restrict__ sw, int64_t M,
                                                           int64_t N, int64_t K, void* __restrict__ y,
-                                                          int64_t ldy, int64_t tiles_m) {
+                                                          int64_t ldy, int64_t tiles_m,
+                                                          const float* __restrict__ za = nullptr,
+                                                          const float* __restrict__ cw = nullptr) {
   __shared__ __align__(16) uint8_t tA[kStageTileBytes];
   __shared__ __align__(16) uint8_t tB[kStageTileBytes];
   __shared__ __align__(16) uint8_t sA[kStageSplitBytes];
@@ -627,10 +644,30 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     return __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rs, int(sc_off), int((g < G ? g : G - 1) * 4), 0));
   };
+  // ASYM: the zero point (rows) or weight code sum (columns) of the same
+  // row or column
+  const __amdgpu_buffer_rsrc_t rz =
+      row_scale ? make_rsrc(za + m0 * G, ASYM ? rows_a * G * 4 : 0) : make_rsrc(cw + n0 * G, ASYM ? rows_b * G * 4 : 0);
+  auto z_load = [&](int64_t g) {
+    if constexpr (!ASYM) return 0.0f;
+    return __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rz, int(sc_off), int((g < G ? g : G - 1) * 4), 0));
+  };
   const SplitSel sel = split_selectors(row_scale);
-  auto put_split = [&](uint8_t* S, int q, float x) {
+  auto put_split = [&](uint8_t* S, int q, float x, float zx) {
     const uint4 o = split_operand(x, sel);
-    *reinterpret_cast<v4u*>(S + q * kSplitGroupBytes + tid * 16) = v4u{o.x, o.y, o.z, o.w};
+    uint32_t w = 0;
+    if constexpr (ASYM) {
+      // slots 6, 7: rows (-za, -za), columns (cw rounded toward zero to bf16, the exact rest)
+      if (row_scale) {
+        const uint32_t nz = __float_as_uint(-zx) >> 16;  // small integers: exact in bf16
+        w = nz | (nz << 16);
+      } else {
+        const uint32_t hi = __float_as_uint(zx) & 0xFFFF0000u;
+        w = (hi >> 16) | (__float_as_uint(zx - __uint_as_float(hi)) & 0xFFFF0000u);
+      }
+    }
+    *reinterpret_cast<v4u*>(S + q * kSplitGroupBytes + tid * 16) = v4u{o.x, o.y, o.z, w};
   };
 
   // byte offsets of this lane's fragments inside a group slot (as the read
@@ -677,7 +714,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
   auto mfma_half = [&](const v4u (&f)[4], bool init) {
     v8i oa[2], ob[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) oa[i] = f8_operand(f[i]);
+    for (int i = 0; i < 2; ++i) oa[i] = ASYM ? f8u_operand(f[i]) : f8_operand(f[i]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) ob[j] = f8_operand(f[2 + j]);
 #pragma unroll
@@ -688,11 +725,25 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
                                                                    0, kE8Scale, 0, kE8Scale);
   };
   // scale products of the four 32 x 32 tiles (bf16 MFMA on the splits), then y += acc * p
+  // ASYM: the accumulators of a group start at -za cw (K slots 6 and 7 only)
+  auto init_acc = [&](const v4u (&ps)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, v4u{0u, 0u, 0u, ps[i][3] & keep}),
+                                                           __builtin_bit_cast(v8bf, v4u{0u, 0u, 0u, ps[2 + j][3]}),
+                                                           v16f{}, 0, 0, 0);
+  };
   auto epilogue = [&](v4u (&ps)[4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
+    if constexpr (ASYM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[i][3] = 0u;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const v16f p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ps[t >> 1]),
@@ -715,9 +766,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
   issue(tA, 0, 0);
   issue(tA, 1, 1);
   {
-    const float x0 = sc_load(0), x1 = sc_load(1);
-    put_split(sA, 0, x0);
-    put_split(sA, 1, x1);
+    const float x0 = sc_load(0), x1 = sc_load(1), z0 = z_load(0), z1 = z_load(1);
+    put_split(sA, 0, x0, z0);
+    put_split(sA, 1, x1, z1);
   }
   const int64_t S = (G + 1) / 2;
   // Wave priority alternates stage by stage, opposite for odd and even
@@ -736,13 +787,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
       __builtin_amdgcn_s_setprio(0);
     wait_vm_barrier<0>();
     const float x0 = sc_load(2 * s + 2), x1 = sc_load(2 * s + 3);
+    const float z0 = z_load(2 * s + 2), z1 = z_load(2 * s + 3);
     issue(Tn, 0, 2 * s + 2);
     issue(Tn, 1, 2 * s + 3);
     v4u f0[4], f1[4], ps[4];
     read_half(Tc, 0, oa0, ob0, f0);
     read_half(Tc, 0, oa1, ob1, f1);
     read_splits(Sc, 0, ps);
-    mfma_half(f0, true);
+    if constexpr (ASYM) init_acc(ps);
+    mfma_half(f0, !ASYM);
     const bool two = 2 * s + 1 < G;
     if (two) read_half(Tc, 1, oa0, ob0, f0);
     mfma_half(f1, false);
@@ -750,12 +803,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     if (two) {
       read_half(Tc, 1, oa1, ob1, f1);
       read_splits(Sc, 1, ps);
-      mfma_half(f0, true);
+      if constexpr (ASYM) init_acc(ps);
+      mfma_half(f0, !ASYM);
       mfma_half(f1, false);
       epilogue(ps);
     }
-    put_split(Sn, 0, x0);
-    put_split(Sn, 1, x1);
+    put_split(Sn, 0, x0, z0);
+    put_split(Sn, 1, x1, z1);
   };
   for (int64_t s = 0; s < S; s += 2) {
     stage(tA, sA, tB, sB, s);
@@ -865,27 +919,37 @@ struct SmallCfg {
   static_assert(CT * MT <= kSmallWaves, "one wave per output tile in the epilogue");
 };
 
-template <int GSZ, int MT, int CT>
+template <int GSZ, int MT, int CT, bool ASYM = false>
 struct SmallStage {
   using C = SmallCfg<GSZ, MT, CT>;
   float sa[C::SAR], sw[C::SWR];
+  float za[ASYM ? C::SAR : 1], cw[ASYM ? C::SWR : 1];  // ASYM: zero points and weight code sums
   v4u a[C::AR];
   v4u b[CT][C::NS];
 };
 
-template <bool BF16, int GSZ, int MT, int CT>
+// ASYM (GSZ = 128): plain-nibble activation codes with zero points za and
+// weight code sums cw, staged like sa and sw; each product starts at
+// -za cw.
+template <bool BF16, int GSZ, int MT, int CT, bool ASYM = false>
 __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t* __restrict__ qa,
                                                                    const float* __restrict__ sa,
                                                                    const uint8_t* __restrict__ qw,
                                                                    const float* __restrict__ sw, int64_t M,
                                                                    int64_t N, int64_t K, void* __restrict__ y,
-                                                                   int64_t ldy) {
+                                                                   int64_t ldy, const float* __restrict__ za = nullptr,
+                                                                   const float* __restrict__ cw = nullptr) {
   using C = SmallCfg<GSZ, MT, CT>;
-  using Stage = SmallStage<GSZ, MT, CT>;
-  __shared__ __align__(16) uint8_t lds[C::BYTES];
+  using Stage = SmallStage<GSZ, MT, CT, ASYM>;
+  static_assert(!ASYM || GSZ == 128, "asymmetric groups of 128");
+  constexpr int ZA_OFF = C::BYTES, CW_OFF = ZA_OFF + C::SAR * kSmallThreads * 4;
+  constexpr int LDS_BYTES = ASYM ? CW_OFF + C::SWR * kSmallThreads * 4 : C::BYTES;
+  __shared__ __align__(16) uint8_t lds[LDS_BYTES];
   v4u* const As = reinterpret_cast<v4u*>(lds);
   float* const saT = reinterpret_cast<float*>(lds + C::SA_OFF);
   float* const swT = reinterpret_cast<float*>(lds + C::SW_OFF);
+  float* const zaT = reinterpret_cast<float*>(lds + ZA_OFF);
+  float* const cwT = reinterpret_cast<float*>(lds + CW_OFF);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -904,6 +968,8 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + m0 * GS, mrows * GS * 4);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + n0 * rowbytes, nrows * rowbytes);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw + n0 * GS, nrows * GS * 4);
+  const __amdgpu_buffer_rsrc_t rza = make_rsrc(za + m0 * GS, ASYM ? mrows * GS * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rcw = make_rsrc(cw + n0 * GS, ASYM ? nrows * GS * 4 : 0);
 
   // staged A chunk j of this thread: row, chunk within the row slice
   auto a_row = [&](int j) { return (j * kSmallThreads + tid) / C::AROW; };
@@ -920,6 +986,9 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
       const bool ok = idx < C::SAE && col < GS;
       S.sa[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rsa, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
+      if constexpr (ASYM)
+        S.za[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rza, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
     }
 #pragma unroll
     for (int j = 0; j < C::SWR; ++j) {
@@ -928,6 +997,9 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
       const bool ok = idx < C::SWE && col < GS;
       S.sw[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rsw, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
+      if constexpr (ASYM)
+        S.cw[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rcw, int(ok ? uint32_t(((idx / C::CW) * GS + col) * 4) : kNoRead), 0, 0));
     }
 #pragma unroll
     for (int j = 0; j < C::AR; ++j) {
@@ -951,11 +1023,13 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
     for (int j = 0; j < C::SAR; ++j) {
       const int idx = j * kSmallThreads + tid;
       saT[idx < C::SAE ? (idx % C::CW) * (16 * MT) + idx / C::CW : idx] = S.sa[j];
+      if constexpr (ASYM) zaT[idx < C::SAE ? (idx % C::CW) * (16 * MT) + idx / C::CW : idx] = S.za[j];
     }
 #pragma unroll
     for (int j = 0; j < C::SWR; ++j) {
       const int idx = j * kSmallThreads + tid;
       swT[idx < C::SWE ? (idx % C::CW) * (16 * CT) + idx / C::CW : idx] = S.sw[j];
+      if constexpr (ASYM) cwT[idx < C::SWE ? (idx % C::CW) * (16 * CT) + idx / C::CW : idx] = S.cw[j];
     }
 #pragma unroll
     for (int j = 0; j < C::AR; ++j) As[a_row(j) * (C::AROW + 1) + a_chunk(j)] = S.a[j];
@@ -976,7 +1050,17 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
 #pragma unroll
     for (int r = 0; r < 4; ++r) yv[ct][mt][r] = fmaf(acc[r], s4[r] * swv, yv[ct][mt][r]);
   };
-  auto a_frag = [&](int mt, int gl) { return f8_operand(As[(mt * 16 + am) * (C::AROW + 1) + gl * 4 + part]); };
+  auto a_frag = [&](int mt, int gl) {
+    const v4u w = As[(mt * 16 + am) * (C::AROW + 1) + gl * 4 + part];
+    return ASYM ? f8u_operand(w) : f8_operand(w);
+  };
+  // ASYM: the product of tile (ct, mt) in scale column cl starts at -za cw
+  auto acc_init = [&](int ct, int mt, int cl) {
+    if constexpr (!ASYM) return v4f{};
+    const v4f z4 = *reinterpret_cast<const v4f*>(zaT + cl * (16 * MT) + mt * 16 + part * 4);
+    const float c = cwT[cl * (16 * CT) + ct * 16 + am];
+    return v4f{-z4[0] * c, -z4[1] * c, -z4[2] * c, -z4[3] * c};
+  };
   auto compute = [&](const Stage& S) {
 #pragma unroll
     for (int ns = 0; ns < C::NS; ns += C::P) {
@@ -1006,8 +1090,8 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
           for (int p = 0; p < C::P; ++p) a[p] = a_frag(mt, gl + p);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
-            v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0][ct], v4f{}, 0, 0, 0, kE8Scale, 0,
-                                                                       kE8Scale);
+            v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0][ct], acc_init(ct, mt, gl / C::P),
+                                                                       0, 0, 0, kE8Scale, 0, kE8Scale);
             if constexpr (C::P == 2)
               acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], b[1][ct], acc, 0, 0, 0, kE8Scale, 0,
                                                                      kE8Scale);
@@ -1386,6 +1470,43 @@ hipError_t launch_gemm_g(const uint8_t* qa, const float* sa, const uint8_t* qw, 
   else
     hipLaunchKernelGGL((gemm_f8_kernel<false, GSZ>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N,
                        K, y, ldy, tiles_m);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_asym(const uint8_t* qa, const float* sa, const float* za, const uint8_t* qw, const float* sw,
+                            const float* cw, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
+                            hipStream_t st) {
+  if (use_small_kernel(M, N)) {
+    auto run = [&](auto mt_const, auto ct_const) {
+      constexpr int MT = decltype(mt_const)::value, CT = decltype(ct_const)::value;
+      const int64_t blocks = (N + 16 * CT - 1) / (16 * CT);
+      const int64_t chunks = (M + 16 * MT - 1) / (16 * MT);
+      if (blocks > 0x7FFFFFFF || chunks > 65535) return hipErrorInvalidValue;
+      const dim3 grid{unsigned(blocks), unsigned(chunks), 1u};
+      if (y_bf16)
+        hipLaunchKernelGGL((gemm_small_kernel<true, 128, MT, CT, true>), grid, dim3(kSmallThreads), 0, st, qa, sa,
+                           qw, sw, M, N, K, y, ldy, za, cw);
+      else
+        hipLaunchKernelGGL((gemm_small_kernel<false, 128, MT, CT, true>), grid, dim3(kSmallThreads), 0, st, qa, sa,
+                           qw, sw, M, N, K, y, ldy, za, cw);
+      return hipGetLastError();
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (M <= 16) return N > 12288 ? run(I1{}, I2{}) : run(I1{}, I1{});
+    if (M <= 32) return run(I2{}, I1{});
+    return run(std::integral_constant<int, 4>{}, I1{});
+  }
+  if (K > (int64_t(1) << 24)) return hipErrorInvalidValue;
+  const int64_t tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (y_bf16)
+    hipLaunchKernelGGL((gemm_f8p_kernel<true, true>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N, K, y, ldy,
+                       tiles_m, za, cw);
+  else
+    hipLaunchKernelGGL((gemm_f8p_kernel<false, true>), dim3(blocks), dim3(256), 0, st, qa, sa, qw, sw, M, N, K, y,
+                       ldy, tiles_m, za, cw);
   return hipGetLastError();
 }
 

@@ -168,12 +168,15 @@ struct RawRow {
 // stays 128: a 64-group is one 8-lane half of a DPP row (lane l holds
 // Sylvester lane f(l), and f keeps lane bit 3), a 256-group two adjacent
 // rows (lanes l and l ^ 16).
-template <bool BF16, bool SIGNED, int D, int GS>
+// ASYM (GS = 128 only): the asymmetric (s, z) encoder (encode8_asym) with
+// plain nibbles; zs receives the zero points as floats.
+template <bool BF16, bool SIGNED, int D, int GS, bool ASYM = false>
 __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                              int64_t rows, int64_t G, int64_t Q, int64_t R,
                                                              const uint32_t* __restrict__ sign_mask,
                                                              uint8_t* __restrict__ q, float* __restrict__ s,
-                                                             float post_scale) {
+                                                             float post_scale, float* __restrict__ zs = nullptr) {
+  static_assert(!ASYM || GS == 128, "asymmetric groups of 128");
   constexpr int ES = BF16 ? 2 : 4;  // bytes per input element
   const int lane = threadIdx.x & 63;
   // wave index (4 waves per block), Q * R below 2^31 (checked on the host):
@@ -253,6 +256,29 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
       raw[d] = load(row + D * R);
       fwht8(v);
       lane_stages_dpp(v, c1, c2, c7, c8);
+      if constexpr (ASYM) {
+        // true signs (the lane stages leave every value times flip), then
+        // the group's range with zero inside it
+        float hi = 0.0f, nlo = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] *= flip;
+          hi = fmaxf(hi, v[e]);
+          nlo = fmaxf(nlo, -v[e]);
+        }
+        hi = row16_max_dpp(hi);
+        nlo = row16_max_dpp(nlo);
+        uint32_t z;
+        const uint32_t packed = encode8_asym(v, hi, nlo, z);
+        const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, live ? G * 4 : 0);
+        const __amdgpu_buffer_rsrc_t rz = buf_rsrc(zs + row * G, live ? G * 4 : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((hi + nlo) * post_scale), rs, int(s_off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(float(z)), rz, int(s_off), 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
@@ -1156,6 +1182,31 @@ hipError_t launch_h128_act(const void* x, bool bf16, int64_t ldx, const uint32_t
   return hipGetLastError();
 }
 
+// The asymmetric form of launch_h128_act (groups of 128): codes, scales
+// (range / 15 of the normalized transform) and zero points.
+hipError_t launch_h128_act_asym(const void* x, bool bf16, int64_t ldx, const uint32_t* sign_mask, int64_t rows,
+                                int64_t G, uint8_t* q, float* s, float* z, hipStream_t st) {
+  constexpr int D = 1, GS = 128;
+  constexpr int64_t kResidentWaves = 256 * 32;
+  const int64_t Q = (G + 3) / 4;
+  const int64_t rows_per_wave = Q * rows <= kResidentWaves ? 1 : Q * rows <= 2 * kResidentWaves ? 2 : 3;
+  int64_t R = (rows + rows_per_wave - 1) / rows_per_wave;
+  if (R < 1) R = 1;
+  const int64_t blocks = (Q * R + 3) / 4;
+  if (Q * R > 0x7FFFFFFF - 3 || G * 64 * (bf16 ? 4 : 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const float post = (1.0f / 15.0f) / sqrtf(128.0f);
+#define RW4_H128_ASYM(B, S)                                                                                   \
+  hipLaunchKernelGGL((quant_h128_act_kernel<B, S, D, GS, true>), dim3(blocks), dim3(256), 0, st, x, ldx, rows, G, \
+                     Q, R, sign_mask, q, s, post, z)
+  if (bf16) {
+    if (sign_mask) RW4_H128_ASYM(true, true); else RW4_H128_ASYM(true, false);
+  } else {
+    if (sign_mask) RW4_H128_ASYM(false, true); else RW4_H128_ASYM(false, false);
+  }
+#undef RW4_H128_ASYM
+  return hipGetLastError();
+}
+
 // Rotated Runtime Smooth over whole rows of K = 512 NC channels.
 template <int NC>
 hipError_t launch_rrs_full(const void* x, bool bf16, int64_t ldx, int64_t rows, uint8_t* q, float* s,
@@ -1407,6 +1458,12 @@ bool rowh_supported(int64_t K) {
 // Activations: X [M, K] row-major.
 // group: 64, 128 or 256 for the block-128 Hadamard in per-group mode, else
 // 128 (the caller checks).
+hipError_t launch_quantize_act_asym(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
+                                    uint8_t* q, float* s, float* z, hipStream_t st) {
+  if (t.kind != TransformKind::Hadamard || t.block != kGroup) return hipErrorInvalidValue;
+  return launch_h128_act_asym(x, bf16, ldx, t.sign_mask, M, t.K / kGroup, q, s, z, st);
+}
+
 hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, bool bf16, int64_t M,
                                int64_t ldx, uint8_t* q, float* s, float* smooth, int group, hipStream_t st) {
   const int64_t K = t.K, G = K / kGroup;

@@ -327,4 +327,38 @@ __device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float fl
   return pack8_bits(b);
 }
 
+// ---------------------------------------------------------------------------
+// Asymmetric (s, z) encoder: 8 values t (true signs) of a group whose range,
+// with zero kept inside it, is [-nlo, hi] (hi, nlo >= 0, reduced over the
+// group).  With d = hi + nlo: z = rne(15 nlo / d) and code
+// clamp(rne(15 t / d) + z, 0, 15), packed as plain nibbles (code e in
+// nibble e).  15 / d is the hardware reciprocal of d / 15; groups with
+// 0 < d < 2^-100 are lifted by 2^64 (exact) as in encode8_rcp; d = 0 gives
+// z = 0 and codes 0.  Returns the word; z in z_out.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float nlo, uint32_t& z_out) {
+  float d = hi + nlo, nl = nlo;
+  if (__builtin_amdgcn_ballot_w64(d > 0.0f && d < kTinyMax) != 0) {
+    if (d > 0.0f && d < kTinyMax) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] *= kTinyLift;
+      d *= kTinyLift;
+      nl *= kTinyLift;
+    }
+  }
+  const float inv = d > 0.0f ? __builtin_amdgcn_rcpf(d * (1.0f / 15.0f)) : 0.0f;
+  const uint32_t z = rne_code_bits(nl, inv) - kRoundMagicBits;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int e = 7; e >= 0; --e) {
+    // rne(t inv) + z, clamped to [0, 15], in the magic-constant domain
+    uint32_t b = rne_code_bits(t[e], inv) + z;
+    b = b < kRoundMagicBits ? kRoundMagicBits : b;
+    b = b > kRoundMagicBits + 15u ? kRoundMagicBits + 15u : b;
+    acc = (acc << 4) + (b - kRoundMagicBits);
+  }
+  z_out = z;
+  return acc;
+}
+
 }  // namespace rw4

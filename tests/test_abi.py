@@ -400,3 +400,40 @@ def test_decode_fused_validation():
         assert f(h, FAKE, 1, 4, 512, FAKE, FAKE, 64, FAKE, 1, 64, None) == UNSUP    # block 256
     finally:
         lib.rw4_transform_destroy(h)
+
+
+def test_asym_entry_points_validation():
+    """The asymmetric calls: block-128 Hadamard only, groups of 128, null and alignment checks."""
+    f = lib.rw4_quantize_act_asym
+    assert f(None, FAKE, 1, 4, 256, FAKE, FAKE, FAKE, None) == ARG          # no transform
+    st, h = _had(256, 128)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 7, 4, 256, FAKE, FAKE, FAKE, None) == ARG         # unknown dtype
+        assert f(h, FAKE, 1, -1, 256, FAKE, FAKE, FAKE, None) == SHAPE
+        assert f(h, None, 1, 0, 256, None, None, None, None) == OK          # empty
+        assert f(h, FAKE, 1, 4, 256, FAKE, FAKE, None, None) == ARG         # no zero points
+        assert f(h, FAKE, 1, 4, 200, FAKE, FAKE, FAKE, None) == ARG         # ldx < K
+        assert f(h, FAKE, 1, 4, 256, FAKE, FAKE, FAKE + 4, None) == ARG     # misaligned za
+    finally:
+        lib.rw4_transform_destroy(h)
+    st, h = _had(512, 512)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 1, 4, 512, FAKE, FAKE, FAKE, None) == UNSUP       # block 512
+    finally:
+        lib.rw4_transform_destroy(h)
+    c = lib.rw4_weight_code_sums
+    assert c(FAKE, 4, 100, FAKE, None) == SHAPE
+    assert c(FAKE, 0, 128, None, None) == OK
+    assert c(None, 4, 128, FAKE, None) == ARG
+    g = lib.rw4_w4a4_gemm_asym
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 200, FAKE, 1, 4, None) == SHAPE    # K % 128
+    assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 4, 256, FAKE, 1, 4, None) == ARG     # no za
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 256, FAKE, 1, 4, None) == ARG     # no cw
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 256, FAKE, 9, 4, None) == ARG     # bad dtype
+    assert g(None, None, None, None, None, None, 0, 4, 256, None, 1, 4, None) == OK      # empty
+    d = lib.rw4_dequantize_asym
+    assert d(FAKE, FAKE, FAKE, 4, 200, FAKE, 1, 256, None) == SHAPE
+    assert d(FAKE, FAKE, None, 4, 256, FAKE, 1, 256, None) == ARG
+    assert d(FAKE, FAKE, FAKE, 4, 256, FAKE, 1, 100, None) == ARG                        # ldo < K
