@@ -47,6 +47,13 @@ reason in the design notes):
   * packed INT4 (the pages fix no layout): sign-magnitude nibbles, 8 codes
     per little-endian 32-bit word; nibble e (byte e // 2, low nibble for
     even e) holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 8) in bit 3;
+  * 8-bit groups for extreme outliers ([Paro] section 4.1, mixed
+    precision): the caller names the 128-channel groups; their codes are
+    symmetric with 225 levels, q8 in [-112, 112] (scale max / 112), split
+    exactly as q8 = 15 h + l with h, l in [-7, 7], two INT4 planes: h in
+    place of the group (scale 15 s8), l in an extra group appended after
+    the K channels (scale s8), against a weight matrix whose named groups
+    are appended again;
   * asymmetric (s, z) groups ([Paro] section 2.3; the [RRS] symbol table's
     q = round(x * scale) + offset): min/max round-to-nearest with zero kept
     inside the range, unsigned codes 0..15 with an integer zero point,
@@ -65,6 +72,7 @@ GROUP = 128
 QMAX = 7      # 2^(4-1) - 1
 QMIN = -QMAX  # symmetric: max / 7 never gives -8
 UMAX = 15     # 2^4 - 1: asymmetric (affine) codes 0..15
+Q8MAX = 112   # 8-bit groups: 15 * 7 + 7, the largest |q| that splits into two INT4 codes
 
 __all__ = [
     "GROUP", "QMAX", "QMIN",
@@ -74,7 +82,7 @@ __all__ = [
     "transform_act", "transform_weight",
     "quantize_groups", "quantize_rrs", "rrs_channel_order", "quantize_per_channel", "permute_codes",
     "quantize_groups_asym", "UMAX", "pack_uint4", "unpack_uint4", "dequantize_asym", "weight_code_sums",
-    "w4a4_gemm_asym",
+    "w4a4_gemm_asym", "Q8MAX", "quantize_groups_mixed", "split_q8", "extend_weight_groups", "mixed_gemm_reference",
     "pack_int4", "unpack_int4",
     "group_accumulators", "dequant_gemm",
     "round_bf16", "round_output", "dequantize", "round_dequant_output",
@@ -282,6 +290,56 @@ def quantize_groups_asym(xt: np.ndarray, g: int = GROUP):
     codes = np.clip(np.rint(ratio) + z[:, :, None], 0, UMAX)
     codes = np.where(s[:, :, None] > 0, codes, 0).astype(np.uint8)
     return codes.reshape(R, K), s, z, ratio.reshape(R, K), zratio
+
+
+def split_q8(q8: np.ndarray):
+    """q8 = 15 h + l with h, l in [-7, 7]: h = rne(q8 / 15) (q8 / 15 is never a tie,
+    15 being odd), l = q8 - 15 h."""
+    q8 = np.asarray(q8, dtype=np.int64)
+    h = np.rint(q8 / 15.0).astype(np.int64)
+    return h, q8 - 15 * h
+
+
+def quantize_groups_mixed(xt: np.ndarray, groups8, g: int = GROUP):
+    """Per-(row, group) symmetric INT4, with the groups named in ``groups8`` kept
+    at 8 bits ([Paro] section 4.1: mixed precision, an 8-bit representation for
+    extreme outliers).  Reading: an 8-bit group uses the symmetric scale
+    s8 = max|x| / 112 and codes q8 = clamp(rne(x / s8), -112, 112) (225 levels,
+    so that q8 splits exactly into two INT4 codes, see split_q8).
+
+    Returns (q [R, K] int64: INT4 codes in 4-bit groups, q8 in 8-bit groups;
+    scales [R, G]: max/7 or max/112; ratio x / scale [R, K])."""
+    xt = np.asarray(xt, dtype=np.float64)
+    R, K = xt.shape
+    Gn = K // g
+    codes, sc, ratio = quantize_groups(xt, g)
+    codes = codes.astype(np.int64)
+    for gi in groups8:
+        sl = slice(gi * g, (gi + 1) * g)
+        m = np.abs(xt[:, sl]).max(axis=1)
+        s8 = m / Q8MAX
+        safe = np.where(s8 > 0, s8, 1.0)
+        r = np.where(s8[:, None] > 0, xt[:, sl] / safe[:, None], 0.0)
+        codes[:, sl] = np.clip(np.rint(r), -Q8MAX, Q8MAX)
+        sc[:, gi] = s8
+        ratio[:, sl] = r
+    return codes, sc, ratio
+
+
+def extend_weight_groups(codes_w: np.ndarray, sw: np.ndarray, groups8, g: int = GROUP):
+    """Weight codes [N, K] and scales [N, G] with the groups named in groups8
+    appended again, in that order: [N, K + 128 n8], [N, G + n8]."""
+    cw = np.asarray(codes_w)
+    extra = [cw[:, gi * g:(gi + 1) * g] for gi in groups8]
+    sw = np.asarray(sw)
+    return (np.concatenate([cw] + extra, axis=1),
+            np.concatenate([sw] + [sw[:, gi:gi + 1] for gi in groups8], axis=1))
+
+
+def mixed_gemm_reference(q, sa, groups8, codes_w, sw, g: int = GROUP) -> np.ndarray:
+    """Y = sum over groups of sa * sw * (sum of q * w) with q the mixed codes
+    (INT4, or q8 in the 8-bit groups): the plain definition, float64."""
+    return dequant_gemm(q, sa, codes_w, sw, g)
 
 
 def dequantize_asym(codes: np.ndarray, s: np.ndarray, z: np.ndarray, g: int = GROUP) -> np.ndarray:
@@ -538,7 +596,11 @@ def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GRO
     ``g`` is the quantization group ([Paro] section 2.3 uses 128; other
     group sizes are a knob of the same quantizer).  Mode "group128_asym" is
     the asymmetric (s, z) quantizer (quantize_groups_asym; the dict also
-    holds za and zratio, qa holds plain unsigned nibbles).  Mode "rrs_reorder" is
+    holds za and zratio, qa holds plain unsigned nibbles).  Mode
+    "group128_mixed" keeps the groups listed in ``order`` at 8 bits
+    (quantize_groups_mixed): qa [M, (K + 128 n8) / 2] holds the INT4 codes
+    with each 8-bit group's h plane in place and its l planes appended, sa
+    [M, G + n8] their scales; codes/scales hold the unsplit codes.  Mode "rrs_reorder" is
     Rotated Runtime Smooth with the channel reorder of [RRS] Figure 4 (1):
     the transformed channels are permuted by ``order`` (default: the
     rrs_channel_order of this call's activations) before grouping, and the
@@ -549,6 +611,23 @@ def quantize_act(X: np.ndarray, spec: dict, mode: str = "group128", g: int = GRO
     """
     xt = transform_act(X, spec)
     m = None
+    if mode == "group128_mixed":
+        # 8-bit groups as two INT4 planes: h in place, l appended (scales 15 s8 and s8)
+        groups8 = list(order if order is not None else [])
+        q, sc, ratio = quantize_groups_mixed(xt, groups8, g)
+        planes = q.copy()
+        sa_ext = [sc.copy()]
+        lows = []
+        for gi in groups8:
+            sl = slice(gi * g, (gi + 1) * g)
+            h, lo = split_q8(q[:, sl])
+            planes[:, sl] = h
+            sa_ext[0][:, gi] = 15.0 * sc[:, gi]
+            lows.append(lo)
+            sa_ext.append(sc[:, gi:gi + 1])
+        ext = np.concatenate([planes] + lows, axis=1).astype(np.int8)
+        return {"qa": pack_int4(ext), "sa": np.concatenate(sa_ext, axis=1), "codes": q, "scales": sc,
+                "ratio": ratio, "xt": xt, "s": None, "order": groups8, "m": None}
     if mode == "group128_asym":
         codes, sa, za, ratio, zratio = quantize_groups_asym(xt, g)
         return {"qa": pack_uint4(codes), "sa": sa, "za": za, "codes": codes, "ratio": ratio, "zratio": zratio,
