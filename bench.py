@@ -161,7 +161,8 @@ def parse():
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
                              "decode128", "decode256", "tiny", "kv", "rrs_reorder", "fused1", "fused2", "fused4",
-                             "fused8", "fused16", "q_proj_asym", "down_proj_asym", "decode16_asym"])
+                             "fused8", "fused16", "q_proj_asym", "down_proj_asym", "decode16_asym", "q_proj_mixed",
+                             "down_proj_mixed"])
     ap.add_argument("--group", type=int, default=128, choices=[64, 128, 256],
                     help="quantization group size (block-128 Hadamard workloads for 64 and 256)")
     ap.add_argument("--launch", default="prepared", choices=["prepared", "eager", "graph"],
@@ -613,6 +614,74 @@ def main_asym(args, torch, rw4, gu, dev):
     print(json.dumps(out), flush=True)
 
 
+def main_mixed(args, torch, rw4, gu, dev, n8=4):
+    """8-bit groups for extreme outliers on a block-128 Hadamard workload: the n8 groups
+    holding the workload's largest channel maxima are kept at 8 bits (two INT4 planes); one
+    step = quantize_act_mixed + w4a4_gemm over K + 128 n8 (weights extended offline), beside
+    the all-INT4 step on the same data."""
+    base = args.workload[:-len("_mixed")]
+    wl = workload(base)
+    M, K, N = wl.M, wl.K, wl.N
+    G = K // 128
+    t = rw4.Transform.hadamard(K, 128)
+    gmax = np.abs(wl.x).reshape(M, G, 128).max(axis=(0, 2))
+    groups8 = sorted(int(g) for g in np.argsort(-gmax)[:n8])
+    slot, glist = rw4.mixed_tables(K, groups8, dev)
+    x = gu.x_to_device(wl.x, wl.x_dtype)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(wl.w).to(dev))
+    qx, sx = rw4.extend_weight_groups(qw, sw, glist)
+    Kx = K + 128 * n8
+    nsets = max(2, math.ceil(MALL_FLUSH_BYTES / (M * K * 2 + M * Kx // 2 + N * Kx // 2 + M * N * 2)))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(x=x.clone(), qa=torch.empty((M, Kx // 2), dtype=torch.uint8, device=dev),
+                         sa=torch.empty((M, Kx // 128), dtype=torch.float32, device=dev),
+                         q4=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                         s4=torch.empty((M, G), dtype=torch.float32, device=dev),
+                         qx=qx.clone(), sx=sx.clone(), qw=qw.clone(), sw=sw.clone(),
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    qc = [rw4.prepare_quantize_act_mixed(t, s["x"], slot, n8, qa=s["qa"], sa=s["sa"]) for s in sets]
+    gc = [rw4.prepare_w4a4_gemm(s["qa"], s["sa"], s["qx"], s["sx"], out=s["y"]) for s in sets]
+    q4 = [rw4.prepare_quantize_act(t, s["x"], qa=s["q4"], sa=s["s4"]) for s in sets]
+    g4 = [rw4.prepare_w4a4_gemm(s["q4"], s["s4"], s["qw"], s["sw"], out=s["y"]) for s in sets]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        qc[i % nsets]()
+        gc[i % nsets]()
+
+    for i in range(args.warmup):
+        step(i)
+    r0, r1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    (q_us, _), (g_us, _) = (gpu_bound_us(torch, stream, lambda i: qc[i % nsets]()),
+                            gpu_bound_us(torch, stream, lambda i: gc[i % nsets]()))
+    (q4_us, _), (g4_us, _) = (gpu_bound_us(torch, stream, lambda i: q4[i % nsets]()),
+                              gpu_bound_us(torch, stream, lambda i: g4[i % nsets]()))
+    ops = 2.0 * M * N * K
+    log(f"{args.workload} M={M} K={K} N={N}, 8-bit groups {groups8}: step {ms_per_step * 1e3:.1f} us; "
+        f"mixed quantize {q_us:.2f} us, gemm over K + {128 * n8} {g_us:.2f} us; all-INT4 quantize {q4_us:.2f} us, "
+        f"gemm {g4_us:.2f} us")
+    out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
+                      "act_mode": f"group128 with {n8} groups at 8 bits (two INT4 planes)", "groups8": groups8},
+           "quantize_us": q_us, "gemm_us": g_us, "int4_quantize_us": q4_us, "int4_gemm_us": g4_us,
+           "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": gemm_kernel_for(M, N),
+                        "avg_launch_us": g_us, "note": "ops of the layer (2 M N K), the GEMM runs over K + 128 n8"}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -644,6 +713,8 @@ def main():
         return main_decode_fused(args, torch, rw4, gu, dev)
     if args.workload.endswith("_asym"):
         return main_asym(args, torch, rw4, gu, dev)
+    if args.workload.endswith("_mixed"):
+        return main_mixed(args, torch, rw4, gu, dev)
     wl = workload(args.workload)
     M, K, N = wl.M, wl.K, wl.N
     grp = args.group

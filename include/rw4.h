@@ -240,6 +240,34 @@ rw4_status rw4_w4a4_gemm_asym(const uint8_t* qa, const float* sa, const float* z
 rw4_status rw4_dequantize_asym(const uint8_t* q, const float* s, const float* z, int64_t M, int64_t K, void* out,
                                rw4_dtype out_dtype, int64_t ldo, void* stream);
 
+/* ---- 8-bit groups for extreme outliers ----------------------------------
+ * The independent-rotation article, section 4.1: mixed precision, an 8-bit
+ * representation kept for extreme outliers.  Reading: the caller names the
+ * 128-channel groups (a per-layer choice, like the article's other
+ * remedies for outlier-heavy layers).  Such a group is quantized
+ * symmetrically with 225 levels, q8 = rne(112 x~ / max|x~|) in [-112, 112],
+ * and split exactly as q8 = 15 h + l, h = rne(q8 / 15), h and l in [-7, 7]:
+ * two INT4 planes that the INT4 GEMM multiplies by the same weights.
+ *   slot_of_group [K/128] int32 (device): -1 for an INT4 group, j in
+ *     [0, n8) for the j-th 8-bit group (values outside [-1, n8) act as -1);
+ *   qa [M][(K + 128 n8)/2]: rw4_quantize_act's codes for INT4 groups; an
+ *     8-bit group's h plane in its own place and its l plane as extra group
+ *     K/128 + j;
+ *   sa [M][K/128 + n8]: max/7 (scaled as rw4_quantize_act) for INT4 groups,
+ *     15 max/112 for an h plane, max/112 for an l plane.
+ * Block-128 Hadamard only (else RW4_ERR_UNSUPPORTED); n8 <= K/128. */
+rw4_status rw4_quantize_act_mixed(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                                  const int32_t* slot_of_group, int64_t n8, uint8_t* qa, float* sa, void* stream);
+
+/* The matching weights: qw [N][K/2] and sw [N][K/128] (rw4_pack_weight)
+ * copied to qw_ext [N][(K + 128 n8)/2] and sw_ext [N][K/128 + n8] with the
+ * groups groups8[0..n8) (device int32, the 8-bit groups in slot order)
+ * appended again; a listed group outside [0, K/128) gives zero codes and
+ * scale.  Offline, with the weight pack.  rw4_w4a4_gemm over K + 128 n8 then
+ * computes the layer. */
+rw4_status rw4_extend_weight_groups(const uint8_t* qw, const float* sw, int64_t N, int64_t K, const int32_t* groups8,
+                                    int64_t n8, uint8_t* qw_ext, float* sw_ext, void* stream);
+
 /* ---- One decode step in one launch ---------------------------------------
  * y [M, N] = w4a4_gemm(quantize_act(t, x), qw, sw) for a decode-sized step
  * (1 <= M <= 16 tokens) in one kernel launch (the independent-rotation

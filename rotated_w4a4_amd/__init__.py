@@ -27,7 +27,7 @@ __all__ = [
     "prepare_rotate_act", "quantize_act_static", "quantize_act_rrs_reorder", "pack_weight_per_channel",
     "permute_codes", "prepare_permute_codes", "decode_fused", "prepare_decode_fused",
     "quantize_act_asym", "prepare_quantize_act_asym", "weight_code_sums", "w4a4_gemm_asym", "prepare_w4a4_gemm_asym",
-    "dequantize_asym",
+    "dequantize_asym", "mixed_tables", "quantize_act_mixed", "prepare_quantize_act_mixed", "extend_weight_groups",
     "status_str", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "rw4_dequantize_g", "rw4_w4a4_gemm_g", "rw4_rotate_act", "rw4_quantize_act_static", "rw4_status_str",
     "rw4_version", "rw4_rrs_reorder_workspace_bytes", "rw4_quantize_act_rrs_reorder", "rw4_pack_weight_per_channel",
     "rw4_permute_codes", "rw4_decode_fused", "rw4_quantize_act_asym", "rw4_weight_code_sums", "rw4_w4a4_gemm_asym",
-    "rw4_dequantize_asym",
+    "rw4_dequantize_asym", "rw4_quantize_act_mixed", "rw4_extend_weight_groups",
 )
 
 
@@ -97,6 +97,8 @@ lib.rw4_quantize_act_asym.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _p, 
 lib.rw4_weight_code_sums.argtypes = [_p, _i64, _i64, _p, _p]
 lib.rw4_w4a4_gemm_asym.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int, _i64, _p]
 lib.rw4_dequantize_asym.argtypes = [_p, _p, _p, _i64, _i64, _p, ctypes.c_int, _i64, _p]
+lib.rw4_quantize_act_mixed.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _p, _i64, _p, _p, _p]
+lib.rw4_extend_weight_groups.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p]
 for _name in EXPORTED_SYMBOLS:
     if _name not in ("rw4_status_str", "rw4_version", "rw4_transform_k", "rw4_rrs_reorder_workspace_bytes"):
         getattr(lib, _name).restype = ctypes.c_int
@@ -625,6 +627,73 @@ def dequantize_asym(q, s, z, out_dtype=None, out=None):
         raise ValueError(f"out must be [{M}, {K}] with unit stride along K")
     args = (q.data_ptr(), s.data_ptr(), z.data_ptr(), M, K, out.data_ptr(), _dtype_code(out), out.stride(0))
     return Call(lib.rw4_dequantize_asym, args, dev, "rw4_dequantize_asym", (q, s, z), out)()
+
+
+def mixed_tables(K: int, groups8, device):
+    """The device tables of a set of 8-bit groups: (slot_of_group int32 [K/128],
+    groups8 int32 [n8]) for quantize_act_mixed and extend_weight_groups."""
+    torch = _torch()
+    G = K // 128
+    groups8 = [int(g) for g in groups8]
+    if len(set(groups8)) != len(groups8) or any(g < 0 or g >= G for g in groups8):
+        raise ValueError(f"groups8 must be distinct group indices in [0, {G})")
+    slot = np.full(G, -1, dtype=np.int32)
+    for j, g in enumerate(groups8):
+        slot[g] = j
+    return (torch.from_numpy(slot).to(device),
+            torch.tensor(groups8 if groups8 else [0], dtype=torch.int32, device=device)[:len(groups8)])
+
+
+def quantize_act_mixed(t: Transform, x, slot_of_group, n8: int, qa=None, sa=None):
+    """Block-128 Hadamard activations with n8 groups at 8 bits (two INT4 planes):
+    qa uint8 [M, (K + 128 n8)/2], sa fp32 [M, K/128 + n8]."""
+    return prepare_quantize_act_mixed(t, x, slot_of_group, n8, qa, sa)()
+
+
+def prepare_quantize_act_mixed(t: Transform, x, slot_of_group, n8: int, qa=None, sa=None) -> Call:
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    dev = _on_gpu("x", x)
+    M, K = x.shape
+    if K != t.K:
+        raise ValueError(f"x has {K} channels, the transform {t.K}")
+    G = K // 128
+    _on_gpu("slot_of_group", slot_of_group, dev)
+    if slot_of_group.dtype != torch.int32 or slot_of_group.shape != (G,) or not slot_of_group.is_contiguous():
+        raise ValueError(f"slot_of_group must be a contiguous int32 tensor of {G} entries")
+    Kx = K + 128 * int(n8)
+    qa = torch.empty((M, Kx // 2), dtype=torch.uint8, device=x.device) if qa is None else qa
+    sa = torch.empty((M, Kx // 128), dtype=torch.float32, device=x.device) if sa is None else sa
+    _out("qa", qa, (M, Kx // 2), torch.uint8, dev)
+    _out("sa", sa, (M, Kx // 128), torch.float32, dev)
+    args = (t.handle, x.data_ptr(), _dtype_code(x), M, x.stride(0), slot_of_group.data_ptr(), int(n8), qa.data_ptr(),
+            sa.data_ptr())
+    return Call(lib.rw4_quantize_act_mixed, args, dev, "rw4_quantize_act_mixed", (t, x, slot_of_group), (qa, sa))
+
+
+def extend_weight_groups(qw, sw, groups8, qw_ext=None, sw_ext=None):
+    """qw/sw with the groups of groups8 (device int32 [n8]) appended: [N, (K + 128 n8)/2], [N, K/128 + n8]."""
+    torch = _torch()
+    N, Kh = qw.shape
+    K = Kh * 2
+    n8 = int(groups8.numel())
+    dev = _on_gpu("qw", qw)
+    for name, tns, dt in (("qw", qw, torch.uint8), ("sw", sw, torch.float32), ("groups8", groups8, torch.int32)):
+        _on_gpu(name, tns, dev)
+        if tns.dtype != dt or not tns.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if sw.shape != (N, K // 128):
+        raise ValueError("sw must be [N, K/128]")
+    Kx = K + 128 * n8
+    qw_ext = torch.empty((N, Kx // 2), dtype=torch.uint8, device=qw.device) if qw_ext is None else qw_ext
+    sw_ext = torch.empty((N, Kx // 128), dtype=torch.float32, device=qw.device) if sw_ext is None else sw_ext
+    _out("qw_ext", qw_ext, (N, Kx // 2), torch.uint8, dev)
+    _out("sw_ext", sw_ext, (N, Kx // 128), torch.float32, dev)
+    args = (qw.data_ptr(), sw.data_ptr(), N, K, groups8.data_ptr() if n8 else None, n8, qw_ext.data_ptr(),
+            sw_ext.data_ptr())
+    return Call(lib.rw4_extend_weight_groups, args, dev, "rw4_extend_weight_groups", (qw, sw, groups8),
+                (qw_ext, sw_ext))()
 
 
 def w4a4_gemm(qa, sa, qw, sw, out_dtype=None, out=None):

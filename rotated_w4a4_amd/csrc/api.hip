@@ -365,6 +365,35 @@ rw4_status rw4_quantize_act_asym(const rw4_transform* t, const void* x, rw4_dtyp
   return from_hip(rw4::launch_quantize_act_asym(t->dev, x, x_dtype == RW4_BF16, M, ldx, qa, sa, za, st));
 }
 
+rw4_status rw4_quantize_act_mixed(const rw4_transform* t, const void* x, rw4_dtype x_dtype, int64_t M, int64_t ldx,
+                                  const int32_t* slot_of_group, int64_t n8, uint8_t* qa, float* sa, void* stream) {
+  if (!t) return RW4_ERR_ARG;
+  if (x_dtype != RW4_F32 && x_dtype != RW4_BF16) return RW4_ERR_ARG;
+  if (M < 0 || n8 < 0) return RW4_ERR_SHAPE;
+  if (t->dev.kind != rw4::TransformKind::Hadamard || t->dev.block != 128) return RW4_ERR_UNSUPPORTED;
+  const int64_t K = t->dev.K;
+  if (n8 > K / kGroup) return RW4_ERR_SHAPE;
+  if (!on_home_device(t)) return RW4_ERR_ARG;
+  if (M == 0) return RW4_OK;
+  if (!x || !slot_of_group || !qa || !sa) return RW4_ERR_ARG;
+  if (ldx < K) return RW4_ERR_ARG;
+  const int64_t esz = x_dtype == RW4_BF16 ? 2 : 4;
+  if (!aligned16(x) || (ldx * esz) % 16 || !aligned16(qa) || !aligned16(sa)) return RW4_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(rw4::launch_quantize_act_mixed(t->dev, x, x_dtype == RW4_BF16, M, ldx, slot_of_group, n8, qa, sa,
+                                                 st));
+}
+
+rw4_status rw4_extend_weight_groups(const uint8_t* qw, const float* sw, int64_t N, int64_t K, const int32_t* groups8,
+                                    int64_t n8, uint8_t* qw_ext, float* sw_ext, void* stream) {
+  if (N < 0 || n8 < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24) || n8 > K / kGroup) return RW4_ERR_SHAPE;
+  if (N == 0) return RW4_OK;
+  if (!qw || !sw || !qw_ext || !sw_ext || (n8 > 0 && !groups8)) return RW4_ERR_ARG;
+  if (!aligned16(qw) || !aligned16(qw_ext)) return RW4_ERR_ARG;
+  return from_hip(rw4::launch_extend_weight_groups(qw, sw, N, K, groups8, n8, qw_ext, sw_ext,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 rw4_status rw4_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, void* stream) {
   if (N < 0 || K <= 0 || K % kGroup || K > (int64_t(1) << 24)) return RW4_ERR_SHAPE;
   if (N == 0) return RW4_OK;

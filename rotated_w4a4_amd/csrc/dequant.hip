@@ -167,4 +167,46 @@ hipError_t launch_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, floa
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Weights for 8-bit activation groups: every row of the packed weights with
+// the groups listed in groups8 appended again (codes and scales), so that
+// the INT4 GEMM over K + 128 n8 multiplies an 8-bit group's two planes by
+// the same weights.  One lane per 16-byte chunk of an output row; a listed
+// group outside [0, G) yields zero codes and scale.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void extend_weight_groups_kernel(const uint8_t* __restrict__ qw,
+                                                                   const float* __restrict__ sw, int64_t G,
+                                                                   const int32_t* __restrict__ groups8, int64_t n8,
+                                                                   int64_t row0, uint8_t* __restrict__ qx,
+                                                                   float* __restrict__ sx) {
+  const int64_t Gx = G + n8;
+  const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // 16-byte chunk of the output row
+  if (c >= Gx * 4) return;
+  const int64_t n = row0 + blockIdx.y;
+  const int64_t gx = c >> 2;
+  int64_t src = gx;
+  if (gx >= G) src = groups8[gx - G];
+  const bool ok = src >= 0 && src < G;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *reinterpret_cast<const uint4*>(qw + n * (G * 64) + src * 64 + (c & 3) * 16);
+  *reinterpret_cast<uint4*>(qx + n * (Gx * 64) + c * 16) = v;
+  if ((c & 3) == 0) sx[n * Gx + gx] = ok ? sw[n * G + src] : 0.0f;
+}
+
+hipError_t launch_extend_weight_groups(const uint8_t* qw, const float* sw, int64_t N, int64_t K,
+                                       const int32_t* groups8, int64_t n8, uint8_t* qx, float* sx, hipStream_t st) {
+  const int64_t G = K / kGroup, chunks = (G + n8) * 4;
+  const int64_t bx = (chunks + 255) / 256;
+  if (bx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  constexpr int64_t kMaxRows = 65535;
+  for (int64_t r0 = 0; r0 < N; r0 += kMaxRows) {
+    const int64_t rows = N - r0 < kMaxRows ? N - r0 : kMaxRows;
+    hipLaunchKernelGGL(extend_weight_groups_kernel, dim3(unsigned(bx), unsigned(rows)), dim3(256), 0, st, qw, sw, G,
+                       groups8, n8, r0, qx, sx);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace rw4

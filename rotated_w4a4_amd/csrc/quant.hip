@@ -1458,6 +1458,109 @@ bool rowh_supported(int64_t K) {
 // Activations: X [M, K] row-major.
 // group: 64, 128 or 256 for the block-128 Hadamard in per-group mode, else
 // 128 (the caller checks).
+// ---------------------------------------------------------------------------
+// quant_h128_mixed: block-128 Hadamard activations in groups of 128, with the
+// groups named by slot_of_group (>= 0) kept at 8 bits (the independent-
+// rotation article, section 4.1: mixed precision for extreme outliers).  An
+// 8-bit group gets q8 = rne(112 x~ / max) (225 levels) split exactly as
+// q8 = 15 h + l (h = rne(q8 / 15), never a tie): h is stored in place with
+// scale 15 max / 112, l in the extra group G + slot with scale max / 112.
+// Every other group is quant_h128_act's INT4 group (same arithmetic).
+// Rows hold G + n8 groups.  A block covers 16 groups of one row (wave w:
+// groups 4 w .. 4 w + 3, 16 lanes each).
+// ---------------------------------------------------------------------------
+template <bool BF16, bool SIGNED>
+__global__ __launch_bounds__(256) void quant_h128_mixed_kernel(const void* __restrict__ x, int64_t ldx, int64_t G,
+                                                               int64_t n8, int64_t blocks_per_row,
+                                                               const uint32_t* __restrict__ sign_mask,
+                                                               const int32_t* __restrict__ slot_of_group,
+                                                               uint8_t* __restrict__ q, float* __restrict__ s,
+                                                               float post4, float post8h, float post8l) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 15;
+  const int64_t row = int64_t(blockIdx.x) / blocks_per_row;
+  const int64_t grp = (int64_t(blockIdx.x) - row * blocks_per_row) * 16 + wave * 4 + (lane >> 4);
+  const bool valid = grp < G;
+  const int64_t Gx = G + n8;
+  float v[8];
+  if (valid) {
+    RowSrc<BF16>{x, ldx}.load8(row, grp * kGroup + sub * 8, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  }
+  if constexpr (SIGNED) {
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ sign_mask[grp * kGroup + sub * 8 + e]);
+    }
+  }
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  const float flip = parity_sign(lane & 15);
+  fwht8(v);
+  lane_stages_dpp(v, c1, c2, c7, c8);
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+  m = row16_max_dpp(m);
+  const int32_t slot = valid ? slot_of_group[grp] : -1;
+  const int word = h128_lane_word(sub);
+  uint8_t* const qrow = q + row * (Gx * 64);
+  float* const srow = s + row * Gx;
+  if (slot < 0 || slot >= n8) {
+    const uint32_t packed = encode8_rcp(v, m, flip);
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = packed;
+      if (sub == 0) srow[grp] = m * post4;
+    }
+    return;
+  }
+  // 8-bit group: 112 / m as the reciprocal of m / 112 (tiny maxima lifted as in encode8_rcp)
+  float mm = m;
+  if (m > 0.0f && m < kTinyMax) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
+    mm = m * kTinyLift;
+  }
+  const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 112.0f)) : 0.0f;
+  uint32_t bh[8], bl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q8 = int(rne_code_bits(v[e], inv) - kRoundMagicBits);
+    const int h = int(rne_code_bits(float(q8), 1.0f / 15.0f) - kRoundMagicBits);
+    bh[e] = kRoundMagicBits + uint32_t(h);
+    bl[e] = kRoundMagicBits + uint32_t(q8 - 15 * h);
+  }
+  *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = pack8_bits(bh);
+  *reinterpret_cast<uint32_t*>(qrow + (G + slot) * 64 + word * 4) = pack8_bits(bl);
+  if (sub == 0) {
+    srow[grp] = m * post8h;
+    srow[G + slot] = m * post8l;
+  }
+}
+
+hipError_t launch_quantize_act_mixed(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
+                                     const int32_t* slot_of_group, int64_t n8, uint8_t* q, float* s, hipStream_t st) {
+  if (t.kind != TransformKind::Hadamard || t.block != kGroup) return hipErrorInvalidValue;
+  const int64_t G = t.K / kGroup;
+  const int64_t bpr = (G + 15) / 16, blocks = M * bpr;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const float norm = 1.0f / sqrtf(128.0f);
+  const float post4 = norm * (1.0f / 7.0f), post8h = norm * (15.0f / 112.0f), post8l = norm * (1.0f / 112.0f);
+#define RW4_MIXED(B, S)                                                                                          \
+  hipLaunchKernelGGL((quant_h128_mixed_kernel<B, S>), dim3(unsigned(blocks)), dim3(256), 0, st, x, ldx, G, n8, bpr, \
+                     t.sign_mask, slot_of_group, q, s, post4, post8h, post8l)
+  if (bf16) {
+    if (t.sign_mask) RW4_MIXED(true, true); else RW4_MIXED(true, false);
+  } else {
+    if (t.sign_mask) RW4_MIXED(false, true); else RW4_MIXED(false, false);
+  }
+#undef RW4_MIXED
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act_asym(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
                                     uint8_t* q, float* s, float* z, hipStream_t st) {
   if (t.kind != TransformKind::Hadamard || t.block != kGroup) return hipErrorInvalidValue;

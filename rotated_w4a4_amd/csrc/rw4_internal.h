@@ -34,6 +34,13 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
 // unsigned nibbles, scales and zero points (floats) [M][K / 128].
 hipError_t launch_quantize_act_asym(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
                                     uint8_t* q, float* s, float* z, hipStream_t st);
+// Block-128 Hadamard activations with the groups whose slot_of_group entry
+// is in [0, n8) kept at 8 bits as two INT4 planes (rows of G + n8 groups).
+hipError_t launch_quantize_act_mixed(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
+                                     const int32_t* slot_of_group, int64_t n8, uint8_t* q, float* s, hipStream_t st);
+// Packed weights [N][K/2] and scales with the groups of groups8 [n8] appended.
+hipError_t launch_extend_weight_groups(const uint8_t* qw, const float* sw, int64_t N, int64_t K,
+                                       const int32_t* groups8, int64_t n8, uint8_t* qx, float* sx, hipStream_t st);
 // cw[n][g] = sum of the 128 codes of group g of packed weight row n (floats).
 hipError_t launch_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, hipStream_t st);
 // y = sum_g sa sw (sum_k qa qw - za cw) with plain-nibble activation codes (groups of 128).

@@ -437,3 +437,29 @@ def test_asym_entry_points_validation():
     assert d(FAKE, FAKE, FAKE, 4, 200, FAKE, 1, 256, None) == SHAPE
     assert d(FAKE, FAKE, None, 4, 256, FAKE, 1, 256, None) == ARG
     assert d(FAKE, FAKE, FAKE, 4, 256, FAKE, 1, 100, None) == ARG                        # ldo < K
+
+
+def test_mixed_entry_points_validation():
+    """8-bit groups: block-128 Hadamard only, n8 <= K/128, null checks before device work."""
+    f = lib.rw4_quantize_act_mixed
+    assert f(None, FAKE, 1, 4, 256, FAKE, 1, FAKE, FAKE, None) == ARG
+    st, h = _had(256, 128)
+    assert st == OK
+    try:
+        assert f(h, FAKE, 1, 4, 256, FAKE, 3, FAKE, FAKE, None) == SHAPE     # n8 > K / 128
+        assert f(h, FAKE, 1, 4, 256, FAKE, -1, FAKE, FAKE, None) == SHAPE
+        assert f(h, FAKE, 1, 4, 256, None, 1, FAKE, FAKE, None) == ARG       # no slot map
+        assert f(h, None, 1, 0, 256, None, 1, None, None, None) == OK        # empty
+        assert f(h, FAKE, 1, 4, 200, FAKE, 1, FAKE, FAKE, None) == ARG       # ldx < K
+    finally:
+        lib.rw4_transform_destroy(h)
+    st, h = _had(512, 256)
+    try:
+        assert f(h, FAKE, 1, 4, 512, FAKE, 1, FAKE, FAKE, None) == UNSUP
+    finally:
+        lib.rw4_transform_destroy(h)
+    e = lib.rw4_extend_weight_groups
+    assert e(FAKE, FAKE, 4, 100, FAKE, 1, FAKE, FAKE, None) == SHAPE
+    assert e(FAKE, FAKE, 4, 256, FAKE, 3, FAKE, FAKE, None) == SHAPE
+    assert e(FAKE, FAKE, 4, 256, None, 1, FAKE, FAKE, None) == ARG
+    assert e(FAKE, FAKE, 0, 256, None, 1, None, None, None) == OK
