@@ -831,14 +831,36 @@ __global__ __launch_bounds__(256) void rrs_chanmax_kernel(Src src, int64_t M, in
   for (int j = threadIdx.x; j < K; j += blockDim.x) partial[int64_t(blockIdx.x) * K + j] = red[j];
 }
 
-// m[j] = max over the P partial rows (one thread per channel).
-__global__ __launch_bounds__(256) void chanmax_reduce_kernel(const float* __restrict__ partial, int P, int64_t K,
-                                                             float* __restrict__ m) {
-  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+// m[j] = max over the P partial rows.  A block of 16 waves takes 64
+// channels; wave w reads partial rows w, w + 16, ... (64 consecutive floats
+// per row, all of a lane's loads in flight at once), then the 16 waves
+// combine in LDS.  (One thread per channel over all P rows left 16 blocks
+// waiting on memory latency: 61 us at K = 4096.)
+__global__ __launch_bounds__(1024) void chanmax_reduce_kernel(const float* __restrict__ partial, int P, int64_t K,
+                                                              float* __restrict__ m) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t j = int64_t(blockIdx.x) * 64 + lane;
   float v = 0.0f;
-  for (int p = 0; p < P; ++p) v = fmaxf(v, partial[int64_t(p) * K + j]);
-  m[j] = v;
+  if (j < K) {
+    int p = w;
+    for (; p + 15 * 16 < P; p += 16 * 16) {
+      float t[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) t[u] = partial[int64_t(p + 16 * u) * K + j];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v = fmaxf(v, t[u]);
+    }
+    for (; p < P; p += 16) v = fmaxf(v, partial[int64_t(p) * K + j]);
+  }
+  red[w][lane] = v;
+  __syncthreads();
+  if (w == 0 && j < K) {
+    float r = red[0][lane];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) r = fmaxf(r, red[k][lane]);
+    m[j] = r;
+  }
 }
 
 // rank(j) = #{i : m_i > m_j} + #{i < j : m_i == m_j}: the position of
@@ -982,43 +1004,64 @@ __global__ __launch_bounds__(256) void quant_row_perchannel_kernel(Src src, int6
 }
 
 // Codes of every row taken in channel order: out[r, j] = code(q[r], order[j]).
-// A block walks rows with the order in LDS; each row's stored words are
-// staged in LDS, every thread builds whole output words (8 codes).  The
-// stored form puts the sign of code e in bit 3 of nibble (e + 1) mod 8 of its
-// word.
+// A block walks rows four at a time: their stored words are staged in LDS
+// together, and every thread builds whole output words (8 codes) of all four
+// rows.  A thread's output words and their source positions are the same
+// in every row, so it reads the order once (K <= 8192: at most 4 output
+// words of 8 codes per thread).  The stored form puts the sign of code e in
+// bit 3 of nibble (e + 1) mod 8 of its word.
+constexpr int kPermuteRows = 4;
 __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t K,
                                                             const int32_t* __restrict__ order,
                                                             uint8_t* __restrict__ out) {
-  extern __shared__ uint32_t pc_smem[];  // K order entries, then K / 8 stored words of a row
-  int32_t* ord = reinterpret_cast<int32_t*>(pc_smem);
-  uint32_t* words = pc_smem + K;
-  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
-  const int64_t W = K / 8;
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    __syncthreads();  // order staged / the previous row's words consumed
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(q + row * (K / 2));
-    for (int64_t i = threadIdx.x; i < W; i += blockDim.x) words[i] = src[i];
+  extern __shared__ uint32_t pc_smem[];  // kPermuteRows rows of K / 8 stored words
+  const int W = int(K / 8);
+  // source word and nibble of this thread's output codes (word i = threadIdx.x + 256 u)
+  uint16_t srcw[4][8];
+  uint8_t srcn[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = int(threadIdx.x) + 256 * u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t k = i < W ? min(uint32_t(order[i * 8 + e]), uint32_t(K - 1)) : 0u;  // clamped into the row
+      srcw[u][e] = uint16_t(k >> 3);
+      srcn[u][e] = uint8_t(k & 7);
+    }
+  }
+  for (int64_t row0 = int64_t(blockIdx.x) * kPermuteRows; row0 < rows; row0 += int64_t(gridDim.x) * kPermuteRows) {
+    const int nr = int(rows - row0 < kPermuteRows ? rows - row0 : kPermuteRows);
+    __syncthreads();  // the previous rows' words consumed
+    for (int r = 0; r < nr; ++r) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(q + (row0 + r) * (K / 2));
+      for (int i = threadIdx.x; i < W; i += blockDim.x) pc_smem[r * W + i] = src[i];
+    }
     __syncthreads();
-    uint32_t* dst = reinterpret_cast<uint32_t*>(out + row * (K / 2));
-    for (int64_t i = threadIdx.x; i < W; i += blockDim.x) {
-      int code[8];
+    for (int r = 0; r < nr; ++r) {
+      const uint32_t* words = pc_smem + r * W;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(out + (row0 + r) * (K / 2));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int32_t k = int32_t(min(uint32_t(ord[i * 8 + e]), uint32_t(K - 1)));  // clamped into the row
-        const uint32_t wd = words[k >> 3];
-        const int n = k & 7;
-        const int mag = int((wd >> (4 * n)) & 7u);
-        const int neg = int((wd >> (4 * ((n + 1) & 7) + 3)) & 1u);
-        code[e] = neg ? -mag : mag;
-      }
-      uint32_t o = 0;
+      for (int u = 0; u < 4; ++u) {
+        const int i = int(threadIdx.x) + 256 * u;
+        if (i >= W) break;
+        int code[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t mag = uint32_t(code[e] < 0 ? -code[e] : code[e]);
-        const uint32_t prev_neg = code[(e + 7) & 7] < 0 ? 8u : 0u;
-        o |= (mag | prev_neg) << (4 * e);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wd = words[srcw[u][e]];
+          const int n = srcn[u][e];
+          const int mag = int((wd >> (4 * n)) & 7u);
+          const int neg = int((wd >> (4 * ((n + 1) & 7) + 3)) & 1u);
+          code[e] = neg ? -mag : mag;
+        }
+        uint32_t o = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t mag = uint32_t(code[e] < 0 ? -code[e] : code[e]);
+          const uint32_t prev_neg = code[(e + 7) & 7] < 0 ? 8u : 0u;
+          o |= (mag | prev_neg) << (4 * e);
+        }
+        dst[i] = o;
       }
-      dst[i] = o;
     }
   }
 }
@@ -1346,7 +1389,7 @@ hipError_t launch_rrs_reorder_src(const Src& src, int64_t K, int log2b, int64_t 
   auto run = [&](auto e_const) {
     constexpr int E = decltype(e_const)::value;
     hipLaunchKernelGGL((rrs_chanmax_kernel<E, Src>), dim3(kChanmaxBlocks), dim3(256), 0, st, src, M, log2b, partial);
-    hipLaunchKernelGGL(chanmax_reduce_kernel, dim3(unsigned((K + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(chanmax_reduce_kernel, dim3(unsigned((K + 63) / 64)), dim3(1024), 0, st,
                        (const float*)partial, kChanmaxBlocks, K, m);
     hipLaunchKernelGGL(rrs_rank_kernel, dim3(unsigned(K / 16)), dim3(256), rank_lds, st, (const float*)m, K, order,
                        smooth);
@@ -1419,8 +1462,9 @@ hipError_t launch_pack_weight_per_channel(const TransformDev& t, const void* w, 
 
 hipError_t launch_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const int32_t* order, uint8_t* out,
                                 hipStream_t st) {
-  const int64_t grid = rows < 1024 ? rows : 1024;
-  const int lds = int(K * 4 + (K / 8) * 4);
+  const int64_t batches = (rows + kPermuteRows - 1) / kPermuteRows;
+  const int64_t grid = batches < 1024 ? batches : 1024;
+  const int lds = int(kPermuteRows * (K / 8) * 4);
   hipLaunchKernelGGL(permute_codes_kernel, dim3(unsigned(grid)), dim3(256), lds, st, q, rows, K, order, out);
   return hipGetLastError();
 }
