@@ -149,6 +149,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Block barrier for LDS hand-offs only: waits for this wave's LDS accesses
+// (vmcnt left at its maximum), so the global loads of later stages stay in
+// flight across it; __syncthreads() would drain them (its workgroup release
+// fence waits for vmcnt(0)).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
@@ -1101,14 +1110,26 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
       }
     }
   };
-  // one iteration: stage cur into LDS, issue the next iteration into nxt, compute cur
+  // one iteration: stage cur into LDS, issue the next iteration into nxt,
+  // compute cur.  With 32 channels per block (CT = 2, several blocks per CU)
+  // the barriers wait for LDS only, so nxt's loads stay in flight across
+  // them (-11 % at 1 x 4096 x 14336); with one block per CU (CT = 1) the
+  // draining __syncthreads() measured faster (5.2 against 5.6 us at
+  // 1 x 4096 x 4096, 8.1 against 9.3 us at 64 x 4096 x 4096), also with a
+  // third register stage.
+  auto block_sync = [] {
+    if constexpr (CT == 2)
+      lds_barrier();
+    else
+      __syncthreads();
+  };
   auto step = [&](Stage& cur, Stage& nxt, int64_t it) {
     store(cur);
-    __syncthreads();
+    block_sync();
     issue(nxt, it + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(cur);
-    __syncthreads();  // LDS free for the next store
+    block_sync();  // LDS free for the next store
   };
 
   Stage s0, s1;
@@ -1345,15 +1366,21 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
   };
   // one iteration: the next weights are requested, this iteration's
   // activations (loaded one iteration ago) are quantized into LDS, the next
-  // activations requested, then the MFMAs
+  // activations requested, then the MFMAs (barriers as in gemm_small_kernel)
+  auto block_sync = [] {
+    if constexpr (CT == 2)
+      lds_barrier();
+    else
+      __syncthreads();
+  };
   auto step = [&](Stage& cur, Stage& nxt, int64_t it) __attribute__((always_inline)) {
     issue_b(nxt, it + 1);
     quantize(it);
     issue_x(it + 1);
     store_b(cur);
-    __syncthreads();
+    block_sync();
     compute(cur);
-    __syncthreads();  // LDS free for the next iteration
+    block_sync();  // LDS free for the next iteration
   };
   Stage s0, s1;
   issue_x(0);
