@@ -3,7 +3,7 @@
 
 One step = one pass of the whole online path over one batch: quantize_act
 (load bf16 activations, block Walsh-Hadamard, group-128 absmax, INT4 RNE,
-pack) followed by w4a4_gemm (FP8 MFMA on the exact codes, per-128-group
+pack) followed by w4a4_gemm (FP6 MFMA on the exact codes, per-128-group
 rescale, fp32 epilogue, bf16 output).  Weights are transformed and packed once before timing, as in
 deployment (the offline step).  Default workload: LLaMA-3-8B q_proj prefill,
 X 2048x4096 bf16 with channel outliers and spikes, W 4096x4096.
@@ -18,7 +18,8 @@ Prints one JSON line (stdout).  Per-kernel times come from HIP events
 caches) recorded on the stream the library launches on, around the kernels
 of every fourth timed step (recording them on every step would slow the
 timed throughput itself by ~7 % at q_proj); the GEMM is the
-dominant kernel and its FP8/int8 MFMA roofline (5 POPS dense) is reported,
+dominant kernel and its int8 MFMA roofline (5 POPS dense) is reported (the
+GEMM issues FP6 MFMAs; the fraction of their 10.1 PFLOP/s peak is given too),
 the quantize kernel's HBM roofline beside it.  Steps are issued through
 calls prepared once per buffer set (arguments checked and marshalled once,
 as a serving loop reuses its buffers; `--launch eager` checks on every
@@ -49,7 +50,8 @@ if ROOT not in sys.path:
 
 METRIC = "W4A4 layer TOPS + quantize GB/s (% roofline) at LLaMA-3-8B q_proj shapes"
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
-PEAK_I8_TOPS = 5000.0        # MI355X dense FP8 / int8 MFMA (the GEMM runs on the FP8 units)
+PEAK_I8_TOPS = 5000.0        # MI355X dense int8 (and FP8) MFMA: the INT4 GEMM's roofline
+PEAK_F6_TFLOPS = 10100.0     # MI355X dense FP6 MFMA: the units the GEMM's products run on
 MALL_FLUSH_BYTES = 512 << 20
 EVENT_EVERY = 4              # timed steps per step instrumented with per-kernel events
 
@@ -478,12 +480,13 @@ def main_rrs_reorder(args, torch, rw4, gu, dev):
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
-           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"rrs_reorder M={M} K={K} N={N}", "transform": f"hadamard{K}",
                       "act_mode": "rrs with channel reorder", "weights": "per output channel, permuted per call"},
            "quantize_us": q_us, "permute_us": p_us, "gemm_us": g_us,
            "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": "gemm_f8p_kernel",
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "peak_fp6": PEAK_F6_TFLOPS,
+                        "frac_fp6": ops / g_us / 1e6 / PEAK_F6_TFLOPS, "traffic": None, "kernel": "gemm_f8p_kernel",
                         "avg_launch_us": g_us},
            "permute": {"kernel": "permute_codes_kernel", "avg_launch_us": p_us, "algorithmic_bytes": pbytes,
                        "gbps": pbytes / p_us / 1e3, "frac_hbm": pbytes / p_us / 1e3 / PEAK_HBM_GBPS},
@@ -539,7 +542,7 @@ def main_decode_fused(args, torch, rw4, gu, dev):
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
-           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"decode_fused M={M} K={K} N={N}", "transform": "hadamard128",
                       "act_mode": "group128"},
            "fused_us": f_us, "two_launch_us": t_us,
@@ -603,12 +606,13 @@ def main_asym(args, torch, rw4, gu, dev):
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
-           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
                       "act_mode": "group128 asymmetric (s, z)"},
            "quantize_us": q_us, "gemm_us": g_us, "symmetric_quantize_us": qs_us, "symmetric_gemm_us": gs_us,
            "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": gk, "avg_launch_us": g_us},
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "peak_fp6": PEAK_F6_TFLOPS,
+                        "frac_fp6": ops / g_us / 1e6 / PEAK_F6_TFLOPS, "traffic": None, "kernel": gk, "avg_launch_us": g_us},
            "quantize": {"kernel": "quant_h128_act_kernel (asymmetric)", "avg_us": q_us, "algorithmic_bytes": qbytes,
                         "gbps": qbytes / q_us / 1e3, "frac_hbm": qbytes / q_us / 1e3 / PEAK_HBM_GBPS}}
     print(json.dumps(out), flush=True)
@@ -672,12 +676,13 @@ def main_mixed(args, torch, rw4, gu, dev, n8=4):
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
-           "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
+           "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
                       "act_mode": f"group128 with {n8} groups at 8 bits (two INT4 planes)", "groups8": groups8},
            "quantize_us": q_us, "gemm_us": g_us, "int4_quantize_us": q4_us, "int4_gemm_us": g4_us,
            "roofline": {"bound": "mfma", "achieved": ops / g_us / 1e6, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "traffic": None, "kernel": gemm_kernel_for(M, N),
+                        "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "peak_fp6": PEAK_F6_TFLOPS,
+                        "frac_fp6": ops / g_us / 1e6 / PEAK_F6_TFLOPS, "traffic": None, "kernel": gemm_kernel_for(M, N),
                         "avg_launch_us": g_us, "note": "ops of the layer (2 M N K), the GEMM runs over K + 128 n8"}}
     print(json.dumps(out), flush=True)
 
@@ -857,10 +862,11 @@ def main():
                           "eager step overstate by the host's launch gaps"}
     else:
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                "frac": gemm_tops / PEAK_I8_TOPS, "traffic": traffic,
+                "frac": gemm_tops / PEAK_I8_TOPS, "peak_fp6": PEAK_F6_TFLOPS, "frac_fp6": gemm_tops / PEAK_F6_TFLOPS,
+                "traffic": traffic,
                 "kernel": gemm_kernel, "ops_per_launch": ops, "avg_launch_us": g_us,
                 "algorithmic_bytes_per_launch": gbytes,
-                "note": "ops = 2 M N K (2 per MAC of INT4 codes, computed exactly on the FP8 MFMA) against the dense FP8/int8 MFMA peak; traffic in bytes"}
+                "note": "ops = 2 M N K (2 per MAC of INT4 codes, computed exactly on the FP6 MFMA) against the dense int8 MFMA peak (frac) and the dense FP6 peak (frac_fp6); traffic in bytes"}
     if wl.transform[0] == "givens":
         quant_kernel = "quant_givens_kernel"
     elif wl.transform[1] == 128 and wl.mode == "group128":
@@ -880,7 +886,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes (exact on fp8 MFMA), fp32 transform, rescale and epilogue",
+        "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue",
         "data": "synthetic",
         "config": {"workload": f"{wl.name} M={M} K={K} N={N}", "M": M, "K": K, "N": N,
                    "transform": f"{wl.transform[0]}{wl.transform[1]}", "act_mode": wl.mode,

@@ -39,12 +39,19 @@
  *     problem definition), but the symmetric scale max/7 maps every value
  *     into [-7, 7] (-8 never arises), and this layout stores exactly that
  *     domain: a code of -8 cannot be represented.  Every 32-bit
- *     little-endian word (bytes 4w..4w+3 of a row) holds codes c_0..c_7 of
- *     that word as sign-magnitude nibbles: nibble e (byte e/2, low nibble
- *     for even e) = |c_e| in bits 0-2 plus the sign (1 = negative) of
- *     c_((e-1) mod 8) in bit 3; zero has sign 0.  Masking a word with
- *     0x87878787, and its rotation right by 4 bits likewise, gives the even
- *     and the odd codes as sign-magnitude bytes.
+ *     little-endian word w (bytes 4w..4w+3 of a row) holds the codes
+ *     c_0..c_7 of channels 8w..8w+7 as sign-magnitude (|c| in 3 bits, sign
+ *     1 = negative, zero with sign 0), bit t of code e (t = 0, 1, 2 for |c|,
+ *     t = 3 for the sign) at position P[w % 2][e][t]:
+ *       even words: (0,1,2,5) (6,7,8,11) (12,13,14,17) (18,19,20,23)
+ *                   (24,25,26,29) (30,31,16,3) (4,21,22,9) (10,27,28,15)
+ *       odd words:  (0,17,18,5) (6,23,24,11) (12,29,30,1) (2,3,4,7)
+ *                   (8,9,10,13) (14,15,16,19) (20,21,22,25) (26,27,28,31)
+ *     A word pair (W0, W1) = words 2j, 2j+1 opens into the dense 96-bit
+ *     string of its 16 codes' FP6 E2M3 encodings (code k, as the subnormal
+ *     c/8, at bits 6k..6k+5) as D0 = W0 & 0xE79E79E7, D2 = W1 & 0x9E79E79E,
+ *     D1 = (rot16(V) & 0x18611861) | (V & ~0x18611861) with
+ *     V = (W0 & ~0xE79E79E7) | (W1 & ~0x9E79E79E): the GEMM's operand form.
  *     qa is [M, K/2] bytes, qw is [N, K/2] bytes, rows contiguous.
  *   - Scales: fp32, row-major, sa [M, G], sw [N, G].
  *   - stream is a hipStream_t (NULL = the null stream).  Every call checks
@@ -211,8 +218,14 @@ rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, co
  * the transformed row x~ (block-128 Hadamard only):
  *   lo = min(0, min x~), hi = max(0, max x~), s = (hi - lo) / 15,
  *   z = rne(-lo / s), q = clamp(rne(x~ / s) + z, 0, 15);  x~ ~ s (q - z).
- * qa [M][K/2]: plain nibbles, code 2b in the low nibble of byte b (NOT the
- * sign-magnitude form of rw4_quantize_act); sa [M][K/128] fp32 scales s;
+ * qa [M][K/2]: unsigned codes, 8 per 32-bit word w, bit t of code e at
+ * position U[w % 2][e][t] (NOT the signed form of rw4_quantize_act):
+ *   even words: (0,1,2,3) (6,7,8,9) (12,13,14,15) (18,19,20,21)
+ *               (24,25,26,27) (30,31,16,17) (4,5,22,23) (10,11,28,29)
+ *   odd words:  (0,1,18,19) (6,7,24,25) (12,13,30,31) (2,3,4,5)
+ *               (8,9,10,11) (14,15,16,17) (20,21,22,23) (26,27,28,29)
+ * (a word pair opens into the codes' FP6 E2M3 encodings, u/8, as in the
+ * signed form with masks 0xCF3CF3CF, 0x3CF3CF3C, 0x30C330C3); sa [M][K/128] fp32 scales s;
  * za [M][K/128] fp32 zero points (integers 0..15).  A group of zeros gets
  * s = 0, z = 0 and codes 0.  Arguments and errors otherwise as
  * rw4_quantize_act; other transforms: RW4_ERR_UNSUPPORTED. */
@@ -380,9 +393,9 @@ rw4_status rw4_dequantize(const uint8_t* q, const float* s, int64_t M, int64_t K
  * the sum of the per-channel partial products, each multiplied back by its
  * scale) and Figure 4 (3) (the GEMM block equals the quantization group and
  * the block's scale multiplies the block's partial result); the
- * ParoQuant-style article, section 2.3 (one scale per 128-channel group).  Each group's integer dot products are exact (FP8 matrix cores on
- * the codes as exact small values, fp32 accumulation of integers below
- * 2^24); the per-group rescale and the sum over groups are fp32, the output
+ * ParoQuant-style article, section 2.3 (one scale per 128-channel group).
+ * Each group's integer dot products are exact (FP6 matrix cores on the
+ * codes as exact small values, fp32 accumulation of integers below 2^24); the per-group rescale and the sum over groups are fp32, the output
  * is rounded once to y_dtype (F32, or BF16 with round-to-nearest-even).
  * Any M >= 0, N >= 0; K % 128 == 0 and K <= 2^24 (RW4_ERR_SHAPE otherwise).
  *   y [M, N] with leading dimension ldy >= N elements (16-byte aligned

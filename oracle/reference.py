@@ -44,9 +44,12 @@ reason in the design notes):
     (token t, group g) is a_t * s_g;
   * the symmetric quantizer's codes lie in [-7, 7] (scale = max / 7), the
     range the packed form holds;
-  * packed INT4 (the pages fix no layout): sign-magnitude nibbles, 8 codes
-    per little-endian 32-bit word; nibble e (byte e // 2, low nibble for
-    even e) holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 8) in bit 3;
+  * packed INT4 (the pages fix no layout): 4 bits per code, 8 codes per
+    little-endian 32-bit word, each code as sign-magnitude (|c| in 3 bits,
+    sign 1 for negative, zero with sign 0) at bit positions given by a
+    fixed table, one table for even and one for odd words of a row (the
+    layout of the stored form, chosen so that a pair of words opens into
+    16 FP6 E2M3 values with a few masks);
   * 8-bit groups for extreme outliers ([Paro] section 4.1, mixed
     precision): the caller names the 128-channel groups; their codes are
     symmetric with 225 levels, q8 in [-112, 112] (scale max / 112), split
@@ -57,7 +60,7 @@ reason in the design notes):
   * asymmetric (s, z) groups ([Paro] section 2.3; the [RRS] symbol table's
     q = round(x * scale) + offset): min/max round-to-nearest with zero kept
     inside the range, unsigned codes 0..15 with an integer zero point,
-    packed as plain nibbles (code 2b in the low nibble of byte b).
+    packed 4 bits per code by a second pair of position tables.
 
 Shapes: X [M, K] (tokens x input channels), W [K, N], Y = X W [M, N];
 group size g = 128, G = K / g.
@@ -83,7 +86,7 @@ __all__ = [
     "quantize_groups", "quantize_rrs", "rrs_channel_order", "quantize_per_channel", "permute_codes",
     "quantize_groups_asym", "UMAX", "pack_uint4", "unpack_uint4", "dequantize_asym", "weight_code_sums",
     "w4a4_gemm_asym", "Q8MAX", "quantize_groups_mixed", "split_q8", "extend_weight_groups", "mixed_gemm_reference",
-    "pack_int4", "unpack_int4",
+    "pack_int4", "unpack_int4", "SIGNED_LAYOUT", "UNSIGNED_LAYOUT",
     "group_accumulators", "dequant_gemm",
     "round_bf16", "round_output", "dequantize", "round_dequant_output",
     "quantize_act", "pack_weight", "w4a4_gemm", "layer_forward",
@@ -417,65 +420,112 @@ def quantize_per_channel(wt_rows: np.ndarray):
 # Packing
 # --------------------------------------------------------------------------
 
+# Bit positions, inside a little-endian 32-bit word, of the four bits of
+# each of its 8 codes (code e of the word = channel 8 w + e of the row for
+# word w): signed codes (|c| bit 0, bit 1, bit 2, sign), unsigned codes
+# (bits 0-3).  Even words use the first table, odd words the second.  The
+# tables are the layout of the stored form (no page fixes one): read as a
+# pair, words 2j and 2j + 1 hold the 16 codes' FP6 E2M3 encodings (sign,
+# two zero exponent bits, the magnitude as subnormal mantissa: the value
+# c / 8; an unsigned u <= 15 is the E2M3 encoding of u / 8 with a zero
+# sign bit) such that, with f_k the 6-bit encoding of code k, the dense
+# 96-bit string sum_k f_k << 6 k splits into its three 32-bit words as
+#   D0 = W0 & A,  D2 = W1 & C,
+#   D1 = (rot16(V) & E) | (V & ~E),  V = (W0 & ~A) | (W1 & ~C)
+# with masks A = 0xE79E79E7, C = 0x9E79E79E, E = 0x18611861 (signed) and
+# A = 0xCF3CF3CF, C = 0x3CF3CF3C, E = 0x30C330C3 (unsigned).  The tests pin
+# the tables to this identity by brute force.
+SIGNED_LAYOUT = (
+    ((0, 1, 2, 5), (6, 7, 8, 11), (12, 13, 14, 17), (18, 19, 20, 23),
+     (24, 25, 26, 29), (30, 31, 16, 3), (4, 21, 22, 9), (10, 27, 28, 15)),
+    ((0, 17, 18, 5), (6, 23, 24, 11), (12, 29, 30, 1), (2, 3, 4, 7),
+     (8, 9, 10, 13), (14, 15, 16, 19), (20, 21, 22, 25), (26, 27, 28, 31)),
+)
+UNSIGNED_LAYOUT = (
+    ((0, 1, 2, 3), (6, 7, 8, 9), (12, 13, 14, 15), (18, 19, 20, 21),
+     (24, 25, 26, 27), (30, 31, 16, 17), (4, 5, 22, 23), (10, 11, 28, 29)),
+    ((0, 1, 18, 19), (6, 7, 24, 25), (12, 13, 30, 31), (2, 3, 4, 5),
+     (8, 9, 10, 11), (14, 15, 16, 17), (20, 21, 22, 23), (26, 27, 28, 29)),
+)
+
+
+def _pack_words(bits: np.ndarray, layout) -> np.ndarray:
+    """bits [..., K, 4] (0/1) -> bytes [..., K/2] through the position tables."""
+    if bits.shape[-2] % 8:
+        raise ValueError("row length must be a multiple of 8")
+    nw = bits.shape[-2] // 8
+    b = bits.reshape(bits.shape[:-2] + (nw, 8, 4)).astype(np.uint64)
+    words = np.zeros(bits.shape[:-2] + (nw,), dtype=np.uint64)
+    for parity in (0, 1):
+        sel = words[..., parity::2]
+        bp = b[..., parity::2, :, :]
+        for e in range(8):
+            for t in range(4):
+                sel |= bp[..., e, t] << np.uint64(layout[parity][e][t])
+        words[..., parity::2] = sel
+    out = np.empty(words.shape + (4,), dtype=np.uint8)
+    for k in range(4):
+        out[..., k] = (words >> np.uint64(8 * k)) & np.uint64(0xFF)
+    return out.reshape(bits.shape[:-2] + (nw * 4,))
+
+
+def _unpack_words(packed: np.ndarray, layout) -> np.ndarray:
+    """bytes [..., 4 W] -> bits [..., 8 W, 4] through the position tables."""
+    p = np.asarray(packed, dtype=np.uint8)
+    if p.shape[-1] % 4:
+        raise ValueError("packed row length must be a multiple of 4 bytes")
+    nw = p.shape[-1] // 4
+    q = p.reshape(p.shape[:-1] + (nw, 4)).astype(np.uint64)
+    words = q[..., 0] | (q[..., 1] << np.uint64(8)) | (q[..., 2] << np.uint64(16)) | (q[..., 3] << np.uint64(24))
+    bits = np.zeros(p.shape[:-1] + (nw, 8, 4), dtype=np.int64)
+    for parity in (0, 1):
+        w = words[..., parity::2]
+        for e in range(8):
+            for t in range(4):
+                bits[..., parity::2, e, t] = ((w >> np.uint64(layout[parity][e][t])) & np.uint64(1)).astype(np.int64)
+    return bits.reshape(p.shape[:-1] + (nw * 8, 4))
+
+
 def pack_int4(codes: np.ndarray) -> np.ndarray:
     """[R, K] codes in [-7, 7] -> [R, K/2] bytes, K a multiple of 8.
 
-    Sign-magnitude nibbles, 8 codes c_0..c_7 per little-endian 32-bit word
-    (bytes 4w..4w+3 of the row): nibble e of the word (byte e // 2, low
-    nibble for even e) holds |c_e| in its bits 0-2, and its bit 3 holds the
-    sign (1 = negative) of the code before it, c_((e-1) mod 8).  Zero is
-    always stored with sign 0.  (No page fixes a packed layout; this one
-    lets a reader split a word into two 4-byte groups of sign-magnitude
-    bytes with one mask and one rotate + mask.)
+    Sign-magnitude, 4 bits per code, 8 codes c_0..c_7 per little-endian
+    32-bit word (bytes 4w..4w+3 of the row); the bits of code e (|c_e| bit
+    0, 1, 2 and the sign, 1 = negative) sit at SIGNED_LAYOUT[w % 2][e].
+    Zero is always stored with sign 0.
     """
     c = np.asarray(codes)
-    if c.shape[-1] % 8:
-        raise ValueError("row length must be a multiple of 8")
     if c.min(initial=0) < QMIN or c.max(initial=0) > QMAX:
         raise ValueError("code out of the symmetric INT4 range [-7, 7]")
     c = c.astype(np.int64)
-    words = c.reshape(c.shape[:-1] + (c.shape[-1] // 8, 8))
-    mag = np.abs(words)
-    neg = (words < 0).astype(np.int64)
-    nib = mag | (np.roll(neg, 1, axis=-1) << 3)   # nibble e gets the sign of code e-1
-    nib = nib.reshape(c.shape)
-    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    mag = np.abs(c)
+    bits = np.stack([mag & 1, (mag >> 1) & 1, (mag >> 2) & 1, (c < 0).astype(np.int64)], axis=-1)
+    return _pack_words(bits, SIGNED_LAYOUT)
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
     """Inverse of pack_int4: int8 codes [R, 2 * bytes]."""
-    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
-    if p.shape[-1] % 4:
-        raise ValueError("packed row length must be a multiple of 4 bytes")
-    nib = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int64)
-    nib[..., 0::2] = p & 0xF
-    nib[..., 1::2] = p >> 4
-    words = nib.reshape(nib.shape[:-1] + (nib.shape[-1] // 8, 8))
-    mag = words & 7
-    neg = np.roll(words >> 3, -1, axis=-1)          # sign of code e sits in nibble e+1
-    codes = np.where(neg == 1, -mag, mag)
-    return codes.reshape(nib.shape).astype(np.int8)
+    bits = _unpack_words(packed, SIGNED_LAYOUT)
+    mag = bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
+    return np.where(bits[..., 3] == 1, -mag, mag).astype(np.int8)
 
 
 def pack_uint4(codes: np.ndarray) -> np.ndarray:
-    """[R, K] unsigned codes 0..15 -> [R, K/2] bytes: code 2b in the low nibble
-    of byte b, code 2b + 1 in the high nibble (the asymmetric form)."""
+    """[R, K] unsigned codes 0..15 -> [R, K/2] bytes (the asymmetric form), K a
+    multiple of 8: 8 codes per little-endian 32-bit word, bit t of code e at
+    UNSIGNED_LAYOUT[w % 2][e][t]."""
     c = np.asarray(codes)
-    if c.shape[-1] % 2:
-        raise ValueError("row length must be even")
     if c.min(initial=0) < 0 or c.max(initial=0) > UMAX:
         raise ValueError("code out of the unsigned INT4 range [0, 15]")
     c = c.astype(np.int64)
-    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    bits = np.stack([(c >> t) & 1 for t in range(4)], axis=-1)
+    return _pack_words(bits, UNSIGNED_LAYOUT)
 
 
 def unpack_uint4(packed: np.ndarray) -> np.ndarray:
     """Inverse of pack_uint4: uint8 codes [R, 2 * bytes]."""
-    p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
-    out[..., 0::2] = p & 0xF
-    out[..., 1::2] = p >> 4
-    return out
+    bits = _unpack_words(packed, UNSIGNED_LAYOUT)
+    return (bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2) | (bits[..., 3] << 3)).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------

@@ -537,7 +537,7 @@ def prepare_dequantize(q, s, out_dtype=None, out=None) -> Call:
 def quantize_act_asym(t: Transform, x, qa=None, sa=None, za=None):
     """Transform + asymmetric (s, z) INT4 in groups of 128 (block-128 Hadamard).
 
-    Returns (qa uint8 [M, K/2] plain nibbles, sa fp32 [M, K/128], za fp32 [M, K/128])."""
+    Returns (qa uint8 [M, K/2] unsigned codes (stored form of rw4.h), sa fp32 [M, K/128], za fp32 [M, K/128])."""
     return prepare_quantize_act_asym(t, x, qa, sa, za)()
 
 

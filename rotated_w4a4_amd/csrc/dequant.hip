@@ -11,19 +11,12 @@
 // grid's y dimension is the row (in launches of at most 65535 rows), x
 // covers the row's words with blocks of 64 to 256 lanes.  The product
 // code * scale is rounded once to fp32, then to bf16 (round to nearest even)
-// when asked.
-//
-// Each stored word gives its even and odd codes as FP8 E4M3 bytes of value
-// c * 2^-9 (w & 0x87878787, rotr(w, 4) & 0x87878787, as the GEMM reads
-// them); v_cvt_pk_f32_fp8 widens two at a time exactly, and
-// (c * 2^-9) * (s * 2^9) is the exact product c * s rounded once, as long
-// as s * 2^9 is finite (s < 2^119).  Larger scales take the per-code path.
+// when asked.  A word gives its 8 codes as 6-bit sign-magnitude fields
+// (stored_fields: the inverse of the stored form's fold).
 #include "rw4_device.h"
 #include "rw4_internal.h"
 
 namespace rw4 {
-
-typedef float v2f __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ q,
@@ -34,22 +27,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t row = row0 + blockIdx.y;
   const uint32_t w = reinterpret_cast<const uint32_t*>(q + row * (K / 2))[j];
   const float sc = s[row * (K >> log2g) + ((j * 8) >> log2g)];
+  uint32_t lo, hi;
+  stored_fields<true>(w, (j & 1) != 0, lo, hi);
   float v[8];
-  if (sc < 0x1p119f) {
-    const float s9 = sc * 512.0f;  // exact
-    const int ev = int(w & 0x87878787u);                                   // codes 0, 2, 4, 6
-    const int od = int(__builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u);  // codes 1, 3, 5, 7
-    const v2f e0 = __builtin_amdgcn_cvt_pk_f32_fp8(ev, false), e1 = __builtin_amdgcn_cvt_pk_f32_fp8(ev, true);
-    const v2f o0 = __builtin_amdgcn_cvt_pk_f32_fp8(od, false), o1 = __builtin_amdgcn_cvt_pk_f32_fp8(od, true);
-    v[0] = e0[0] * s9; v[1] = o0[0] * s9; v[2] = e0[1] * s9; v[3] = o0[1] * s9;
-    v[4] = e1[0] * s9; v[5] = o1[0] * s9; v[6] = e1[1] * s9; v[7] = o1[1] * s9;
-  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t mag = (w >> (4 * e)) & 7u;
-      const uint32_t neg = (w >> (4 * ((e + 1) & 7) + 3)) & 1u;  // sign of code e: bit 3 of nibble e + 1
-      v[e] = (neg ? -float(mag) : float(mag)) * sc;
-    }
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t f = field6(lo, hi, e);
+    const float mag = float(f & 7u);
+    v[e] = ((f & 32u) ? -mag : mag) * sc;
   }
   if constexpr (BF16) {
     __bf16 h[8];
@@ -86,7 +71,7 @@ hipError_t launch_dequantize(const uint8_t* q, const float* s, int64_t M, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Asymmetric codes (plain nibbles, groups of 128): x_hat = s (q - z), with
+// Asymmetric codes (unsigned stored form, groups of 128): x_hat = s (q - z), with
 // q - z an exact small integer, so the product is rounded once to fp32 (then
 // to bf16 when asked).  One lane per stored word, as dequant_kernel.
 // ---------------------------------------------------------------------------
@@ -101,9 +86,11 @@ __global__ __launch_bounds__(256) void dequant_asym_kernel(const uint8_t* __rest
   const uint32_t w = reinterpret_cast<const uint32_t*>(q + row * (K / 2))[j];
   const int64_t gi = row * (K / kGroup) + (j * 8) / kGroup;
   const float sc = s[gi], zp = z[gi];
+  uint32_t lo, hi;
+  stored_fields<false>(w, (j & 1) != 0, lo, hi);
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float((w >> (4 * e)) & 15u) - zp) * sc;
+  for (int e = 0; e < 8; ++e) v[e] = (float(field6(lo, hi, e)) - zp) * sc;
   if constexpr (BF16) {
     __bf16 h[8];
 #pragma unroll
@@ -138,8 +125,8 @@ hipError_t launch_dequantize_asym(const uint8_t* q, const float* s, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Code sums of packed (sign-magnitude) weight rows per 128-group: the totals
-// an asymmetric activation's zero point multiplies.  One lane per (row,
+// Code sums of packed (signed) weight rows per 128-group: the totals an
+// asymmetric activation's zero point multiplies.  One lane per (row,
 // group); offline, with the weight pack.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __restrict__ qw, int64_t N, int64_t G,
@@ -149,11 +136,12 @@ __global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __
   const uint32_t* w = reinterpret_cast<const uint32_t*>(qw + i * 64);  // row n = i / G, group i % G
   int sum = 0;
   for (int k = 0; k < 16; ++k) {
-    const uint32_t ev = w[k] & 0x87878787u, od = __builtin_amdgcn_alignbit(w[k], w[k], 4) & 0x87878787u;
+    uint32_t lo, hi;
+    stored_fields<true>(w[k], (k & 1) != 0, lo, hi);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t e = (ev >> (8 * b)) & 0xFFu, o = (od >> (8 * b)) & 0xFFu;
-      sum += (e & 0x80u ? -int(e & 7u) : int(e & 7u)) + (o & 0x80u ? -int(o & 7u) : int(o & 7u));
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t f = field6(lo, hi, e);
+      sum += (f & 32u) ? -int(f & 7u) : int(f & 7u);
     }
   }
   cw[i] = float(sum);

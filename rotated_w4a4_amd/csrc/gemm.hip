@@ -1,4 +1,4 @@
-// W4A4 GEMM on the gfx950 FP8 matrix cores.
+// W4A4 GEMM on the gfx950 FP6 matrix cores.
 //
 //   Y[m, n] = sum over 128-wide groups g of sa[m, g] * sw[n, g] * acc[m, n, g]
 //   acc[m, n, g] = sum over k in g of qa[m, k] * qw[n, k]     (exact)
@@ -8,21 +8,22 @@
 // block's partial result; the QuIP#/QTIP page, section 4.2, folds the
 // rotation into the weights so the GEMM itself is a plain product.)
 //
-// Operands.  A 32-bit word of the stored form holds 8 sign-magnitude codes
-// (nibble e = |c_e| | sign(c_{e-1 mod 8}) << 3).  w & 0x87878787 gives the
-// even codes and rotr(w, 4) & 0x87878787 the odd codes, each as a byte
-// sign << 7 | |c|: an FP8 E4M3 subnormal of value c * 2^-9.  The scaled FP8
-// MFMA with E8M0 operand scale 2^9 on both sides therefore returns acc
-// itself, exactly (integer products, partial sums below 128 * 49 < 2^24).
-// Both operands use the same unpack, so the permutation of codes inside a
-// word is the same on both sides and the dot product over the group is
-// unchanged.
+// Operands.  Two words of the stored form (16 codes) open into the dense
+// string of the codes' FP6 E2M3 encodings with three masks and one 16-bit
+// rotation (rw4_device.h): a signed code c becomes the subnormal c / 8, an
+// unsigned code u (asymmetric activations) the value u / 8.  The scaled
+// MFMA with format FP6 E2M3 on both sides and E8M0 operand scale 2^3 on
+// both therefore returns acc itself, exactly (integer products, partial
+// sums below 128 * 15 * 7 < 2^24).  Both operands open the same way, so
+// the order of codes inside an operand is the same on both sides and the
+// dot product over the group is unchanged.  FP6 operands take 6 registers
+// and issue at about 1.5 times the FP8 rate.
 //
 // Kernels:
 //   gemm_f8_kernel     large products: 128 x 128 block tiles, 4 waves of 64 x 64
 //                      (gemm_f8p_kernel: the same for 128-wide groups, with
 //                      the LDS reads software-pipelined),
-//                      v_mfma_scale_f32_32x32x64_f8f6f4 (2 per group per
+//                      v_mfma_scale_f32_32x32x64_f8f6f4 on FP6 (2 per group per
 //                      32 x 32 tile); the scale products sa * sw of a tile
 //                      come from one v_mfma_f32_32x32x16_bf16 on a 3-way
 //                      bf16 split of each scale, split once per block and
@@ -50,26 +51,30 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kE8Scale = 127 + 9;  // E8M0 encoding of 2^9
+constexpr int kF6Scale = 127 + 3;  // E8M0 encoding of 2^3: FP6 code c / 8 times 2^3 is c
+constexpr int kF6 = 2;             // MFMA operand format FP6 E2M3
 
-__device__ __forceinline__ uint32_t f8_even(uint32_t w) { return w & 0x87878787u; }
-__device__ __forceinline__ uint32_t f8_odd(uint32_t w) {
-  return __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;
+// 4 stored words (32 codes, two word pairs) -> the 6-register FP6 operand
+// (the last two registers of the vector are not read by an FP6 MFMA).
+template <bool SIGNED>
+__device__ __forceinline__ void open_pair(uint32_t w0, uint32_t w1, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC, kE = SIGNED ? kSgnE : kUnsE;
+  // six instructions per word pair; written out because the compiler
+  // otherwise splits the two combining steps into three
+  const uint32_t t = w1 & ~kC;
+  uint32_t v;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(v) : "v"(w0), "s"(~kA), "v"(t));  // (w0 & ~A) | t
+  const uint32_t r = __builtin_amdgcn_alignbit(v, v, 16);
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d1) : "s"(kE), "v"(r), "v"(v));  // (r & E) | (v & ~E)
+  d0 = w0 & kA;
+  d2 = w1 & kC;
 }
-// 4 stored words (32 codes) -> the 8-dword FP8 operand
-__device__ __forceinline__ v8i f8_operand(v4u w) {
-  return v8i{int(f8_even(w[0])), int(f8_odd(w[0])), int(f8_even(w[1])), int(f8_odd(w[1])),
-             int(f8_even(w[2])), int(f8_odd(w[2])), int(f8_even(w[3])), int(f8_odd(w[3]))};
-}
-
-// 4 words of plain unsigned nibbles (asymmetric codes 0..15) -> the FP8
-// operand in the same code order as f8_operand.  The E4M3 byte of u * 2^-9
-// is u itself for every u in 0..15 (subnormals 0..7, exponent field 1 for
-// 8..15), so the bytes are the nibbles.
-__device__ __forceinline__ v8i f8u_operand(v4u w) {
-  return v8i{int(w[0] & 0x0F0F0F0Fu), int((w[0] >> 4) & 0x0F0F0F0Fu), int(w[1] & 0x0F0F0F0Fu),
-             int((w[1] >> 4) & 0x0F0F0F0Fu), int(w[2] & 0x0F0F0F0Fu), int((w[2] >> 4) & 0x0F0F0F0Fu),
-             int(w[3] & 0x0F0F0F0Fu), int((w[3] >> 4) & 0x0F0F0F0Fu)};
+template <bool SIGNED = true, class W>
+__device__ __forceinline__ v8i f6_operand(const W& w) {
+  uint32_t d[6];
+  open_pair<SIGNED>(uint32_t(w[0]), uint32_t(w[1]), d[0], d[1], d[2]);
+  open_pair<SIGNED>(uint32_t(w[2]), uint32_t(w[3]), d[3], d[4], d[5]);
+  return v8i{int(d[0]), int(d[1]), int(d[2]), int(d[3]), int(d[4]), int(d[5]), 0, 0};
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -332,8 +337,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
   };
 
   // per-lane LDS read bases (group buffer 0).  Lanes 32..63 supply K slots
-  // 8..15 of the bf16 scale-product MFMA: their row operands are zeroed in
-  // registers, their column operands are finite values that multiply zero.
+  // 8..15 of the bf16 scale-product MFMA with the same split operands as
+  // lanes 0..31 (the product comes out doubled; see the epilogue).
   const int frow = lane & 31, h = lane >> 5;
   uint32_t ba0, ba1, bb0, bb1, bsa, bsb;
   {
@@ -352,8 +357,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
     bsa = s0 + (wm * 64 + frow) * 16;
     bsb = s0 + (wn * 64 + frow) * 16;  // + 2048 (column operands) in the read offsets
   }
-  const uint32_t keep = h ? 0u : 0xFFFFFFFFu;
-
   float yacc[2][2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -363,13 +366,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
       for (int r = 0; r < 16; ++r) yacc[i][j][r] = 0.0f;
 
   // Scale products of the four 32 x 32 tiles from the split operands ps
-  // (rows, rows, columns, columns), then y += acc * p.
+  // (rows, rows, columns, columns), then y += acc * p.  Both lane halves
+  // supply the same split operands (K slots 0-7 and 8-15), so the bf16
+  // MFMA returns 2 sa sw; the integer MFMAs take the B-side scale 2^2
+  // instead of 2^3 and return acc / 2 (exact), so the product is unchanged.
   v16f acc[2][2];
   auto epilogue = [&](v4u (&ps)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
     // tile by tile, one tile ahead of the accumulation (the scheduling
     // barriers keep at most two product tiles live)
     auto prod = [&](int t) {
@@ -416,16 +418,16 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
         lds_read_half0<tile_off(q)>(fr, ba1, bb1);  // K-half 1 fragments only
       v8i oa[2], ob[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) oa[i] = f8_operand(fr[i]);
+      for (int i = 0; i < 2; ++i) oa[i] = f6_operand(fr[i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) ob[j] = f8_operand(fr[2 + j]);
+      for (int j = 0; j < 2; ++j) ob[j] = f6_operand(fr[2 + j]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const v16f c = (init && ks == 0) ? v16f{} : acc[i][j];
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], c, 0, 0, 0, kE8Scale,
-                                                                     0, kE8Scale);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], c, kF6, kF6, 0, kF6Scale,
+                                                                     0, kF6Scale - 1);
         }
       // keep each half's unpack and MFMAs together (bounds register use)
       __builtin_amdgcn_sched_barrier(0);
@@ -447,15 +449,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
         lds_read_half1<tile_off(q), split_off64(q, 1)>(fr, ps, ba1, bb1, bsa, bsb);
       v8i oa[2], ob[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) oa[i] = f8_operand(fr[i]);
+      for (int i = 0; i < 2; ++i) oa[i] = f6_operand(fr[i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) ob[j] = f8_operand(fr[2 + j]);
+      for (int j = 0; j < 2; ++j) ob[j] = f6_operand(fr[2 + j]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], v16f{}, 0, 0, 0, kE8Scale, 0,
-                                                                     kE8Scale);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], v16f{}, kF6, kF6, 0, kF6Scale, 0,
+                                                                     kF6Scale - 1);
       __builtin_amdgcn_sched_barrier(0);
       epilogue(ps);
     }
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f8_kernel(const uint8_t* __restri
 constexpr int kStageTileBytes = 2 * kGroupBytes;        // A and B tiles of two groups
 constexpr int kStageSplitBytes = 2 * kSplitGroupBytes;  // their split scale operands
 
-// ASYM: plain-nibble activation codes with zero points za [M][G] and the
+// ASYM: unsigned activation codes with zero points za [M][G] and the
 // weight code sums cw [N][G]: every group's accumulators start at
 // -za cw (exact integers, from a bf16 MFMA on the spare K slots 6 and 7 of
 // the split scale operands: -za twice against cw split into two bf16
@@ -694,7 +696,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     osa = (wm * 64 + frow) * 16;
     osb = 2048 + (wn * 64 + frow) * 16;
   }
+  // Symmetric codes: both lane halves supply the same split operands, the
+  // bf16 MFMA returns 2 sa sw and the integer MFMAs return acc / 2 (B-side
+  // scale 2^2, exact).  ASYM: the lanes of K slots 8-15 zero their row
+  // operands (slots 6-7 carry the zero-point products, which must count
+  // once), and acc keeps its scale.
   const uint32_t keep = h ? 0u : 0xFFFFFFFFu;
+  constexpr int kBScale = ASYM ? kF6Scale : kF6Scale - 1;
   auto rd = [](const uint8_t* base, uint32_t off) { return *reinterpret_cast<const v4u*>(base + off); };
   auto read_half = [&](const uint8_t* T, int q, uint32_t oa, uint32_t ob, v4u (&f)[4]) {
     const uint8_t* b = T + q * kGroupBytes;
@@ -723,15 +731,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
   auto mfma_half = [&](const v4u (&f)[4], bool init) {
     v8i oa[2], ob[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) oa[i] = ASYM ? f8u_operand(f[i]) : f8_operand(f[i]);
+    for (int i = 0; i < 2; ++i) oa[i] = ASYM ? f6_operand<false>(f[i]) : f6_operand(f[i]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ob[j] = f8_operand(f[2 + j]);
+    for (int j = 0; j < 2; ++j) ob[j] = f6_operand(f[2 + j]);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], init ? v16f{} : acc[i][j], 0, 0,
-                                                                   0, kE8Scale, 0, kE8Scale);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa[i], ob[j], init ? v16f{} : acc[i][j], kF6, kF6,
+                                                                   0, kF6Scale, 0, kBScale);
   };
   // scale products of the four 32 x 32 tiles (bf16 MFMA on the splits), then y += acc * p
   // ASYM: the accumulators of a group start at -za cw (K slots 6 and 7 only)
@@ -745,11 +753,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
                                                            v16f{}, 0, 0, 0);
   };
   auto epilogue = [&](v4u (&ps)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
     if constexpr (ASYM) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ps[i][3] = 0u;
     }
@@ -937,7 +945,7 @@ struct SmallStage {
   v4u b[CT][C::NS];
 };
 
-// ASYM (GSZ = 128): plain-nibble activation codes with zero points za and
+// ASYM (GSZ = 128): unsigned activation codes with zero points za and
 // weight code sums cw, staged like sa and sw; each product starts at
 // -za cw.
 template <bool BF16, int GSZ, int MT, int CT, bool ASYM = false>
@@ -1061,7 +1069,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
   };
   auto a_frag = [&](int mt, int gl) {
     const v4u w = As[(mt * 16 + am) * (C::AROW + 1) + gl * 4 + part];
-    return ASYM ? f8u_operand(w) : f8_operand(w);
+    return ASYM ? f6_operand<false>(w) : f6_operand(w);
   };
   // ASYM: the product of tile (ct, mt) in scale column cl starts at -za cw
   auto acc_init = [&](int ct, int mt, int cl) {
@@ -1078,7 +1086,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
 #pragma unroll
       for (int p = 0; p < C::P; ++p)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) b[p][ct] = f8_operand(S.b[ct][ns + p]);
+        for (int ct = 0; ct < CT; ++ct) b[p][ct] = f6_operand(S.b[ct][ns + p]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if constexpr (GSZ == 64) {
@@ -1089,8 +1097,8 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
               apply(ct, mt,
-                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b[0][ct], v4f{}, 0, 0, 0, kE8Scale, 0,
-                                                                     kE8Scale),
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, b[0][ct], v4f{}, kF6, kF6, 0, kF6Scale, 0,
+                                                                     kF6Scale),
                     2 * gl + h);
           }
         } else {
@@ -1100,10 +1108,10 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_small_kernel(const uint8_t
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0][ct], acc_init(ct, mt, gl / C::P),
-                                                                       0, 0, 0, kE8Scale, 0, kE8Scale);
+                                                                       kF6, kF6, 0, kF6Scale, 0, kF6Scale);
             if constexpr (C::P == 2)
-              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], b[1][ct], acc, 0, 0, 0, kE8Scale, 0,
-                                                                     kE8Scale);
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[1], b[1][ct], acc, kF6, kF6, 0, kF6Scale, 0,
+                                                                     kF6Scale);
             apply(ct, mt, acc, gl / C::P);
           }
         }
@@ -1318,7 +1326,7 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
       const int ns = q & 1;
       const int64_t m = q >> 1;
       const int gl = wave * C::NS + ns;
-      const uint32_t packed = encode8_rcp(v, mx, flip);
+      const uint32_t packed = encode8_rcp(v, mx, flip, (word & 1) != 0);
       if (m < M && g0 + ns < SL) {
         *reinterpret_cast<uint32_t*>(Ab + gl * 64 + m * (C::AROW + 1) * 16 + word * 4) = packed;
         if (sub == 0) saT[gl * 16 + m] = mx * post;
@@ -1351,13 +1359,13 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
       const int gl = wave * C::NS + ns;
       v8i b[CT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) b[ct] = f8_operand(S.b[ct][ns]);
-      const v8i a = f8_operand(As[am * (C::AROW + 1) + gl * 4 + part]);
+      for (int ct = 0; ct < CT; ++ct) b[ct] = f6_operand(S.b[ct][ns]);
+      const v8i a = f6_operand(As[am * (C::AROW + 1) + gl * 4 + part]);
       const v4f s4 = *reinterpret_cast<const v4f*>(saT + gl * 16 + part * 4);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const v4f acc =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[ct], v4f{}, 0, 0, 0, kE8Scale, 0, kE8Scale);
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[ct], v4f{}, kF6, kF6, 0, kF6Scale, 0, kF6Scale);
         const float swv = swT[gl * (16 * CT) + ct * 16 + am];
 #pragma unroll
         for (int r = 0; r < 4; ++r) yv[ct][r] = fmaf(acc[r], s4[r] * swv, yv[ct][r]);

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     if constexpr (GS == 256) m = max_x<16>(m);
     uint32_t b[8];
     encode<8>(v[u], m, b, flip);
-    const uint32_t packed = pack8_bits(b);
+    const uint32_t packed = pack8_bits(b, (sub & 1) != 0);
     const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
     if (grp < G) {
       reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
@@ -169,7 +169,7 @@ struct RawRow {
 // Sylvester lane f(l), and f keeps lane bit 3), a 256-group two adjacent
 // rows (lanes l and l ^ 16).
 // ASYM (GS = 128 only): the asymmetric (s, z) encoder (encode8_asym) with
-// plain nibbles; zs receives the zero points as floats.
+// the unsigned stored form; zs receives the zero points as floats.
 template <bool BF16, bool SIGNED, int D, int GS, bool ASYM = false>
 __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                              int64_t rows, int64_t G, int64_t Q, int64_t R,
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   // the row's buffer range (their loads read zeros, their stores vanish)
   const uint32_t x_off = uint32_t((grp * kGroup + sub * 8) * ES);
   const uint32_t q_off = uint32_t(grp * 64 + h128_lane_word(sub) * 4);
+  const bool odd = (h128_lane_word(sub) & 1) != 0;  // word parity selects the stored form's table
   const int64_t GSN = G * kGroup / GS;  // scale columns per row
   uint32_t s_off;
   if constexpr (GS == 64)
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
         hi = row16_max_dpp(hi);
         nlo = row16_max_dpp(nlo);
         uint32_t z;
-        const uint32_t packed = encode8_asym(v, hi, nlo, z);
+        const uint32_t packed = encode8_asym(v, hi, nlo, z, odd);
         const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
         const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, live ? G * 4 : 0);
         const __amdgpu_buffer_rsrc_t rz = buf_rsrc(zs + row * G, live ? G * 4 : 0);
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
           m = fmaxf(m, t);
         }
       }
-      const uint32_t packed = encode8_rcp(v, m, flip);
+      const uint32_t packed = encode8_rcp(v, m, flip, odd);
       const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
       const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * GSN, live ? GSN * 4 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256) void quant_rowh_kernel(Src src, int64_t M, int
         const float m = group_absmax<E>(v, c);
         uint32_t b[8];
         encode<8>(&v[c * 8], m, b);
-        qrow[c * 64 + lane] = pack8_bits(b);
+        qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
         if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
       }
     } else {
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(256) void quant_rowh_kernel(Src src, int64_t M, int
       for (int c = 0; c < NC; ++c) {
         uint32_t b[8];
         encode<8>(&v[c * 8], m, b);
-        qrow[c * 64 + lane] = pack8_bits(b);
+        qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
         if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
       }
     }
@@ -691,7 +692,7 @@ __global__ __launch_bounds__(256) void quant_rrs_full_kernel(const void* __restr
       uint32_t b[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[c][e], k);
-      __builtin_amdgcn_raw_buffer_store_b32(pack8_bits(b), rq, int(q_off[c]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(pack8_bits(b, (h128_lane_word(lane & 15) & 1) != 0), rq, int(q_off[c]), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a_t * (sg[c] * post_scale)), rs, int(s_off[c]), 0, 0);
     }
   }
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
     float xv[2] = {x0, x1};
     uint32_t b[2];
     encode<2>(xv, m, b);
-    const uint32_t byte = pack2_bits_quad(b[0], b[1]);
+    const uint32_t byte = pack2_bits_quad(b[0], b[1], lane & 3, ((lane >> 2) & 1) != 0);
     const int64_t row = row0 + r;
     q[row * (G * 64) + grp * 64 + lane] = uint8_t(byte);
     if (lane == 0) s[row * G + grp] = m * (1.0f / 7.0f);
@@ -959,7 +960,7 @@ __global__ __launch_bounds__(256) void quant_rrs_order_kernel(Src src, int64_t M
     for (int c = 0; c < NC; ++c) {
       uint32_t b[8];
       encode<8>(&v[c * 8], m, b);
-      qrow[c * 64 + lane] = pack8_bits(b);
+      qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
       if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
     }
   }
@@ -997,70 +998,64 @@ __global__ __launch_bounds__(256) void quant_row_perchannel_kernel(Src src, int6
     for (int c = 0; c < NC; ++c) {
       uint32_t b[8];
       encode<8>(&v[c * 8], m, b);
-      qrow[c * 64 + lane] = pack8_bits(b);
+      qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
       if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
     }
   }
 }
 
 // Codes of every row taken in channel order: out[r, j] = code(q[r], order[j]).
-// A block walks rows four at a time: their stored words are staged in LDS
-// together, and every thread builds whole output words (8 codes) of all four
-// rows.  A thread's output words and their source positions are the same
-// in every row, so it reads the order once (K <= 8192: at most 4 output
-// words of 8 codes per thread).  The stored form puts the sign of code e in
-// bit 3 of nibble (e + 1) mod 8 of its word.
+// A block walks rows four at a time: their stored words are decoded into
+// LDS as one signed byte per code, then every thread gathers whole output
+// words (8 codes) of all four rows and encodes them in the stored form.  A
+// thread's output words and their source channels are the same in every
+// row, so it reads the order once (K <= 8192: at most 4 output words of 8
+// codes per thread).
 constexpr int kPermuteRows = 4;
 __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t K,
                                                             const int32_t* __restrict__ order,
                                                             uint8_t* __restrict__ out) {
-  extern __shared__ uint32_t pc_smem[];  // kPermuteRows rows of K / 8 stored words
+  extern __shared__ int8_t pc_codes[];  // kPermuteRows rows of K codes
   const int W = int(K / 8);
-  // source word and nibble of this thread's output codes (word i = threadIdx.x + 256 u)
-  uint16_t srcw[4][8];
-  uint8_t srcn[4][8];
+  // source channel of this thread's output codes (word i = threadIdx.x + 256 u)
+  uint16_t src[4][8];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = int(threadIdx.x) + 256 * u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t k = i < W ? min(uint32_t(order[i * 8 + e]), uint32_t(K - 1)) : 0u;  // clamped into the row
-      srcw[u][e] = uint16_t(k >> 3);
-      srcn[u][e] = uint8_t(k & 7);
-    }
+    for (int e = 0; e < 8; ++e)
+      src[u][e] = uint16_t(i < W ? min(uint32_t(order[i * 8 + e]), uint32_t(K - 1)) : 0u);  // clamped into the row
   }
   for (int64_t row0 = int64_t(blockIdx.x) * kPermuteRows; row0 < rows; row0 += int64_t(gridDim.x) * kPermuteRows) {
     const int nr = int(rows - row0 < kPermuteRows ? rows - row0 : kPermuteRows);
-    __syncthreads();  // the previous rows' words consumed
+    __syncthreads();  // the previous rows' codes consumed
     for (int r = 0; r < nr; ++r) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(q + (row0 + r) * (K / 2));
-      for (int i = threadIdx.x; i < W; i += blockDim.x) pc_smem[r * W + i] = src[i];
+      const uint32_t* words = reinterpret_cast<const uint32_t*>(q + (row0 + r) * (K / 2));
+      for (int i = threadIdx.x; i < W; i += blockDim.x) {
+        uint32_t lo, hi;
+        stored_fields<true>(words[i], (i & 1) != 0, lo, hi);
+        uint32_t c4[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t f = field6(lo, hi, e);
+          const uint32_t c = (f & 32u) ? uint32_t(-int(f & 7u)) & 0xFFu : (f & 7u);
+          c4[e >> 2] |= c << (8 * (e & 3));
+        }
+        *reinterpret_cast<uint2*>(pc_codes + r * K + i * 8) = make_uint2(c4[0], c4[1]);
+      }
     }
     __syncthreads();
     for (int r = 0; r < nr; ++r) {
-      const uint32_t* words = pc_smem + r * W;
+      const int8_t* codes = pc_codes + r * K;
       uint32_t* dst = reinterpret_cast<uint32_t*>(out + (row0 + r) * (K / 2));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = int(threadIdx.x) + 256 * u;
         if (i >= W) break;
-        int code[8];
+        uint32_t b[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wd = words[srcw[u][e]];
-          const int n = srcn[u][e];
-          const int mag = int((wd >> (4 * n)) & 7u);
-          const int neg = int((wd >> (4 * ((n + 1) & 7) + 3)) & 1u);
-          code[e] = neg ? -mag : mag;
-        }
-        uint32_t o = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t mag = uint32_t(code[e] < 0 ? -code[e] : code[e]);
-          const uint32_t prev_neg = code[(e + 7) & 7] < 0 ? 8u : 0u;
-          o |= (mag | prev_neg) << (4 * e);
-        }
-        dst[i] = o;
+        for (int e = 0; e < 8; ++e) b[e] = kRoundMagicBits + uint32_t(int(codes[src[u][e]]));
+        dst[i] = pack8_bits(b, (i & 1) != 0);
       }
     }
   }
@@ -1464,7 +1459,7 @@ hipError_t launch_permute_codes(const uint8_t* q, int64_t rows, int64_t K, const
                                 hipStream_t st) {
   const int64_t batches = (rows + kPermuteRows - 1) / kPermuteRows;
   const int64_t grid = batches < 1024 ? batches : 1024;
-  const int lds = int(kPermuteRows * (K / 8) * 4);
+  const int lds = int(kPermuteRows * K);
   hipLaunchKernelGGL(permute_codes_kernel, dim3(unsigned(grid)), dim3(256), lds, st, q, rows, K, order, out);
   return hipGetLastError();
 }
@@ -1553,8 +1548,9 @@ __global__ __launch_bounds__(256) void quant_h128_mixed_kernel(const void* __res
   const int word = h128_lane_word(sub);
   uint8_t* const qrow = q + row * (Gx * 64);
   float* const srow = s + row * Gx;
+  const bool odd = (word & 1) != 0;
   if (slot < 0 || slot >= n8) {
-    const uint32_t packed = encode8_rcp(v, m, flip);
+    const uint32_t packed = encode8_rcp(v, m, flip, odd);
     if (valid) {
       *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = packed;
       if (sub == 0) srow[grp] = m * post4;
@@ -1577,8 +1573,8 @@ __global__ __launch_bounds__(256) void quant_h128_mixed_kernel(const void* __res
     bh[e] = kRoundMagicBits + uint32_t(h);
     bl[e] = kRoundMagicBits + uint32_t(q8 - 15 * h);
   }
-  *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = pack8_bits(bh);
-  *reinterpret_cast<uint32_t*>(qrow + (G + slot) * 64 + word * 4) = pack8_bits(bl);
+  *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = pack8_bits(bh, odd);
+  *reinterpret_cast<uint32_t*>(qrow + (G + slot) * 64 + word * 4) = pack8_bits(bl, odd);
   if (sub == 0) {
     srow[grp] = m * post8h;
     srow[G + slot] = m * post8l;

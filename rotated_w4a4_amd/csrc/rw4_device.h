@@ -181,46 +181,127 @@ __device__ __forceinline__ uint32_t rne_code_bits(float v, float inv) {
   return __float_as_uint(fmaf(v, inv, kRoundMagic));
 }
 
-// Two's-complement nibbles from 8 magic-rounded float bit patterns (code e
-// at nibble e): Horner sum of the raw patterns, then subtract the magic
-// constant from every nibble while adding 8 (offset binary, no borrows),
-// then flip the nibble sign bits.
-__device__ __forceinline__ uint32_t pack8_twos(const uint32_t b[8]) {
-  uint32_t acc = b[7];
+// ---------------------------------------------------------------------------
+// Stored form of the codes: 4 bits per code, 8 codes per 32-bit word (code
+// e of word w = channel 8 w + e of the row), at bit positions fixed by one
+// table for even and one for odd words.  Its purpose: the GEMM reads codes
+// as FP6 E2M3 values (the gfx950 FP6 matrix-core rate is about 1.5x the
+// FP8 rate), whose encodings are 6 bits wide.  Let f_k be the 6-bit E2M3
+// encoding of code k of a word pair (words 2j, 2j + 1; 16 codes): signed
+// codes c as the subnormal c / 8 (sign bit 5, exponent bits 3-4 zero,
+// mantissa |c| in bits 0-2), unsigned codes u (0..15) as u / 8, whose
+// encoding is u itself.  The stored words W0, W1 of the pair are the dense
+// 96-bit string X = sum_k f_k << 6 k folded into 64 bits: with masks A, C
+// and E (per code kind, below) and rot16 a rotation by 16 bits,
+//   X[0:32]  = W0 & A
+//   X[64:96] = W1 & C
+//   X[32:64] = (rot16(V) & E) | (V & ~E),  V = (W0 & ~A) | (W1 & ~C).
+// A marks the bits of X[0:32] that can be nonzero (fields 0-4 and the low
+// bits of field 5), C those of X[64:96]; the bits of X[32:64] that can be
+// nonzero are exactly the zero positions of the other two words, half of
+// them moved by 16 bits.  Each word depends on its own 8 codes only: W0
+// holds fields 0-7 (X bits 0-47), W1 fields 8-15 (X bits 48-95).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSgnA = 0xE79E79E7u, kSgnC = 0x9E79E79Eu, kSgnE = 0x18611861u;
+constexpr uint32_t kUnsA = 0xCF3CF3CFu, kUnsC = 0x3CF3CF3Cu, kUnsE = 0x30C330C3u;
+
+// Stored word from the 48-bit field string of its 8 codes (lo: bits 0-31,
+// hi: bits 32-47): an even word keeps lo's A bits and takes the field bits
+// 32-47 into its spare (~A) positions, in place or moved up by 16; an odd
+// word holds X bits 48-95 = (hi:lo) >> 16 at its C positions and lo's low
+// half in its spare (~C) positions.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t stored_word(uint32_t lo, uint32_t hi, bool odd) {
+  constexpr uint32_t kZ0 = ~(SIGNED ? kSgnA : kUnsA), kZ2 = ~(SIGNED ? kSgnC : kUnsC);
+  const uint32_t src = odd ? lo : hi;
+  const uint32_t dup = __builtin_amdgcn_perm(src, src, 0x01000100u);  // low half in both halves
+  const uint32_t base = __builtin_amdgcn_alignbit(hi, lo, odd ? 16u : 0u);
+  const uint32_t z = odd ? kZ2 : kZ0;
+  return (dup & z) | (base & ~z);
+}
+
+// The 48-bit field string of a stored word's 8 codes (the inverse of
+// stored_word): lo = fields 0-4 and bits 0-1 of field 5, hi = the rest.
+template <bool SIGNED>
+__device__ __forceinline__ void stored_fields(uint32_t w, bool odd, uint32_t& lo, uint32_t& hi) {
+  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC, kE = SIGNED ? kSgnE : kUnsE;
+  const uint32_t v = w & (odd ? ~kC : ~kA);
+  const uint32_t d1 = (__builtin_amdgcn_alignbit(v, v, 16) & kE) | (v & ~kE);  // X[32:64] (this word's half)
+  if (odd) {
+    const uint32_t d2 = w & kC;
+    lo = __builtin_amdgcn_alignbit(d2, d1, 16);
+    hi = d2 >> 16;
+  } else {
+    lo = w & kA;
+    hi = d1 & 0xFFFFu;
+  }
+}
+// field k (0-7) of a 48-bit field string
+__device__ __forceinline__ uint32_t field6(uint32_t lo, uint32_t hi, int k) {
+  return k < 5 ? (lo >> (6 * k)) & 63u : k == 5 ? (lo >> 30) | ((hi & 15u) << 2) : (hi >> (6 * k - 32)) & 63u;
+}
+
+// Sign-magnitude 6-bit fields from 6-bit two's-complement codes offset by
+// 32 (t: codes c + 32 in [25, 39], no field borrows from the next): with
+// p = t ^ 32 (two's complement), a negative field is 0b111xxx with xxx =
+// 8 - |c|; clearing bits 3-4 and replacing xxx by its negation mod 8 gives
+// 0b100 |c|, the E2M3 encoding of c / 8.  ones: bit 0 of every field.
+__device__ __forceinline__ uint32_t fp6_sign_magnitude(uint32_t t, uint32_t ones) {
+  const uint32_t p = t ^ (ones << 5);
+  const uint32_t n7 = (p >> 3) & (ones * 7u);        // 7 in negative fields
+  const uint32_t q = p & ~(ones * 24u);               // bits 3-4 cleared
+  return (q ^ n7) + (n7 & ones);                      // xxx -> (~xxx & 7) + 1 = |c|
+}
+
+// Fields of 6-bit stride from 8 magic-rounded float patterns (code e in the
+// low bits of b[e]): Horner sums of the raw patterns over fields 0-5 (lo,
+// field 5 cut at bit 32) and 5-7 (hi), then the magic constant removed
+// from every field with 32 added (offset binary, no borrows).
+constexpr uint32_t f6_rep(uint32_t v, int n) {
+  uint32_t r = 0;
+  for (int k = 0; k < n; ++k) r += v << (6 * k);
+  return r;
+}
+__device__ __forceinline__ void horner6(const uint32_t b[8], uint32_t& lo, uint32_t& hi) {
+  lo = b[5];
 #pragma unroll
-  for (int e = 6; e >= 0; --e) acc = (acc << 4) + b[e];
-  constexpr uint32_t kOnes = 0x11111111u;
-  constexpr uint32_t kFix = (8u - kRoundMagicBits) * kOnes;  // mod 2^32
-  return (acc + kFix) ^ 0x88888888u;
+  for (int e = 4; e >= 0; --e) lo = (lo << 6) + b[e];
+  hi = (((b[7] << 6) + b[6]) << 6) + b[5];
 }
 
-// Stored form of 8 codes (one 32-bit word): sign-magnitude nibbles, nibble e
-// = |c_e| in bits 0-2 and the sign of c_{(e-1) mod 8} in bit 3.  From the
-// two's-complement nibbles t: s = the nibble sign bits; |c| per nibble is
-// (t XOR 0xF) + 1 where negative, done for all nibbles at once (|c| <= 7, so
-// nothing carries); the signs then move up one nibble, the top one wrapping
-// to nibble 0.  Zero is stored with sign 0.
-__device__ __forceinline__ uint32_t twos_to_stored(uint32_t t) {
-  const uint32_t s = t & 0x88888888u;
-  const uint32_t one = s >> 3;
-  const uint32_t mag = (t ^ ((one << 4) - one)) + one;
-  return mag | __builtin_amdgcn_alignbit(s, s, 28);  // rotate left by 4
+// Stored word of 8 signed codes from their magic-rounded patterns; odd:
+// the word's index in the row is odd.
+__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8], bool odd) {
+  uint32_t lo, hi;
+  horner6(b, lo, hi);
+  constexpr uint32_t kOff = 32u - kRoundMagicBits;  // mod 2^32
+  const uint32_t slo = fp6_sign_magnitude(lo + f6_rep(kOff, 6), f6_rep(1u, 5));
+  const uint32_t shi = fp6_sign_magnitude(hi + f6_rep(kOff, 3), f6_rep(1u, 3));
+  return stored_word<true>((slo & 0x3FFFFFFFu) | (shi << 30), shi >> 2, odd);
 }
-
-__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8]) { return twos_to_stored(pack8_twos(b)); }
+// Stored word of 8 unsigned codes (0..15) from their magic-rounded patterns.
+__device__ __forceinline__ uint32_t pack8_ubits(const uint32_t b[8], bool odd) {
+  uint32_t lo, hi;
+  horner6(b, lo, hi);
+  constexpr uint32_t kOff = 0u - kRoundMagicBits;
+  return stored_word<false>(lo + f6_rep(kOff, 6), (hi + f6_rep(kOff, 3)) >> 2, odd);
+}
 
 // One byte of the stored form for codes 2l, 2l+1 of a word, held by lane l of
-// a quad (lanes 4w..4w+3 hold word w): the low nibble takes the sign of code
-// 2l-1, i.e. of the high code of the previous lane of the quad (cyclically).
-__device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1) {
-  constexpr uint32_t kFix2 = (8u - kRoundMagicBits) * 0x11u;
-  const uint32_t t = ((((b1 << 4) + b0) + kFix2) ^ 0x88u) & 0xFFu;  // two's complement byte
-  const uint32_t s = t & 0x88u;
-  const uint32_t one = s >> 3;
-  const uint32_t mag = (t ^ ((one << 4) - one)) + one;
-  // lane i of each quad reads lane (i + 3) % 4: quad_perm [3, 0, 1, 2]
-  const uint32_t prev = uint32_t(__builtin_amdgcn_mov_dpp(int(s), 0x93, 0xF, 0xF, false));
-  return (mag | ((s & 0x08u) << 4) | ((prev >> 4) & 0x08u)) & 0xFFu;
+// a quad (lanes 4w..4w+3 hold word w, odd: w is odd): the quad's 8 patterns
+// are gathered into every lane (quad broadcasts), each lane packs the whole
+// word and keeps byte l.
+__device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1, int l, bool odd) {
+  uint32_t b[8];
+  b[0] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0x00, 0xF, 0xF, false));
+  b[1] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0x00, 0xF, 0xF, false));
+  b[2] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0x55, 0xF, 0xF, false));
+  b[3] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0x55, 0xF, 0xF, false));
+  b[4] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0xAA, 0xF, 0xF, false));
+  b[5] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0xAA, 0xF, 0xF, false));
+  b[6] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0xFF, 0xF, 0xF, false));
+  b[7] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0xFF, 0xF, 0xF, false));
+  return (pack8_bits(b, odd) >> (8 * l)) & 0xFFu;
 }
 
 __device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f ? num / m : 0.0f; }
@@ -311,7 +392,7 @@ __device__ __forceinline__ float row16_max_dpp(float m) {
 // ~1e-6 of a code step at most.  (The reciprocal flushes subnormal
 // results, so it is taken of m / 7, whose reciprocal is normal for every
 // finite m >= 2^-100; 1 / m is not, for m above 2^126.)
-__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float flip) {
+__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float flip, bool odd) {
   float mm = m;
   if (__builtin_amdgcn_ballot_w64(m > 0.0f && m < kTinyMax) != 0) {
     if (m > 0.0f && m < kTinyMax) {
@@ -324,19 +405,18 @@ __device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float fl
   uint32_t b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
-  return pack8_bits(b);
+  return pack8_bits(b, odd);
 }
 
 // ---------------------------------------------------------------------------
 // Asymmetric (s, z) encoder: 8 values t (true signs) of a group whose range,
 // with zero kept inside it, is [-nlo, hi] (hi, nlo >= 0, reduced over the
 // group).  With d = hi + nlo: z = rne(15 nlo / d) and code
-// clamp(rne(15 t / d) + z, 0, 15), packed as plain nibbles (code e in
-// nibble e).  15 / d is the hardware reciprocal of d / 15; groups with
+// clamp(rne(15 t / d) + z, 0, 15), in the unsigned stored form.  15 / d is the hardware reciprocal of d / 15; groups with
 // 0 < d < 2^-100 are lifted by 2^64 (exact) as in encode8_rcp; d = 0 gives
 // z = 0 and codes 0.  Returns the word; z in z_out.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float nlo, uint32_t& z_out) {
+__device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float nlo, uint32_t& z_out, bool odd) {
   float d = hi + nlo, nl = nlo;
   if (__builtin_amdgcn_ballot_w64(d > 0.0f && d < kTinyMax) != 0) {
     if (d > 0.0f && d < kTinyMax) {
@@ -348,17 +428,16 @@ __device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float 
   }
   const float inv = d > 0.0f ? __builtin_amdgcn_rcpf(d * (1.0f / 15.0f)) : 0.0f;
   const uint32_t z = rne_code_bits(nl, inv) - kRoundMagicBits;
-  uint32_t acc = 0;
+  uint32_t b[8];
 #pragma unroll
-  for (int e = 7; e >= 0; --e) {
+  for (int e = 0; e < 8; ++e) {
     // rne(t inv) + z, clamped to [0, 15], in the magic-constant domain
-    uint32_t b = rne_code_bits(t[e], inv) + z;
-    b = b < kRoundMagicBits ? kRoundMagicBits : b;
-    b = b > kRoundMagicBits + 15u ? kRoundMagicBits + 15u : b;
-    acc = (acc << 4) + (b - kRoundMagicBits);
+    b[e] = rne_code_bits(t[e], inv) + z;
+    b[e] = b[e] < kRoundMagicBits ? kRoundMagicBits : b[e];
+    b[e] = b[e] > kRoundMagicBits + 15u ? kRoundMagicBits + 15u : b[e];
   }
   z_out = z;
-  return acc;
+  return pack8_ubits(b, odd);
 }
 
 }  // namespace rw4

@@ -31,7 +31,7 @@ hipError_t launch_quantize_act(const TransformDev& t, bool rrs, const void* x, b
                                int64_t ldx, uint8_t* q, float* s, float* smooth, int group, hipStream_t st);
 
 // Asymmetric (s, z) activations, block-128 Hadamard, groups of 128: plain
-// unsigned nibbles, scales and zero points (floats) [M][K / 128].
+// unsigned codes (stored form), scales and zero points (floats) [M][K / 128].
 hipError_t launch_quantize_act_asym(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
                                     uint8_t* q, float* s, float* z, hipStream_t st);
 // Block-128 Hadamard activations with the groups whose slot_of_group entry
@@ -43,11 +43,11 @@ hipError_t launch_extend_weight_groups(const uint8_t* qw, const float* sw, int64
                                        const int32_t* groups8, int64_t n8, uint8_t* qx, float* sx, hipStream_t st);
 // cw[n][g] = sum of the 128 codes of group g of packed weight row n (floats).
 hipError_t launch_weight_code_sums(const uint8_t* qw, int64_t N, int64_t K, float* cw, hipStream_t st);
-// y = sum_g sa sw (sum_k qa qw - za cw) with plain-nibble activation codes (groups of 128).
+// y = sum_g sa sw (sum_k qa qw - za cw) with unsigned activation codes (groups of 128).
 hipError_t launch_gemm_asym(const uint8_t* qa, const float* sa, const float* za, const uint8_t* qw, const float* sw,
                             const float* cw, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16, int64_t ldy,
                             hipStream_t st);
-// x_hat = s (q - z) from plain-nibble codes (groups of 128).
+// x_hat = s (q - z) from unsigned codes (groups of 128).
 hipError_t launch_dequantize_asym(const uint8_t* q, const float* s, const float* z, int64_t M, int64_t K, void* out,
                                   bool out_bf16, int64_t ldo, hipStream_t st);
 

@@ -103,13 +103,14 @@ def test_asymmetric_beats_symmetric_on_one_sided_data():
 
 
 def test_pack_uint4_layout_and_round_trip():
+    # even-word table: 1 -> bit 0; 2 -> 7; 15 -> 12-15; 7 -> 24-26; 8 -> 17; 9 -> 4, 23; 10 -> 11, 29
     codes = np.array([[1, 2, 15, 0, 7, 8, 9, 10]], dtype=np.uint8)
-    assert oracle.pack_uint4(codes).tolist() == [[0x21, 0x0F, 0x87, 0xA9]]
+    assert oracle.pack_uint4(codes).tolist() == [[0x91, 0xF8, 0x82, 0x27]]
     rng = np.random.default_rng(5)
     c = rng.integers(0, 16, size=(4, 256)).astype(np.uint8)
     np.testing.assert_array_equal(oracle.unpack_uint4(oracle.pack_uint4(c)), c)
     with pytest.raises(ValueError):
-        oracle.pack_uint4(np.array([[16, 0]]))
+        oracle.pack_uint4(np.array([[16, 0, 0, 0, 0, 0, 0, 0]]))
 
 
 def test_weight_code_sums_brute_force():

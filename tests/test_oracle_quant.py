@@ -109,56 +109,79 @@ def test_quant_rounds_half_to_even():
     assert codes[0, :6].tolist() == [0, 2, 2, 0, -2, 7]
 
 
-def test_pack_unpack_roundtrip_and_order():
+def test_pack_unpack_roundtrip_and_positions():
     rng = np.random.default_rng(8)
     c = rng.integers(-7, 8, size=(5, 256)).astype(np.int8)
     p = oracle.pack_int4(c)
     assert p.shape == (5, 128) and p.dtype == np.uint8
     assert np.array_equal(oracle.unpack_int4(p), c)
-    # magnitude in bits 0-2 of nibble e (low nibble = even e); the sign of
-    # code e in bit 3 of nibble e+1, the last code's sign in nibble 0
+    # single codes at the positions of the layout table: (|c| bits 0-2, sign)
     word = np.zeros((1, 8), dtype=np.int8)
-    word[0, 0] = -1
-    assert oracle.pack_int4(word)[0].tolist() == [0x81, 0, 0, 0]
-    word[0] = [0, -7, 0, 0, 0, 0, 0, 0]
-    assert oracle.pack_int4(word)[0].tolist() == [0x70, 0x08, 0, 0]
-    word[0] = [0, 0, 0, 0, 0, 0, 0, -3]
-    assert oracle.pack_int4(word)[0].tolist() == [0x08, 0, 0, 0x30]
-    word[0] = [7, 0, 0, 0, 0, 0, 0, 0]
-    assert oracle.pack_int4(word)[0].tolist() == [0x07, 0, 0, 0]
-    # words are independent: the sign bit never crosses a 4-byte boundary
+    word[0, 0] = -1                     # bits 0 and 5
+    assert oracle.pack_int4(word)[0].tolist() == [0x21, 0, 0, 0]
+    word[0] = [0, -7, 0, 0, 0, 0, 0, 0]  # bits 6, 7, 8 and 11
+    assert oracle.pack_int4(word)[0].tolist() == [0xC0, 0x09, 0, 0]
+    word[0] = [0, 0, 0, 0, 0, 0, 0, -3]  # code 7: bits 10, 27 and sign 15
+    assert oracle.pack_int4(word)[0].tolist() == [0, 0x84, 0, 0x08]
+    word[0] = [0, 0, 0, 0, 0, 7, 0, 0]   # code 5: bits 30, 31, 16
+    assert oracle.pack_int4(word)[0].tolist() == [0, 0, 0x01, 0xC0]
+    # odd words use the second table: code 8 + 2 = 10 with value -5 -> bits 12, 30 and sign 1
     two = np.zeros((1, 16), dtype=np.int8)
+    two[0, 10] = -5
+    assert oracle.pack_int4(two)[0].tolist() == [0, 0, 0, 0, 0x02, 0x10, 0, 0x40]
+    # words are independent: a code never reaches outside its 4 bytes
+    two[0] = 0
     two[0, 7] = -2
-    assert oracle.pack_int4(two)[0].tolist() == [0x08, 0, 0, 0x20, 0, 0, 0, 0]
+    assert oracle.pack_int4(two)[0, 4:].tolist() == [0, 0, 0, 0]
     # a negative zero (sign bit set, magnitude 0) decodes to 0
-    assert oracle.unpack_int4(np.array([[0x08, 0, 0, 0]], dtype=np.uint8)).tolist() == [[0] * 8]
+    assert oracle.unpack_int4(np.array([[0x20, 0, 0, 0]], dtype=np.uint8)).tolist() == [[0] * 8]
     with pytest.raises(ValueError):
         oracle.pack_int4(np.array([[8, 0, 0, 0, 0, 0, 0, 0]]))
     with pytest.raises(ValueError):
         oracle.pack_int4(np.array([[-8, 0, 0, 0, 0, 0, 0, 0]]))
 
 
-def test_packed_word_splits_into_sign_magnitude_bytes():
-    """A word w of the packed form gives the even codes as the bytes of
-    w & 0x87878787 and the odd codes as the bytes of rotr(w, 4) & 0x87878787,
-    each byte = sign << 7 | magnitude (brute force over random words)."""
-    rng = np.random.default_rng(9)
-    c = rng.integers(-7, 8, size=(64, 8)).astype(np.int8)
-    p = oracle.pack_int4(c).astype(np.uint32)
-    w = p[:, 0] | (p[:, 1] << 8) | (p[:, 2] << 16) | (p[:, 3] << 24)
-    def decode(u):
-        out = []
-        for k in range(4):
-            b = (int(u) >> (8 * k)) & 0xFF
-            out.append(-(b & 7) if b & 0x80 else (b & 7))
-        return out
-    for row in range(64):
-        wi = int(w[row])
-        even = decode(wi & 0x87878787)
-        rot = ((wi >> 4) | (wi << 28)) & 0xFFFFFFFF
-        odd = decode(rot & 0x87878787)
-        assert even == c[row, 0::2].tolist()
-        assert odd == c[row, 1::2].tolist()
+def _fp6_dense(codes, signed):
+    """The 96-bit string sum_k f_k << 6 k of 16 codes' FP6 E2M3 encodings
+    (sign bit 5, exponent bits 3-4, mantissa bits 0-2): c / 8 is a
+    subnormal (exponent 0, mantissa |c|) for |c| <= 7; u / 8 for u = 8..15
+    has exponent 1 and mantissa u - 8, i.e. the 6-bit pattern u."""
+    x = 0
+    for k, c in enumerate(codes):
+        c = int(c)
+        f = ((32 if c < 0 else 0) | abs(c)) if signed else c
+        x |= f << (6 * k)
+    return x
+
+
+def _open_pair(w0, w1, signed):
+    """The three words of the dense FP6 string from a stored word pair, by the
+    mask identity the GEMM applies (three masks and one 16-bit rotation)."""
+    A, C, E = (0xE79E79E7, 0x9E79E79E, 0x18611861) if signed else (0xCF3CF3CF, 0x3CF3CF3C, 0x30C330C3)
+    full = 0xFFFFFFFF
+    d0, d2 = w0 & A, w1 & C
+    v = (w0 & ~A & full) | (w1 & ~C & full)
+    r = ((v >> 16) | (v << 16)) & full
+    d1 = (r & E) | (v & ~E & full)
+    return d0 | (d1 << 32) | (d2 << 64)
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_packed_pairs_open_into_dense_fp6(signed):
+    """Brute force over random rows: every pair of stored words, opened with the
+    mask identity, is exactly the dense FP6 E2M3 string of its 16 codes, and
+    the two tables use each of the 32 bit positions once."""
+    layout = oracle.SIGNED_LAYOUT if signed else oracle.UNSIGNED_LAYOUT
+    for tab in layout:
+        assert sorted(p for code in tab for p in code) == list(range(32))
+    rng = np.random.default_rng(10 if signed else 11)
+    c = rng.integers(-7, 8, size=(32, 64)) if signed else rng.integers(0, 16, size=(32, 64))
+    p = (oracle.pack_int4(c) if signed else oracle.pack_uint4(c)).astype(np.uint64)
+    w = p[:, 0::4] | (p[:, 1::4] << np.uint64(8)) | (p[:, 2::4] << np.uint64(16)) | (p[:, 3::4] << np.uint64(24))
+    for row in range(32):
+        for j in range(4):
+            got = _open_pair(int(w[row, 2 * j]), int(w[row, 2 * j + 1]), signed)
+            assert got == _fp6_dense(c[row, 16 * j:16 * j + 16], signed), (row, j)
 
 
 def test_rrs_golden(golden_dir):
