@@ -874,7 +874,22 @@ __global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__
                                                        int32_t* __restrict__ order, float* __restrict__ s_g) {
   extern __shared__ float ms[];  // K maxima, then 256 partial counts
   int* cnt = reinterpret_cast<int*>(ms + K);
-  for (int64_t i = threadIdx.x; i < K; i += blockDim.x) ms[i] = m[i];
+  {
+    // K <= 8192: at most 8 16-byte loads per thread, all issued before the
+    // first LDS store (one memory latency instead of one per load)
+    const __amdgpu_buffer_rsrc_t rm = buf_rsrc(m, K * 4);
+    v4u32 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i4 = threadIdx.x + 256 * u;  // 16-byte chunk; past K / 4 reads zeros
+      t[u] = __builtin_amdgcn_raw_buffer_load_b128(rm, int(i4 < K / 4 ? uint32_t(i4 * 16) : kOutOfRange), 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i4 = threadIdx.x + 256 * u;
+      if (i4 < K / 4) *reinterpret_cast<v4u32*>(ms + i4 * 4) = t[u];
+    }
+  }
   __syncthreads();
   const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
   const int64_t j = int64_t(blockIdx.x) * 16 + c;
@@ -895,6 +910,40 @@ __global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__
   }
 }
 
+// The reordered row (lane l: reordered positions 512 c + 8 l + e, group
+// 4 c + l / 16) smoothed by its groups' scales, then the per-token INT4
+// encoder; stored scale a_t s_g (times post_scale).
+template <int NC>
+__device__ __forceinline__ void rrs_order_encode(float* v, const float* inv_s, const float* s_g, int lane,
+                                                 int64_t row, uint8_t* __restrict__ q, float* __restrict__ s,
+                                                 float post_scale) {
+  constexpr int64_t G = 4 * NC;
+  const int sub = lane & 15;
+  float m = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[c * 8 + e] *= inv_s[c];
+      m = fmaxf(m, fabsf(v[c * 8 + e]));
+    }
+  m = max_x<1>(m);
+  m = max_x<2>(m);
+  m = max_x<4>(m);
+  m = max_x<8>(m);
+  m = max_x<16>(m);
+  m = max_x<32>(m);
+  const float a_t = m * (1.0f / 7.0f);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(q + row * (G * 64));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint32_t b[8];
+    encode<8>(&v[c * 8], m, b);
+    qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
+    if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
+  }
+}
+
 // Second pass: one wave per row.  The transformed row goes to the wave's
 // LDS slice in natural channel order and is read back in the given order,
 // so lane l then holds reordered positions 512 c + 8 l + e; their group is
@@ -907,14 +956,12 @@ __global__ __launch_bounds__(256) void quant_rrs_order_kernel(Src src, int64_t M
                                                               float post_scale) {
   constexpr int K = E * 64;
   constexpr int NC = E / 8;
-  constexpr int64_t G = E / 2;
   __shared__ float rowbuf[4][K];
   __shared__ int32_t ord[K];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
-  const int sub = lane & 15;
   for (int j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
   __syncthreads();
   float inv_s[NC], s_g[NC];
@@ -940,29 +987,108 @@ __global__ __launch_bounds__(256) void quant_rrs_order_kernel(Src src, int64_t M
       for (int e = 0; e < 8; ++e) v[c * 8 + e] = buf[ord[c * 512 + lane * 8 + e]];
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    float m = 0.0f;
+    rrs_order_encode<NC>(v, inv_s, s_g, lane, row, q, s, post_scale);
+  }
+}
+
+// Full-row fast path of the reorder (block = K = 512 NC, row-major source
+// without random signs): the register / DPP transform of quant_rrs_full
+// (lane l holds the values of word rrs_word(l, c), times flip), with the
+// next row's loads in flight while a row is transformed.
+template <int NC, bool BF16>
+__global__ __launch_bounds__(256) void rrs_chanmax_full_kernel(const void* __restrict__ x, int64_t ldx, int64_t M,
+                                                               float* __restrict__ partial) {
+  constexpr int K = 512 * NC;
+  __shared__ float red[K];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  // wave-uniform (the buffer descriptors built from it must be scalar)
+  const int64_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  float cmax[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cmax[c][e] = 0.0f;
+  RawFullRow<NC, BF16> raw = load_full_row<NC, BF16>(x, ldx, M, wave, lane);
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float v[NC][8];
+    unpack_full_row<NC, BF16>(raw, v);
+    raw = load_full_row<NC, BF16>(x, ldx, M, row + n_waves, lane);
+    fwht_row_full<NC>(v, c1, c2, c7, c8);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[c * 8 + e] *= inv_s[c];
-        m = fmaxf(m, fabsf(v[c * 8 + e]));
+      for (int e = 0; e < 8; ++e) cmax[c][e] = fmaxf(cmax[c][e], fabsf(v[c][e]));
+  }
+  // the four waves of the block in turn: wave 0 stores, the others take the maximum
+  for (int t = 0; t < 4; ++t) {
+    if (w == t) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float* r = red + 8 * rrs_word<NC>(lane, c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = t == 0 ? cmax[c][e] : fmaxf(r[e], cmax[c][e]);
       }
-    m = max_x<1>(m);
-    m = max_x<2>(m);
-    m = max_x<4>(m);
-    m = max_x<8>(m);
-    m = max_x<16>(m);
-    m = max_x<32>(m);
-    const float a_t = m * (1.0f / 7.0f);
-    uint32_t* qrow = reinterpret_cast<uint32_t*>(q + row * (G * 64));
+    }
+    __syncthreads();
+  }
+  for (int j = threadIdx.x; j < K; j += blockDim.x) partial[int64_t(blockIdx.x) * K + j] = red[j];
+}
+
+template <int NC, bool BF16>
+__global__ __launch_bounds__(256) void quant_rrs_order_full_kernel(const void* __restrict__ x, int64_t ldx, int64_t M,
+                                                                   const int32_t* __restrict__ order,
+                                                                   const float* __restrict__ smooth,
+                                                                   uint8_t* __restrict__ q, float* __restrict__ s,
+                                                                   float post_scale) {
+  constexpr int K = 512 * NC;
+  constexpr int E = 8 * NC;
+  __shared__ float rowbuf[4][K];
+  __shared__ int32_t ord[K];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
+  __syncthreads();
+  float inv_s[NC], s_g[NC];
+  uint32_t woff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    s_g[c] = smooth[c * 4 + (lane >> 4)];
+    inv_s[c] = safe_inv(s_g[c], 1.0f);
+    woff[c] = uint32_t(8 * rrs_word<NC>(lane, c));
+  }
+  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
+  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
+  const float flip = parity_sign(lane & 15);
+  float* buf = rowbuf[w];
+  RawFullRow<NC, BF16> raw = load_full_row<NC, BF16>(x, ldx, M, wave, lane);
+  for (int64_t row = wave; row < M; row += n_waves) {
+    float t[NC][8];
+    unpack_full_row<NC, BF16>(raw, t);
+    raw = load_full_row<NC, BF16>(x, ldx, M, row + n_waves, lane);
+    fwht_row_full<NC>(t, c1, c2, c7, c8);
+    // the row in natural channel order (true signs) in this wave's slice
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      uint32_t b[8];
-      encode<8>(&v[c * 8], m, b);
-      qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
-      if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
+      float4* d = reinterpret_cast<float4*>(buf + woff[c]);
+      d[0] = make_float4(t[c][0] * flip, t[c][1] * flip, t[c][2] * flip, t[c][3] * flip);
+      d[1] = make_float4(t[c][4] * flip, t[c][5] * flip, t[c][6] * flip, t[c][7] * flip);
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    float v[E];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c * 8 + e] = buf[ord[c * 512 + lane * 8 + e]];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    rrs_order_encode<NC>(v, inv_s, s_g, lane, row, q, s, post_scale);
   }
 }
 
@@ -1401,6 +1527,32 @@ hipError_t launch_rrs_reorder_src(const Src& src, int64_t K, int log2b, int64_t 
   }
 }
 
+template <int NC>
+hipError_t launch_rrs_reorder_full(const void* x, bool bf16, int64_t ldx, int64_t M, uint8_t* q, float* s,
+                                   int32_t* order, float* ws, float post, hipStream_t st) {
+  constexpr int64_t K = 512 * NC;
+  float* partial = ws;
+  float* m = ws + int64_t(kChanmaxBlocks) * K;
+  float* smooth = m + K;
+  const int grid = grid_for_waves(M, 256 * 16);
+  const int rank_lds = int(K * 4 + 256 * 4);
+  if (bf16)
+    hipLaunchKernelGGL((rrs_chanmax_full_kernel<NC, true>), dim3(kChanmaxBlocks), dim3(256), 0, st, x, ldx, M, partial);
+  else
+    hipLaunchKernelGGL((rrs_chanmax_full_kernel<NC, false>), dim3(kChanmaxBlocks), dim3(256), 0, st, x, ldx, M, partial);
+  hipLaunchKernelGGL(chanmax_reduce_kernel, dim3(unsigned((K + 63) / 64)), dim3(1024), 0, st, (const float*)partial,
+                     kChanmaxBlocks, K, m);
+  hipLaunchKernelGGL(rrs_rank_kernel, dim3(unsigned(K / 16)), dim3(256), rank_lds, st, (const float*)m, K, order,
+                     smooth);
+  if (bf16)
+    hipLaunchKernelGGL((quant_rrs_order_full_kernel<NC, true>), dim3(grid), dim3(256), 0, st, x, ldx, M,
+                       (const int32_t*)order, (const float*)smooth, q, s, post);
+  else
+    hipLaunchKernelGGL((quant_rrs_order_full_kernel<NC, false>), dim3(grid), dim3(256), 0, st, x, ldx, M,
+                       (const int32_t*)order, (const float*)smooth, q, s, post);
+  return hipGetLastError();
+}
+
 template <class Src>
 hipError_t launch_perchannel_src(const Src& src, int64_t K, int log2b, int64_t N, uint8_t* q, float* s, float post,
                                  hipStream_t st) {
@@ -1436,6 +1588,11 @@ hipError_t launch_quantize_act_rrs_reorder(const TransformDev& t, const void* x,
                                     post, st);
     return launch_rrs_reorder_src(SignedSrc<RowSrc<false>>{{x, ldx}, t.sign_mask}, t.K, log2b, M, q, s, order, ws,
                                   post, st);
+  }
+  if (t.block == t.K && (t.K == 2048 || t.K == 4096)) {
+    // whole-row transform: the register / DPP kernels of the RRS path
+    if (t.K == 2048) return launch_rrs_reorder_full<4>(x, bf16, ldx, M, q, s, order, ws, post, st);
+    return launch_rrs_reorder_full<8>(x, bf16, ldx, M, q, s, order, ws, post, st);
   }
   if (bf16) return launch_rrs_reorder_src(RowSrc<true>{x, ldx}, t.K, log2b, M, q, s, order, ws, post, st);
   return launch_rrs_reorder_src(RowSrc<false>{x, ldx}, t.K, log2b, M, q, s, order, ws, post, st);

@@ -99,6 +99,9 @@ CASES = [
     ("h128_signed_f32", 20, 1024, 128, True, "f32", 24),
     ("h1024_k2048", 130, 2048, 1024, False, "bf16", 72),
     ("h4096_m1", 1, 4096, 4096, False, "bf16", 16),
+    # whole-row blocks of 2048 and 4096 take the register / DPP transform kernels
+    ("h2048_full_f32", 70, 2048, 2048, False, "f32", 24),
+    ("h4096_full_m300", 300, 4096, 4096, False, "bf16", 32),
 ]
 
 
