@@ -1132,56 +1132,77 @@ __global__ __launch_bounds__(256) void quant_row_perchannel_kernel(Src src, int6
 
 // Codes of every row taken in channel order: out[r, j] = code(q[r], order[j]).
 // A block walks rows four at a time: their stored words are decoded into
-// LDS as one signed byte per code, then every thread gathers whole output
-// words (8 codes) of all four rows and encodes them in the stored form.  A
-// thread's output words and their source channels are the same in every
-// row, so it reads the order once (K <= 8192: at most 4 output words of 8
-// codes per thread).
+// LDS as one byte per code (the code's 6-bit sign-magnitude field), then
+// every thread gathers whole output words (8 fields) of all four rows and
+// folds them into the stored form.  The next four rows' words are loaded
+// while the current ones are gathered.  A thread's output words and their
+// source channels are the same in every row, so it reads the order once
+// (K <= 8192: at most 4 words of a row per thread).
 constexpr int kPermuteRows = 4;
+constexpr int kPermuteWords = 4;  // words of a row per thread (K <= 8192)
 __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t K,
                                                             const int32_t* __restrict__ order,
                                                             uint8_t* __restrict__ out) {
-  extern __shared__ int8_t pc_codes[];  // kPermuteRows rows of K codes
+  extern __shared__ uint8_t pc_fields[];  // kPermuteRows rows of K fields
   const int W = int(K / 8);
   // source channel of this thread's output codes (word i = threadIdx.x + 256 u)
-  uint16_t src[4][8];
+  uint16_t src[kPermuteWords][8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kPermuteWords; ++u) {
     const int i = int(threadIdx.x) + 256 * u;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       src[u][e] = uint16_t(i < W ? min(uint32_t(order[i * 8 + e]), uint32_t(K - 1)) : 0u);  // clamped into the row
   }
-  for (int64_t row0 = int64_t(blockIdx.x) * kPermuteRows; row0 < rows; row0 += int64_t(gridDim.x) * kPermuteRows) {
-    const int nr = int(rows - row0 < kPermuteRows ? rows - row0 : kPermuteRows);
-    __syncthreads();  // the previous rows' codes consumed
-    for (int r = 0; r < nr; ++r) {
-      const uint32_t* words = reinterpret_cast<const uint32_t*>(q + (row0 + r) * (K / 2));
-      for (int i = threadIdx.x; i < W; i += blockDim.x) {
-        uint32_t lo, hi;
-        stored_fields<true>(words[i], (i & 1) != 0, lo, hi);
-        uint32_t c4[2] = {0u, 0u};
+  // words of rows row0 .. row0 + 3; rows past the end and words past the row read zeros
+  uint32_t wv[kPermuteRows][kPermuteWords];
+  auto load = [&](int64_t row0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t f = field6(lo, hi, e);
-          const uint32_t c = (f & 32u) ? uint32_t(-int(f & 7u)) & 0xFFu : (f & 7u);
-          c4[e >> 2] |= c << (8 * (e & 3));
-        }
-        *reinterpret_cast<uint2*>(pc_codes + r * K + i * 8) = make_uint2(c4[0], c4[1]);
+    for (int r = 0; r < kPermuteRows; ++r) {
+      const int64_t row = row0 + r;
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (K / 2), row < rows ? K / 2 : 0);
+#pragma unroll
+      for (int u = 0; u < kPermuteWords; ++u) {
+        const int i = int(threadIdx.x) + 256 * u;
+        wv[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rq, int(i < W ? uint32_t(i * 4) : kOutOfRange), 0, 0);
       }
     }
+  };
+  const int64_t stride = int64_t(gridDim.x) * kPermuteRows;
+  load(int64_t(blockIdx.x) * kPermuteRows);
+  for (int64_t row0 = int64_t(blockIdx.x) * kPermuteRows; row0 < rows; row0 += stride) {
+    const int nr = int(rows - row0 < kPermuteRows ? rows - row0 : kPermuteRows);
+    __syncthreads();  // the previous rows' fields consumed
+#pragma unroll
+    for (int r = 0; r < kPermuteRows; ++r) {
+#pragma unroll
+      for (int u = 0; u < kPermuteWords; ++u) {
+        const int i = int(threadIdx.x) + 256 * u;
+        if (r < nr && i < W) {
+          uint32_t lo, hi;
+          stored_fields<true>(wv[r][u], (i & 1) != 0, lo, hi);
+          uint32_t f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = field6(lo, hi, e);
+          const uint32_t d0 = f[0] | (f[1] << 8) | (f[2] << 16) | (f[3] << 24);
+          const uint32_t d1 = f[4] | (f[5] << 8) | (f[6] << 16) | (f[7] << 24);
+          *reinterpret_cast<uint2*>(pc_fields + r * K + i * 8) = make_uint2(d0, d1);
+        }
+      }
+    }
+    load(row0 + stride);  // the next rows' words, in flight while these are gathered
     __syncthreads();
     for (int r = 0; r < nr; ++r) {
-      const int8_t* codes = pc_codes + r * K;
+      const uint8_t* fr = pc_fields + r * K;
       uint32_t* dst = reinterpret_cast<uint32_t*>(out + (row0 + r) * (K / 2));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kPermuteWords; ++u) {
         const int i = int(threadIdx.x) + 256 * u;
         if (i >= W) break;
-        uint32_t b[8];
+        uint32_t f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = kRoundMagicBits + uint32_t(int(codes[src[u][e]]));
-        dst[i] = pack8_bits(b, (i & 1) != 0);
+        for (int e = 0; e < 8; ++e) f[e] = fr[src[u][e]];
+        dst[i] = pack8_fields(f, (i & 1) != 0);
       }
     }
   }

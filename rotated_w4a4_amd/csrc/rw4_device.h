@@ -279,6 +279,13 @@ __device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8], bool odd) {
   const uint32_t shi = fp6_sign_magnitude(hi + f6_rep(kOff, 3), f6_rep(1u, 3));
   return stored_word<true>((slo & 0x3FFFFFFFu) | (shi << 30), shi >> 2, odd);
 }
+// Stored word of 8 signed codes given as their 6-bit sign-magnitude fields
+// (bits 0-2 |c|, bit 5 the sign, as field6 returns them).
+__device__ __forceinline__ uint32_t pack8_fields(const uint32_t f[8], bool odd) {
+  uint32_t lo, hi;
+  horner6(f, lo, hi);
+  return stored_word<true>(lo, hi >> 2, odd);
+}
 // Stored word of 8 unsigned codes (0..15) from their magic-rounded patterns.
 __device__ __forceinline__ uint32_t pack8_ubits(const uint32_t b[8], bool odd) {
   uint32_t lo, hi;
