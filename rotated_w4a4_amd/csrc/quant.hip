@@ -170,13 +170,16 @@ struct RawRow {
 // rows (lanes l and l ^ 16).
 // ASYM (GS = 128 only): the asymmetric (s, z) encoder (encode8_asym) with
 // the unsigned stored form; zs receives the zero points as floats.
-template <bool BF16, bool SIGNED, int D, int GS, bool ASYM = false>
+template <bool BF16, bool SIGNED, int D, int GS, bool ASYM = false, bool MIXED = false>
 __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                              int64_t rows, int64_t G, int64_t Q, int64_t R,
                                                              const uint32_t* __restrict__ sign_mask,
                                                              uint8_t* __restrict__ q, float* __restrict__ s,
-                                                             float post_scale, float* __restrict__ zs = nullptr) {
+                                                             float post_scale, float* __restrict__ zs = nullptr,
+                                                             const int32_t* __restrict__ slot_of_group = nullptr,
+                                                             int64_t n8 = 0, float post8h = 0.0f, float post8l = 0.0f) {
   static_assert(!ASYM || GS == 128, "asymmetric groups of 128");
+  static_assert(!MIXED || (GS == 128 && !ASYM), "8-bit groups: symmetric groups of 128");
   constexpr int ES = BF16 ? 2 : 4;  // bytes per input element
   const int lane = threadIdx.x & 63;
   // wave index (4 waves per block), Q * R below 2^31 (checked on the host):
@@ -192,7 +195,15 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   const uint32_t x_off = uint32_t((grp * kGroup + sub * 8) * ES);
   const uint32_t q_off = uint32_t(grp * 64 + h128_lane_word(sub) * 4);
   const bool odd = (h128_lane_word(sub) & 1) != 0;  // word parity selects the stored form's table
-  const int64_t GSN = G * kGroup / GS;  // scale columns per row
+  // MIXED: rows of G + n8 groups; a listed group (slot_of_group >= 0) keeps
+  // its h plane in place and its l plane in the extra group G + slot
+  const int64_t GX = MIXED ? G + n8 : G;
+  const int32_t slot = MIXED && grp < G ? slot_of_group[grp] : -1;
+  const bool is8 = MIXED && slot >= 0 && slot < n8;
+  const bool any8 = MIXED && __builtin_amdgcn_ballot_w64(is8) != 0;  // wave-uniform
+  const uint32_t l_off = is8 ? uint32_t((G + slot) * 64 + h128_lane_word(sub) * 4) : kOutOfRange;
+  const uint32_t sl_off = is8 && sub == 0 ? uint32_t((G + slot) * 4) : kOutOfRange;
+  const int64_t GSN = GX * kGroup / GS;  // scale columns per row
   uint32_t s_off;
   if constexpr (GS == 64)
     s_off = (sub & 7) == 0 ? uint32_t((grp * 2 + (sub >> 3)) * 4) : kOutOfRange;
@@ -293,9 +304,47 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
           m = fmaxf(m, t);
         }
       }
-      const uint32_t packed = encode8_rcp(v, m, flip, odd);
-      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (GX * 64), live ? GX * 64 : 0);
       const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * GSN, live ? GSN * 4 : 0);
+      if constexpr (MIXED) {
+        if (any8) {
+          // the 8-bit groups: q8 = rne(112 x~ / m) split as 15 h + l (h = rne(q8 / 15),
+          // never a tie), 112 / m the reciprocal of m / 112 (tiny maxima lifted as
+          // in encode8_rcp); the other groups of the wave as below
+          uint32_t packed, packed_l = 0u;
+          float sc = m * post_scale, sc_l = 0.0f;
+          if (is8) {
+            float mm = m;
+            if (m > 0.0f && m < kTinyMax) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
+              mm = m * kTinyLift;
+            }
+            const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 112.0f)) : 0.0f;
+            uint32_t bh[8], bl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int q8 = int(rne_code_bits(v[e], inv) - kRoundMagicBits);
+              const int h = int(rne_code_bits(float(q8), 1.0f / 15.0f) - kRoundMagicBits);
+              bh[e] = kRoundMagicBits + uint32_t(h);
+              bl[e] = kRoundMagicBits + uint32_t(q8 - 15 * h);
+            }
+            packed = pack8_bits(bh, odd);
+            packed_l = pack8_bits(bl, odd);
+            sc = m * post8h;
+            sc_l = m * post8l;
+          } else {
+            packed = encode8_rcp(v, m, flip, odd);
+          }
+          __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(packed_l, rq, int(l_off), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs, int(s_off), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_l), rs, int(sl_off), 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
+      }
+      const uint32_t packed = encode8_rcp(v, m, flip, odd);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * post_scale), rs, int(s_off), 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -1676,100 +1725,34 @@ bool rowh_supported(int64_t K) {
 // group: 64, 128 or 256 for the block-128 Hadamard in per-group mode, else
 // 128 (the caller checks).
 // ---------------------------------------------------------------------------
-// quant_h128_mixed: block-128 Hadamard activations in groups of 128, with the
+// Mixed precision: block-128 Hadamard activations in groups of 128, with the
 // groups named by slot_of_group (>= 0) kept at 8 bits (the independent-
 // rotation article, section 4.1: mixed precision for extreme outliers).  An
 // 8-bit group gets q8 = rne(112 x~ / max) (225 levels) split exactly as
 // q8 = 15 h + l (h = rne(q8 / 15), never a tie): h is stored in place with
 // scale 15 max / 112, l in the extra group G + slot with scale max / 112.
-// Every other group is quant_h128_act's INT4 group (same arithmetic).
-// Rows hold G + n8 groups.  A block covers 16 groups of one row (wave w:
-// groups 4 w .. 4 w + 3, 16 lanes each).
+// Every other group is the plain INT4 group.  quant_h128_act_kernel's
+// persistent layout in its MIXED form: a wave keeps one quad of groups, so
+// only waves whose quad holds a listed group take the two-plane encoder
+// (decided once per wave); rows hold G + n8 groups.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool SIGNED>
-__global__ __launch_bounds__(256) void quant_h128_mixed_kernel(const void* __restrict__ x, int64_t ldx, int64_t G,
-                                                               int64_t n8, int64_t blocks_per_row,
-                                                               const uint32_t* __restrict__ sign_mask,
-                                                               const int32_t* __restrict__ slot_of_group,
-                                                               uint8_t* __restrict__ q, float* __restrict__ s,
-                                                               float post4, float post8h, float post8l) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane & 15;
-  const int64_t row = int64_t(blockIdx.x) / blocks_per_row;
-  const int64_t grp = (int64_t(blockIdx.x) - row * blocks_per_row) * 16 + wave * 4 + (lane >> 4);
-  const bool valid = grp < G;
-  const int64_t Gx = G + n8;
-  float v[8];
-  if (valid) {
-    RowSrc<BF16>{x, ldx}.load8(row, grp * kGroup + sub * 8, v);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-  }
-  if constexpr (SIGNED) {
-    if (valid) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ sign_mask[grp * kGroup + sub * 8 + e]);
-    }
-  }
-  const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
-  const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
-  const float flip = parity_sign(lane & 15);
-  fwht8(v);
-  lane_stages_dpp(v, c1, c2, c7, c8);
-  float m = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-  m = row16_max_dpp(m);
-  const int32_t slot = valid ? slot_of_group[grp] : -1;
-  const int word = h128_lane_word(sub);
-  uint8_t* const qrow = q + row * (Gx * 64);
-  float* const srow = s + row * Gx;
-  const bool odd = (word & 1) != 0;
-  if (slot < 0 || slot >= n8) {
-    const uint32_t packed = encode8_rcp(v, m, flip, odd);
-    if (valid) {
-      *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = packed;
-      if (sub == 0) srow[grp] = m * post4;
-    }
-    return;
-  }
-  // 8-bit group: 112 / m as the reciprocal of m / 112 (tiny maxima lifted as in encode8_rcp)
-  float mm = m;
-  if (m > 0.0f && m < kTinyMax) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
-    mm = m * kTinyLift;
-  }
-  const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 112.0f)) : 0.0f;
-  uint32_t bh[8], bl[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q8 = int(rne_code_bits(v[e], inv) - kRoundMagicBits);
-    const int h = int(rne_code_bits(float(q8), 1.0f / 15.0f) - kRoundMagicBits);
-    bh[e] = kRoundMagicBits + uint32_t(h);
-    bl[e] = kRoundMagicBits + uint32_t(q8 - 15 * h);
-  }
-  *reinterpret_cast<uint32_t*>(qrow + grp * 64 + word * 4) = pack8_bits(bh, odd);
-  *reinterpret_cast<uint32_t*>(qrow + (G + slot) * 64 + word * 4) = pack8_bits(bl, odd);
-  if (sub == 0) {
-    srow[grp] = m * post8h;
-    srow[G + slot] = m * post8l;
-  }
-}
-
 hipError_t launch_quantize_act_mixed(const TransformDev& t, const void* x, bool bf16, int64_t M, int64_t ldx,
                                      const int32_t* slot_of_group, int64_t n8, uint8_t* q, float* s, hipStream_t st) {
   if (t.kind != TransformKind::Hadamard || t.block != kGroup) return hipErrorInvalidValue;
   const int64_t G = t.K / kGroup;
-  const int64_t bpr = (G + 15) / 16, blocks = M * bpr;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  constexpr int D = 1, GS = 128;
+  constexpr int64_t kResidentWaves = 256 * 32;
+  const int64_t Q = (G + 3) / 4;
+  const int64_t rows_per_wave = Q * M <= kResidentWaves ? 1 : Q * M <= 2 * kResidentWaves ? 2 : 3;
+  int64_t R = (M + rows_per_wave - 1) / rows_per_wave;
+  if (R < 1) R = 1;
+  const int64_t blocks = (Q * R + 3) / 4;
+  if (Q * R > 0x7FFFFFFF - 3 || (G + n8) * 64 * (bf16 ? 4 : 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const float norm = 1.0f / sqrtf(128.0f);
   const float post4 = norm * (1.0f / 7.0f), post8h = norm * (15.0f / 112.0f), post8l = norm * (1.0f / 112.0f);
-#define RW4_MIXED(B, S)                                                                                          \
-  hipLaunchKernelGGL((quant_h128_mixed_kernel<B, S>), dim3(unsigned(blocks)), dim3(256), 0, st, x, ldx, G, n8, bpr, \
-                     t.sign_mask, slot_of_group, q, s, post4, post8h, post8l)
+#define RW4_MIXED(B, S)                                                                                              \
+  hipLaunchKernelGGL((quant_h128_act_kernel<B, S, D, GS, false, true>), dim3(blocks), dim3(256), 0, st, x, ldx, M, G, \
+                     Q, R, t.sign_mask, q, s, post4, nullptr, slot_of_group, n8, post8h, post8l)
   if (bf16) {
     if (t.sign_mask) RW4_MIXED(true, true); else RW4_MIXED(true, false);
   } else {

@@ -34,6 +34,8 @@ CASES = [
     ("mixed_signed", 300, 1024, 200, [5], "bf16", True),
     ("mixed_none", 33, 384, 64, [], "bf16", False),
     ("mixed_q_proj", 2048, 4096, 4096, [4, 17, 30], "bf16", False),
+    # 11 groups (a partial last quad), four 8-bit groups, three of them in one quad
+    ("mixed_dense_quad", 65, 1408, 48, [8, 9, 10, 2], "f32", True),
 ]
 
 
