@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
               for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
               mm = m * kTinyLift;
             }
-            const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 112.0f)) : 0.0f;
+            const float inv = mm > 0.0f ? __builtin_amdgcn_rcpf(mm * signed_const(1.0f / 112.0f, flip)) : 0.0f;
             uint32_t bh[8], bl[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(256) void quant_rrs_full_kernel(const void* __restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[c][e] *= kTinyLift;
     }
-    const float k = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 7.0f)) : 0.0f;
+    const float k = mm > 0.0f ? __builtin_amdgcn_rcpf(mm * signed_const(1.0f / 7.0f, flip)) : 0.0f;
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), G * 64);
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, G * 4);
     const float a_t = m * (1.0f / 7.0f);

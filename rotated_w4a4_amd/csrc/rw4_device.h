@@ -202,6 +202,32 @@ __device__ __forceinline__ uint32_t rne_code_bits(float v, float inv) {
 // them moved by 16 bits.  Each word depends on its own 8 codes only: W0
 // holds fields 0-7 (X bits 0-47), W1 fields 8-15 (X bits 48-95).
 // ---------------------------------------------------------------------------
+// Bitfield insert (mask ? a : b, bit by bit) and a funnel shift by a lane's
+// own amount, written out: for masks and shifts that differ between lanes
+// the compiler otherwise emits two instructions for each.
+__device__ __forceinline__ uint32_t bfi32(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t alignbit_v(uint32_t hi, uint32_t lo, uint32_t shift) {
+  uint32_t r;
+  asm("v_alignbit_b32 %0, %1, %2, %3" : "=v"(r) : "v"(hi), "v"(lo), "v"(shift));
+  return r;
+}
+// c with a lane's sign flip (+-1) applied, as a value the compiler cannot
+// see through: 7 / m times the flip is then one reciprocal of m * (+-1/7)
+// (rcp(-x) = -rcp(x) exactly), where the compiler otherwise computes the
+// reciprocal for both signs and selects.  Never feed a transcendental
+// result into inline asm: gfx950 needs a wait state between a
+// transcendental instruction and a VALU reading its result, which the
+// compiler does not insert for asm operands.
+__device__ __forceinline__ float signed_const(float c, float flip) {
+  uint32_t r;
+  asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "v"(__float_as_uint(c)), "v"(__float_as_uint(flip) & 0x80000000u));
+  return __uint_as_float(r);
+}
+
 constexpr uint32_t kSgnA = 0xE79E79E7u, kSgnC = 0x9E79E79Eu, kSgnE = 0x18611861u;
 constexpr uint32_t kUnsA = 0xCF3CF3CFu, kUnsC = 0x3CF3CF3Cu, kUnsE = 0x30C330C3u;
 
@@ -215,9 +241,8 @@ __device__ __forceinline__ uint32_t stored_word(uint32_t lo, uint32_t hi, bool o
   constexpr uint32_t kZ0 = ~(SIGNED ? kSgnA : kUnsA), kZ2 = ~(SIGNED ? kSgnC : kUnsC);
   const uint32_t src = odd ? lo : hi;
   const uint32_t dup = __builtin_amdgcn_perm(src, src, 0x01000100u);  // low half in both halves
-  const uint32_t base = __builtin_amdgcn_alignbit(hi, lo, odd ? 16u : 0u);
-  const uint32_t z = odd ? kZ2 : kZ0;
-  return (dup & z) | (base & ~z);
+  const uint32_t base = alignbit_v(hi, lo, odd ? 16u : 0u);
+  return bfi32(odd ? kZ2 : kZ0, dup, base);
 }
 
 // The 48-bit field string of a stored word's 8 codes (the inverse of
@@ -408,7 +433,7 @@ __device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float fl
       mm = m * kTinyLift;
     }
   }
-  const float inv = mm > 0.0f ? flip * __builtin_amdgcn_rcpf(mm * (1.0f / 7.0f)) : 0.0f;
+  const float inv = mm > 0.0f ? __builtin_amdgcn_rcpf(mm * signed_const(1.0f / 7.0f, flip)) : 0.0f;
   uint32_t b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
