@@ -941,13 +941,20 @@ __global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__
   }
   __syncthreads();
   const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
-  const int64_t j = int64_t(blockIdx.x) * 16 + c;
+  const int j = int(blockIdx.x) * 16 + c;
   const float mj = j < K ? ms[j] : 0.0f;
-  const int64_t slice = K / 16;
+  const int slice = int(K / 16);  // a multiple of 8 (K % 128 == 0)
   int n = 0;
-  for (int64_t i = r * slice; i < (r + 1) * slice; ++i) {
-    const float mi = ms[i];
-    n += (mi > mj) || (mi == mj && i < j);
+  // 16-byte LDS reads, eight channels per step, unrolled so that the reads
+  // of several steps are in flight together
+  const float4* m4 = reinterpret_cast<const float4*>(ms + r * slice);
+#pragma unroll 4
+  for (int i8 = 0; i8 < slice / 8; ++i8) {
+    const float4 a = m4[2 * i8], b = m4[2 * i8 + 1];
+    const int i0 = r * slice + 8 * i8;
+    const float mi[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n += (mi[e] > mj) || (mi[e] == mj && i0 + e < j);
   }
   cnt[threadIdx.x] = n;
   __syncthreads();
