@@ -1103,13 +1103,23 @@ __global__ __launch_bounds__(256) void quant_rrs_order_full_kernel(const void* _
   constexpr int K = 512 * NC;
   constexpr int E = 8 * NC;
   __shared__ float rowbuf[4][K];
-  __shared__ int32_t ord[K];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
   const int64_t n_waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
-  for (int j = threadIdx.x; j < K; j += blockDim.x) ord[j] = order[j];
-  __syncthreads();
+  // this lane's source channels (reordered positions 512 c + 8 l + e), two
+  // 16-bit indices per register (K <= 8192), so the gather reads LDS once
+  // per element
+  uint32_t ord2[E / 2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int4* src = reinterpret_cast<const int4*>(order + c * 512 + lane * 8);
+    const int4 o0 = src[0], o1 = src[1];
+    ord2[c * 4 + 0] = uint32_t(o0.x) | (uint32_t(o0.y) << 16);
+    ord2[c * 4 + 1] = uint32_t(o0.z) | (uint32_t(o0.w) << 16);
+    ord2[c * 4 + 2] = uint32_t(o1.x) | (uint32_t(o1.y) << 16);
+    ord2[c * 4 + 3] = uint32_t(o1.z) | (uint32_t(o1.w) << 16);
+  }
   float inv_s[NC], s_g[NC];
   uint32_t woff[NC];
 #pragma unroll
@@ -1139,9 +1149,10 @@ __global__ __launch_bounds__(256) void quant_rrs_order_full_kernel(const void* _
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     float v[E];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[c * 8 + e] = buf[ord[c * 512 + lane * 8 + e]];
+    for (int i = 0; i < E / 2; ++i) {
+      v[2 * i] = buf[ord2[i] & 0xFFFFu];
+      v[2 * i + 1] = buf[ord2[i] >> 16];
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     rrs_order_encode<NC>(v, inv_s, s_g, lane, row, q, s, post_scale);
