@@ -13,6 +13,11 @@ Inputs are resident in HBM before the timed region.  Independent buffer sets
 512 MB is touched between two uses of a set: the 256 MB Infinity Cache
 cannot serve them.
 
+Before the timed region the GPU runs the W warm-up steps and then further
+untimed steps until it has been under load for at least --settle-ms (200
+ms by default): its clocks ramp up under sustained load (the down_proj GEMM
+takes 425 us cold and ~250 us settled), and a serving loop runs settled.
+The warm-up actually run is reported as "warmup_run".
 Prints one JSON line (stdout).  Per-kernel times come from HIP events
 (created without the system-scope fence, so recording them flushes no
 caches) recorded on the stream the library launches on, around the kernels
@@ -54,6 +59,31 @@ PEAK_I8_TOPS = 5000.0        # MI355X dense int8 (and FP8) MFMA: the INT4 GEMM's
 PEAK_F6_TFLOPS = 10100.0     # MI355X dense FP6 MFMA: the units the GEMM's products run on
 MALL_FLUSH_BYTES = 512 << 20
 EVENT_EVERY = 4              # timed steps per step instrumented with per-kernel events
+SETTLE_MS = 200.0            # default untimed sustained load before timing (see warm_up)
+
+
+def warm_up(run, args, torch):
+    """The W untimed warm-up steps, then more untimed steps until the warm-up
+    has kept the GPU busy for at least --settle-ms of wall time.  The GPU's
+    clocks ramp up under sustained load: measured on the box, the down_proj
+    GEMM takes 425 us in its first batch of launches and ~250 us after about
+    25 ms of load (and is slow again after 2 s idle); the q_proj step drops
+    from ~68 us to ~48 us within ~20 ms.  A serving loop runs at the settled
+    clocks, so the timed region starts there.  Returns the warm-up steps run
+    and the warm-up wall time in ms."""
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(args.warmup):
+        run(n)
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            run(n)
+            n += 1
+        torch.cuda.synchronize()
+    return {"steps": n, "ms": (time.perf_counter() - t0) * 1e3}
+
 
 
 def log(*a):
@@ -160,6 +190,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed sustained load before timing, at least (after the warm-up steps)")
     ap.add_argument("--workload", default="q_proj",
                     choices=["q_proj", "down_proj", "rrs", "decode1", "decode4", "decode16", "decode32", "decode64",
                              "decode128", "decode256", "tiny", "kv", "rrs_reorder", "fused1", "fused2", "fused4",
@@ -359,8 +391,7 @@ def main_kv(args, torch, rw4, gu, dev):
     else:
         run = step
 
-    for i in range(args.warmup):
-        run(i)
+    warm = warm_up(run, args, torch)
     # the kernels' durations come from the back-to-back runs below; the timed region is
     # bracketed as a whole (events around each short launch would slow the host further)
     r0, r1 = HipEvent(), HipEvent()
@@ -391,7 +422,7 @@ def main_kv(args, torch, rw4, gu, dev):
     log(f"rotate_act (queries, bf16 in/out): {r_b2b:.2f} us ({rb_gbps:.0f} GB/s, host ahead: {r_ahead})")
     out = {
         "metric": KV_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_run": warm, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in/out, int4 codes, fp32 transform and scales", "data": "synthetic",
         "config": {"workload": f"kv M={M} K={K} (8 heads x 128)", "group": grp, "buffer_sets": nsets,
                    "launch": "one HIP graph replay per step" if graph else args.launch + " calls"},
@@ -459,8 +490,7 @@ def main_rrs_reorder(args, torch, rw4, gu, dev):
         perm()
         gemm()
 
-    for i in range(args.warmup):
-        step(i)
+    warm = warm_up(step, args, torch)
     r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -478,7 +508,7 @@ def main_rrs_reorder(args, torch, rw4, gu, dev):
     log(f"rrs reorder step {ms_per_step * 1e3:.1f} us: quantize (4 kernels) {q_us:.2f} us, weight permutation "
         f"{p_us:.2f} us ({pbytes / p_us / 1e3:.0f} GB/s), gemm {g_us:.2f} us ({ops / g_us / 1e6:.0f} TOPS)")
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "warmup_run": warm, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
            "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"rrs_reorder M={M} K={K} N={N}", "transform": f"hadamard{K}",
@@ -522,9 +552,11 @@ def main_decode_fused(args, torch, rw4, gu, dev):
         qc()
         gc[i % nsets]()
 
-    for i in range(args.warmup):
+    def step_and_two(i):
         step(i)
         two(i)
+
+    warm = warm_up(step_and_two, args, torch)
     r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -540,7 +572,7 @@ def main_decode_fused(args, torch, rw4, gu, dev):
     log(f"decode_fused M={M} K={K} N={N}: {f_us:.2f} us per step back to back (host ahead {f_ok}); "
         f"quantize_act + w4a4_gemm {t_us:.2f} us (host ahead {t_ok})")
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "warmup_run": warm, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
            "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"decode_fused M={M} K={K} N={N}", "transform": "hadamard128",
@@ -583,8 +615,7 @@ def main_asym(args, torch, rw4, gu, dev):
         qc[i % nsets]()
         gc[i % nsets]()
 
-    for i in range(args.warmup):
-        step(i)
+    warm = warm_up(step, args, torch)
     r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -604,7 +635,7 @@ def main_asym(args, torch, rw4, gu, dev):
     log(f"{args.workload} M={M} K={K} N={N}: step {ms_per_step * 1e3:.1f} us; asymmetric quantize {q_us:.2f} us, "
         f"gemm {g_us:.2f} us ({ops / g_us / 1e6:.0f} TOPS); symmetric quantize {qs_us:.2f} us, gemm {gs_us:.2f} us")
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "warmup_run": warm, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
            "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
@@ -654,8 +685,7 @@ def main_mixed(args, torch, rw4, gu, dev, n8=4):
         qc[i % nsets]()
         gc[i % nsets]()
 
-    for i in range(args.warmup):
-        step(i)
+    warm = warm_up(step, args, torch)
     r0, r1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -674,7 +704,7 @@ def main_mixed(args, torch, rw4, gu, dev, n8=4):
         f"mixed quantize {q_us:.2f} us, gemm over K + {128 * n8} {g_us:.2f} us; all-INT4 quantize {q4_us:.2f} us, "
         f"gemm {g4_us:.2f} us")
     out = {"metric": METRIC, "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "warmup_run": warm, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
            "dtype": "int4 codes (exact on fp6 MFMA), fp32 transform, rescale and epilogue", "data": "synthetic",
            "config": {"workload": f"{args.workload} M={M} K={K} N={N}", "transform": "hadamard128",
@@ -797,9 +827,7 @@ def main():
     else:
         run = step
 
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
+    warm = warm_up(run, args, torch)
 
     # timed region: exactly `steps` steps, events on the launch stream.  Every EVENT_EVERY-th
     # step records events around its two kernels: recording them on every step adds ~4.4 us
@@ -882,6 +910,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": warm,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
