@@ -590,10 +590,10 @@ constexpr int kStageTileBytes = 2 * kGroupBytes;        // A and B tiles of two 
 constexpr int kStageSplitBytes = 2 * kSplitGroupBytes;  // their split scale operands
 
 // ASYM: unsigned activation codes with zero points za [M][G] and the
-// weight code sums cw [N][G]: every group's accumulators start at
-// -za cw (exact integers, from a bf16 MFMA on the spare K slots 6 and 7 of
-// the split scale operands: -za twice against cw split into two bf16
-// parts), then the integer products add to them.
+// weight code sums cw [N][G]: every group's (halved) accumulators start at
+// -za cw / 2 (exact, from a bf16 MFMA on the spare K slots 6 and 7 of the
+// split scale operands: -za twice against cw / 4 split into two bf16 parts,
+// in both lane halves), then the halved integer products add to them.
 template <bool BF16, bool ASYM = false>
 __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restrict__ qa,
                                                           const float* __restrict__ sa,
@@ -669,13 +669,16 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     const uint4 o = split_operand(x, sel);
     uint32_t w = 0;
     if constexpr (ASYM) {
-      // slots 6, 7: rows (-za, -za), columns (cw rounded toward zero to bf16, the exact rest)
+      // slots 6, 7: rows (-za, -za), columns cw / 4 as (rounded toward zero to
+      // bf16, the exact rest): both lane halves supply them, so the products
+      // add to -za cw / 2, the zero-point term of the halved accumulator
       if (row_scale) {
         const uint32_t nz = __float_as_uint(-zx) >> 16;  // small integers: exact in bf16
         w = nz | (nz << 16);
       } else {
-        const uint32_t hi = __float_as_uint(zx) & 0xFFFF0000u;
-        w = (hi >> 16) | (__float_as_uint(zx - __uint_as_float(hi)) & 0xFFFF0000u);
+        const float c4 = zx * 0.25f;  // exact
+        const uint32_t hi = __float_as_uint(c4) & 0xFFFF0000u;
+        w = (hi >> 16) | (__float_as_uint(c4 - __uint_as_float(hi)) & 0xFFFF0000u);
       }
     }
     *reinterpret_cast<v4u*>(S + q * kSplitGroupBytes + tid * 16) = v4u{o.x, o.y, o.z, w};
@@ -696,13 +699,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
     osa = (wm * 64 + frow) * 16;
     osb = 2048 + (wn * 64 + frow) * 16;
   }
-  // Symmetric codes: both lane halves supply the same split operands, the
-  // bf16 MFMA returns 2 sa sw and the integer MFMAs return acc / 2 (B-side
-  // scale 2^2, exact).  ASYM: the lanes of K slots 8-15 zero their row
-  // operands (slots 6-7 carry the zero-point products, which must count
-  // once), and acc keeps its scale.
-  const uint32_t keep = h ? 0u : 0xFFFFFFFFu;
-  constexpr int kBScale = ASYM ? kF6Scale : kF6Scale - 1;
+  // Both lane halves supply the same split operands: the bf16 MFMA returns
+  // 2 sa sw and the integer MFMAs return acc / 2 (B-side scale 2^2, exact).
+  // ASYM: the accumulators start at -za cw / 2 (slots 6-7, see put_split),
+  // and the scale products leave slots 6-7 out (row operands zeroed there).
+  constexpr int kBScale = kF6Scale - 1;
   auto rd = [](const uint8_t* base, uint32_t off) { return *reinterpret_cast<const v4u*>(base + off); };
   auto read_half = [&](const uint8_t* T, int q, uint32_t oa, uint32_t ob, v4u (&f)[4]) {
     const uint8_t* b = T + q * kGroupBytes;
@@ -742,24 +743,20 @@ __global__ __launch_bounds__(256, 2) void gemm_f8p_kernel(const uint8_t* __restr
                                                                    0, kF6Scale, 0, kBScale);
   };
   // scale products of the four 32 x 32 tiles (bf16 MFMA on the splits), then y += acc * p
-  // ASYM: the accumulators of a group start at -za cw (K slots 6 and 7 only)
+  // ASYM: the accumulators of a group start at -za cw / 2 (K slots 6 and 7 only)
   auto init_acc = [&](const v4u (&ps)[4]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, v4u{0u, 0u, 0u, ps[i][3] & keep}),
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, v4u{0u, 0u, 0u, ps[i][3]}),
                                                            __builtin_bit_cast(v8bf, v4u{0u, 0u, 0u, ps[2 + j][3]}),
                                                            v16f{}, 0, 0, 0);
   };
   auto epilogue = [&](v4u (&ps)[4]) {
     if constexpr (ASYM) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ps[i][e] &= keep;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps[i][3] = 0u;
+      for (int i = 0; i < 2; ++i) ps[i][3] = 0u;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
