@@ -34,7 +34,9 @@ ahead of the GPU: for decode-sized and KV-cache steps, which are shorter
 than the host's Python calls, that is the kernel's own duration and the
 roofline uses it (HBM-bound: the weights or the cache are streamed once).
 The CPU oracle is timed on a bounded sample of the same workload as a
-reported baseline (not a target).
+reported baseline (not a target).  "device" names the GPU (architecture, CU
+count, memory, HIP and ROCm versions) and the shader clock rocm-smi reports
+right after the timed region.
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -323,6 +326,40 @@ def blas_info():
     return {"threads": len(os.sched_getaffinity(0)), "library": "unknown", "file": ""}
 
 
+def device_info(torch):
+    """The GPU the line was measured on: name, architecture, CU count, memory,
+    the HIP runtime torch was built against, and the shader clock that
+    rocm-smi reports right after the timed region (None when unavailable)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "cus": p.multi_processor_count, "memory_gib": round(p.total_memory / 2**30, 1),
+            "hip": torch.version.hip, "rocm": None, "sclk_mhz": None}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        cards = json.loads(r.stdout) if r.returncode == 0 else {}
+        for card in cards.values():
+            for k, v in card.items():
+                if "sclk" in k.lower() and "speed" in k.lower():
+                    info["sclk_mhz"] = float(str(v).strip("()Mhz").split()[0])
+                    break
+            break
+    except Exception:
+        pass
+    return info
+
+
+def emit(out, torch):
+    """print the result line, with the device it was measured on"""
+    if "device" not in out:
+        out["device"] = device_info(torch)
+    print(json.dumps(out), flush=True)
+
+
 def spread(xs):
     """median, p10 and p90 of a list of per-launch durations (us)."""
     a = np.asarray(xs, dtype=np.float64)
@@ -438,6 +475,7 @@ def main_kv(args, torch, rw4, gu, dev):
         "rotate_queries": {"kernel": "rotate_h128_kernel", "avg_launch_us": r_b2b, "gbps": rb_gbps,
                            "frac_hbm": rb_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": rbytes, "host_ahead": r_ahead},
     }
+    out["device"] = device_info(torch)  # the clock as the timed region left it, before the CPU leg
     if not args.no_cpu_baseline:
         import oracle
         from tests.helpers import spec_of
@@ -456,7 +494,7 @@ def main_kv(args, torch, rw4, gu, dev):
                                                          f"dequantize (float64 numpy)", "seconds": dt,
                                "os_cpu_count": os.cpu_count(), "blas": bi["library"], "blas_file": bi["file"],
                                "blas_threads": bi["threads"]}
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 def main_rrs_reorder(args, torch, rw4, gu, dev):
@@ -522,7 +560,7 @@ def main_rrs_reorder(args, torch, rw4, gu, dev):
                        "gbps": pbytes / p_us / 1e3, "frac_hbm": pbytes / p_us / 1e3 / PEAK_HBM_GBPS},
            "quantize": {"kernels": "rrs_chanmax + chanmax_reduce + rrs_rank + quant_rrs_order", "avg_us": q_us,
                         "algorithmic_bytes": qbytes, "gbps": qbytes / q_us / 1e3}}
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 def main_decode_fused(args, torch, rw4, gu, dev):
@@ -581,7 +619,7 @@ def main_decode_fused(args, torch, rw4, gu, dev):
            "roofline": {"bound": "hbm", "achieved": hbm / f_us / 1e3, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": hbm / f_us / 1e3 / PEAK_HBM_GBPS, "traffic": None, "kernel": "decode_fused_kernel",
                         "avg_launch_us": f_us, "algorithmic_bytes": hbm}}
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 def main_asym(args, torch, rw4, gu, dev):
@@ -646,7 +684,7 @@ def main_asym(args, torch, rw4, gu, dev):
                         "frac_fp6": ops / g_us / 1e6 / PEAK_F6_TFLOPS, "traffic": None, "kernel": gk, "avg_launch_us": g_us},
            "quantize": {"kernel": "quant_h128_act_kernel (asymmetric)", "avg_us": q_us, "algorithmic_bytes": qbytes,
                         "gbps": qbytes / q_us / 1e3, "frac_hbm": qbytes / q_us / 1e3 / PEAK_HBM_GBPS}}
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 def main_mixed(args, torch, rw4, gu, dev, n8=4):
@@ -714,7 +752,7 @@ def main_mixed(args, torch, rw4, gu, dev, n8=4):
                         "frac": ops / g_us / 1e6 / PEAK_I8_TOPS, "peak_fp6": PEAK_F6_TFLOPS,
                         "frac_fp6": ops / g_us / 1e6 / PEAK_F6_TFLOPS, "traffic": None, "kernel": gemm_kernel_for(M, N),
                         "avg_launch_us": g_us, "note": "ops of the layer (2 M N K), the GEMM runs over K + 128 n8"}}
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 def main():
@@ -937,6 +975,7 @@ def main():
         "step_gpu_us": step_gpu_us,
         "instrumented_steps": sum(1 for e in events if e),
     }
+    out["device"] = device_info(torch)  # the clock as the timed region left it, before the CPU leg
 
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or (M if M <= 64 else max(16, min(M, 256 * 4096 // K)))
@@ -958,7 +997,7 @@ def main():
                                "os_cpu_count": os.cpu_count(), "blas": bi["library"], "blas_file": bi["file"],
                                "blas_threads": bi["threads"]}
         log(f"cpu oracle: {passes} x {rows} rows in {dt:.2f} s = {cpu_tops * 1e3:.3f} GOPS on {threads} threads")
-    print(json.dumps(out), flush=True)
+    emit(out, torch)
 
 
 if __name__ == "__main__":
