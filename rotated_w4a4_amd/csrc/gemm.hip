@@ -1292,6 +1292,7 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
   const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
   const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
   const float flip = parity_sign(lane & 15);
+  const float s7 = signed_const(1.0f / 7.0f, flip);  // the encoder's signed 1/7
   auto quantize = [&](int64_t it) __attribute__((always_inline)) {
     const int64_t g0 = it * C::GB + wave * C::NS;
     // slices past K: zero codes and scales (gemm_small_kernel's loads read zeros there)
@@ -1327,7 +1328,7 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
       const int ns = q & 1;
       const int64_t m = q >> 1;
       const int gl = wave * C::NS + ns;
-      const uint32_t packed = encode8_rcp(v, mx, flip, (word & 1) != 0);
+      const uint32_t packed = encode8_rcp(v, mx, s7, (word & 1) != 0);
       if (m < M && g0 + ns < SL) {
         *reinterpret_cast<uint32_t*>(Ab + gl * 64 + m * (C::AROW + 1) * 16 + word * 4) = packed;
         if (sub == 0) saT[gl * 16 + m] = mx * post;

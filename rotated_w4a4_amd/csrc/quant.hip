@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   const float c1 = parity_sign(lane & 5), c2 = parity_sign(lane & 6);
   const float c7 = parity_sign(lane & 4), c8 = parity_sign(lane & 8);
   const float flip = parity_sign(lane & 15);
+  const float s7 = signed_const(1.0f / 7.0f, flip);  // the encoder's signed 1/7
 
   // rows at or past the end get an empty range: the prefetch past the last
   // row is issued like any other (so every path has the same memory
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
           float sc = m * post_scale, sc_l = 0.0f;
           if (is8) {
             float mm = m;
-            if (m > 0.0f && m < kTinyMax) {
+            if (tiny_positive(m)) {
 #pragma unroll
               for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
               mm = m * kTinyLift;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
             sc = m * post8h;
             sc_l = m * post8l;
           } else {
-            packed = encode8_rcp(v, m, flip, odd);
+            packed = encode8_rcp(v, m, s7, odd);
           }
           __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b32(packed_l, rq, int(l_off), 0, 0);
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
           continue;
         }
       }
-      const uint32_t packed = encode8_rcp(v, m, flip, odd);
+      const uint32_t packed = encode8_rcp(v, m, s7, odd);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * post_scale), rs, int(s_off), 0, 0);
       __builtin_amdgcn_sched_barrier(0);

@@ -343,6 +343,11 @@ __device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f 
 // (exact) so the reciprocal stays finite.  Codes are identical either way.
 constexpr float kTinyMax = 0x1p-100f;
 constexpr float kTinyLift = 0x1p64f;
+// 0 < m < kTinyMax for m >= +0 (or NaN, which is not tiny), as one unsigned
+// comparison of the bit patterns: +0 wraps to the largest value
+__device__ __forceinline__ bool tiny_positive(float m) {
+  return __float_as_uint(m) - 1u < __float_as_uint(kTinyMax) - 1u;
+}
 
 // sign = -1 encodes the negated values (for inputs that carry a known sign
 // flip); rounding to nearest even is symmetric, so the codes are exactly
@@ -423,17 +428,20 @@ __device__ __forceinline__ float row16_max_dpp(float m) {
 // m / 7: a few ulp from the rounded quotient, which moves v * 7 / m by
 // ~1e-6 of a code step at most.  (The reciprocal flushes subnormal
 // results, so it is taken of m / 7, whose reciprocal is normal for every
-// finite m >= 2^-100; 1 / m is not, for m above 2^126.)
-__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float flip, bool odd) {
+// finite m >= 2^-100; 1 / m is not, for m above 2^126.)  s7 is the lane's
+// signed 1/7, signed_const(1.0f / 7.0f, flip), made once by the caller.
+__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float s7, bool odd) {
   float mm = m;
-  if (__builtin_amdgcn_ballot_w64(m > 0.0f && m < kTinyMax) != 0) {
-    if (m > 0.0f && m < kTinyMax) {
+  if (__builtin_amdgcn_ballot_w64(tiny_positive(m)) != 0) {
+    if (tiny_positive(m)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] *= kTinyLift;
       mm = m * kTinyLift;
     }
   }
-  const float inv = mm > 0.0f ? __builtin_amdgcn_rcpf(mm * signed_const(1.0f / 7.0f, flip)) : 0.0f;
+  // m = 0: the reciprocal is infinite and the select gives 0
+  const float r = __builtin_amdgcn_rcpf(mm * s7);
+  const float inv = mm > 0.0f ? r : 0.0f;
   uint32_t b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
