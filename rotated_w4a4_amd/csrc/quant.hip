@@ -916,17 +916,20 @@ __global__ __launch_bounds__(1024) void chanmax_reduce_kernel(const float* __res
 
 // rank(j) = #{i : m_i > m_j} + #{i < j : m_i == m_j}: the position of
 // channel j in decreasing order of the maxima, equal maxima by increasing
-// index (unique ranks, so order is a permutation).  A block takes 16
-// channels; its 16 groups of 16 threads count over 16 slices of the
-// channels, then add up.  The channel of rank 128 g opens group g, and its
-// maximum is the group's smoothing scale.
+// index (unique ranks, so order is a permutation).  The maxima are >= +0,
+// so their bit patterns order like the values, and the order is that of
+// the 44-bit keys bits(m_i) 2^13 + (8191 - i) (K <= 8192): i precedes j
+// exactly when key_i > key_j, one 64-bit comparison with no branch.  A
+// block takes 16 channels; its 16 groups of 16 threads count over 16
+// slices of the keys, then add up.  The channel of rank 128 g opens group
+// g, and its maximum is the group's smoothing scale.
 __global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__ m, int64_t K,
                                                        int32_t* __restrict__ order, float* __restrict__ s_g) {
-  extern __shared__ float ms[];  // K maxima, then 256 partial counts
-  int* cnt = reinterpret_cast<int*>(ms + K);
+  extern __shared__ v4u32 keys4[];  // K keys (two per 16 bytes), then 256 partial counts
+  int* cnt = reinterpret_cast<int*>(keys4 + K / 2);
   {
-    // K <= 8192: at most 8 16-byte loads per thread, all issued before the
-    // first LDS store (one memory latency instead of one per load)
+    // K <= 8192: at most 8 16-byte loads of 4 maxima per thread, all issued
+    // before the first LDS store (one memory latency instead of one per load)
     const __amdgpu_buffer_rsrc_t rm = buf_rsrc(m, K * 4);
     v4u32 t[8];
 #pragma unroll
@@ -937,33 +940,40 @@ __global__ __launch_bounds__(256) void rrs_rank_kernel(const float* __restrict__
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t i4 = threadIdx.x + 256 * u;
-      if (i4 < K / 4) *reinterpret_cast<v4u32*>(ms + i4 * 4) = t[u];
+      if (i4 < K / 4) {
+        uint32_t w[8];  // keys of channels 4 i4 .. 4 i4 + 3 as (low, high) words
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t idx = uint32_t(i4 * 4 + q);
+          w[2 * q] = (t[u][q] << 13) | (8191u - idx);
+          w[2 * q + 1] = t[u][q] >> 19;
+        }
+        keys4[i4 * 2] = v4u32{w[0], w[1], w[2], w[3]};
+        keys4[i4 * 2 + 1] = v4u32{w[4], w[5], w[6], w[7]};
+      }
     }
   }
   __syncthreads();
+  auto key = [](uint32_t lo, uint32_t hi) { return (uint64_t(hi) << 32) | lo; };
   const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
-  const int j = int(blockIdx.x) * 16 + c;
-  const float mj = j < K ? ms[j] : 0.0f;
-  const int slice = int(K / 16);  // a multiple of 8 (K % 128 == 0)
+  const int j = int(blockIdx.x) * 16 + c;  // < K: the grid has K / 16 blocks
+  const v4u32 kw = keys4[j / 2];
+  const uint64_t kj = (j & 1) ? key(kw[2], kw[3]) : key(kw[0], kw[1]);
+  const int pairs = int(K / 32);  // 16-byte reads per slice of K / 16 keys (K % 128 == 0)
+  const v4u32* k2 = keys4 + r * pairs;
   int n = 0;
-  // 16-byte LDS reads, eight channels per step, unrolled so that the reads
-  // of several steps are in flight together
-  const float4* m4 = reinterpret_cast<const float4*>(ms + r * slice);
-#pragma unroll 4
-  for (int i8 = 0; i8 < slice / 8; ++i8) {
-    const float4 a = m4[2 * i8], b = m4[2 * i8 + 1];
-    const int i0 = r * slice + 8 * i8;
-    const float mi[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) n += (mi[e] > mj) || (mi[e] == mj && i0 + e < j);
+#pragma unroll 8
+  for (int i = 0; i < pairs; ++i) {
+    const v4u32 w = k2[i];
+    n += int(key(w[0], w[1]) > kj) + int(key(w[2], w[3]) > kj);
   }
   cnt[threadIdx.x] = n;
   __syncthreads();
-  if (r == 0 && j < K) {
+  if (r == 0) {
     int rank = 0;
     for (int k = 0; k < 16; ++k) rank += cnt[k * 16 + c];
     order[rank] = int32_t(j);
-    if ((rank & (kGroup - 1)) == 0) s_g[rank / kGroup] = mj;
+    if ((rank & (kGroup - 1)) == 0) s_g[rank / kGroup] = __uint_as_float(uint32_t(kj >> 13));
   }
 }
 
@@ -1595,7 +1605,7 @@ hipError_t launch_rrs_reorder_src(const Src& src, int64_t K, int log2b, int64_t 
   float* m = ws + int64_t(kChanmaxBlocks) * K;
   float* smooth = m + K;
   const int grid = grid_for_waves(M, 256 * 16);
-  const int rank_lds = int(K * 4 + 256 * 4);
+  const int rank_lds = int(K * 8 + 256 * 4);
   auto run = [&](auto e_const) {
     constexpr int E = decltype(e_const)::value;
     hipLaunchKernelGGL((rrs_chanmax_kernel<E, Src>), dim3(kChanmaxBlocks), dim3(256), 0, st, src, M, log2b, partial);
@@ -1624,7 +1634,7 @@ hipError_t launch_rrs_reorder_full(const void* x, bool bf16, int64_t ldx, int64_
   float* m = ws + int64_t(kChanmaxBlocks) * K;
   float* smooth = m + K;
   const int grid = grid_for_waves(M, 256 * 16);
-  const int rank_lds = int(K * 4 + 256 * 4);
+  const int rank_lds = int(K * 8 + 256 * 4);
   if (bf16)
     hipLaunchKernelGGL((rrs_chanmax_full_kernel<NC, true>), dim3(kChanmaxBlocks), dim3(256), 0, st, x, ldx, M, partial);
   else
