@@ -147,6 +147,29 @@ def test_down_proj_full():
     _gemm_parity(wl, qa, sa, qw, sw, rows, aref, wref, a_rows_in_ref=rows)
 
 
+def test_down_proj_whole_output():
+    """The whole 4096 x 4096 down_proj output from identical codes, element by
+    element (the codes themselves are compared in test_down_proj_full), in
+    row chunks so that the oracle's float64 products stay small."""
+    wl = datagen.make("down_proj")
+    t = gu.transform_for(wl)
+    qa, sa, _ = gu.quantize(t, gu.x_to_device(wl.x, wl.x_dtype), wl.mode)
+    qw, sw = rw4.pack_weight(t, torch.from_numpy(wl.w).to(gu.DEV), "kn")
+    y32 = gu.to_np(rw4.w4a4_gemm(qa, sa, qw, sw, torch.float32))
+    qa_np, sa_np, qw_np, sw_np = gu.to_np(qa), gu.to_np(sa), gu.to_np(qw), gu.to_np(sw)
+    ca_all, cw = oracle.unpack_int4(qa_np), oracle.unpack_int4(qw_np)
+    worst = 0.0
+    for r0 in range(0, wl.M, 512):
+        rows = slice(r0, min(r0 + 512, wl.M))
+        y_ref = oracle.w4a4_gemm(qa_np[rows], sa_np[rows], qw_np, sw_np, "f64")
+        bound = epilogue_error_bound(ca_all[rows], sa_np[rows], cw, sw_np, 128, oracle.group_accumulators)
+        _, w = assert_gemm_close(y32[rows], y_ref, bound, f"down_proj rows {r0}..: GEMM from identical codes")
+        worst = max(worst, w)
+        print(f"down_proj whole output: rows {r0}..{rows.stop} match (worst {w:.2f} of the element bound)",
+              flush=True)
+    print(f"down_proj whole output: {wl.M}x{wl.N} outputs, worst {worst:.2f} of the element bound", flush=True)
+
+
 def test_rrs_full():
     wl = datagen.make("rrs")
     t, x, qa, sa, aref = _quant_parity(wl)
