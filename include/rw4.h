@@ -185,7 +185,11 @@ int64_t rw4_transform_k(const rw4_transform* t);
  * normalization (folded into the stored scale), so every block's sum of |x|
  * must stay below FLT_MAX: |x| <= 2.6e36 for b = 128 and <= 8.3e34 for
  * b = 4096 always suffices (bf16 inputs reach 3.4e38).  Larger inputs give
- * infinite scales; they are not detected.
+ * infinite scales; they are not detected.  Inputs must be finite: a NaN or
+ * infinity spreads through the transform over its whole block, and the codes
+ * and scales of the groups it reaches are unspecified (in RRS mode the group
+ * maxima it reaches, and so every row's scales for those groups); no error is
+ * reported.
  *   qa [M, K/2] uint8 packed codes (output)
  *   sa [M, K/128] fp32 scales (output)
  *   workspace: RRS only, >= K/128 fp32 device floats, 16-byte aligned,
