@@ -39,19 +39,23 @@
  *     problem definition), but the symmetric scale max/7 maps every value
  *     into [-7, 7] (-8 never arises), and this layout stores exactly that
  *     domain: a code of -8 cannot be represented.  Every 32-bit
- *     little-endian word w (bytes 4w..4w+3 of a row) holds the codes
+ *     little-endian word w (bytes 4w..4w+3 of a row) carries the codes
  *     c_0..c_7 of channels 8w..8w+7 as sign-magnitude (|c| in 3 bits, sign
- *     1 = negative, zero with sign 0), bit t of code e (t = 0, 1, 2 for |c|,
- *     t = 3 for the sign) at position P[w % 2][e][t]:
- *       even words: (0,1,2,5) (6,7,8,11) (12,13,14,17) (18,19,20,23)
- *                   (24,25,26,29) (30,31,16,3) (4,21,22,9) (10,27,28,15)
- *       odd words:  (0,17,18,5) (6,23,24,11) (12,29,30,1) (2,3,4,7)
- *                   (8,9,10,13) (14,15,16,19) (20,21,22,25) (26,27,28,31)
- *     A word pair (W0, W1) = words 2j, 2j+1 opens into the dense 96-bit
- *     string of its 16 codes' FP6 E2M3 encodings (code k, as the subnormal
- *     c/8, at bits 6k..6k+5) as D0 = W0 & 0xE79E79E7, D2 = W1 & 0x9E79E79E,
- *     D1 = (rot16(V) & 0x18611861) | (V & ~0x18611861) with
- *     V = (W0 & ~0xE79E79E7) | (W1 & ~0x9E79E79E): the GEMM's operand form.
+ *     1 = negative, zero with sign 0), and the words of each 16-byte chunk
+ *     pair up as (4j, 4j+3) and (4j+1, 4j+2), sharing their bits: the
+ *     pair's 16 codes (the first word's c_0..c_7 as k = 0..7, its
+ *     partner's as k = 8..15) form the dense 96-bit string X of their FP6
+ *     E2M3 encodings (code k, as the subnormal c/8, at bits 6k..6k+5:
+ *     |c| in bits 0-2, sign in bit 5), and the pair's words a (first) and
+ *     b (partner) hold
+ *       a = (X[0:32] & A) | (X[32:64] & ~A),
+ *       b = (X[64:96] & C) | (X[32:64] & ~C),  A = 0xE79E79E7, C = 0x9E79E79E,
+ *     so X[0:32] = a & A, X[64:96] = b & C, X[32:64] = (a & ~A) | (b & ~C):
+ *     the GEMM's operand form, opened with two masks.  Bit t of code k
+ *     (t = 0, 1, 2 for |c|, 3 for the sign) sits in word (a or b) at bit:
+ *       k  0-4: a:6k+(0,1,2,5);   k 5: a30 a31 b0 a3;  k 6: a4 b5 b6 a9;
+ *       k 7: a10 b11 b12 a15;  k 8: a16 b17 b18 a21;  k 9: a22 b23 b24 a27;
+ *       k 10: a28 b29 b30 b1;  k 11-15: b:6k-64+(0,1,2,5).
  *     qa is [M, K/2] bytes, qw is [N, K/2] bytes, rows contiguous.
  *   - Scales: fp32, row-major, sa [M, G], sw [N, G].
  *   - stream is a hipStream_t (NULL = the null stream).  Every call checks
@@ -222,14 +226,12 @@ rw4_status rw4_quantize_act_static(const rw4_transform* t, rw4_act_mode mode, co
  * the transformed row x~ (block-128 Hadamard only):
  *   lo = min(0, min x~), hi = max(0, max x~), s = (hi - lo) / 15,
  *   z = rne(-lo / s), q = clamp(rne(x~ / s) + z, 0, 15);  x~ ~ s (q - z).
- * qa [M][K/2]: unsigned codes, 8 per 32-bit word w, bit t of code e at
- * position U[w % 2][e][t] (NOT the signed form of rw4_quantize_act):
- *   even words: (0,1,2,3) (6,7,8,9) (12,13,14,15) (18,19,20,21)
- *               (24,25,26,27) (30,31,16,17) (4,5,22,23) (10,11,28,29)
- *   odd words:  (0,1,18,19) (6,7,24,25) (12,13,30,31) (2,3,4,5)
- *               (8,9,10,11) (14,15,16,17) (20,21,22,23) (26,27,28,29)
- * (a word pair opens into the codes' FP6 E2M3 encodings, u/8, as in the
- * signed form with masks 0xCF3CF3CF, 0x3CF3CF3C, 0x30C330C3); sa [M][K/128] fp32 scales s;
+ * qa [M][K/2]: unsigned codes in the paired form of rw4_quantize_act's
+ * codes (NOT the same bits): the FP6 E2M3 encoding of u/8 is u itself
+ * (bits 0-3), and the masks are A = 0xCF3CF3CF, C = 0x3CF3CF3C; bit t of
+ * code k of a pair: k 0-4: a:6k+t;  k 5: a30 a31 b0 b1;  k 6-10:
+ * a:6k-32+(0,1), b:6k-32+(2,3);  k 11-15: b:6k-64+t
+ * (the same two-mask opening as the signed form); sa [M][K/128] fp32 scales s;
  * za [M][K/128] fp32 zero points (integers 0..15).  A group of zeros gets
  * s = 0, z = 0 and codes 0.  Arguments and errors otherwise as
  * rw4_quantize_act; other transforms: RW4_ERR_UNSUPPORTED. */

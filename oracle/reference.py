@@ -86,7 +86,7 @@ __all__ = [
     "quantize_groups", "quantize_rrs", "rrs_channel_order", "quantize_per_channel", "permute_codes",
     "quantize_groups_asym", "UMAX", "pack_uint4", "unpack_uint4", "dequantize_asym", "weight_code_sums",
     "w4a4_gemm_asym", "Q8MAX", "quantize_groups_mixed", "split_q8", "extend_weight_groups", "mixed_gemm_reference",
-    "pack_int4", "unpack_int4", "SIGNED_LAYOUT", "UNSIGNED_LAYOUT",
+    "pack_int4", "unpack_int4", "SIGNED_PAIR_LAYOUT", "UNSIGNED_PAIR_LAYOUT", "CHUNK_PAIRS",
     "group_accumulators", "dequant_gemm",
     "round_bf16", "round_output", "dequantize", "round_dequant_output",
     "quantize_act", "pack_weight", "w4a4_gemm", "layer_forward",
@@ -420,79 +420,92 @@ def quantize_per_channel(wt_rows: np.ndarray):
 # Packing
 # --------------------------------------------------------------------------
 
-# Bit positions, inside a little-endian 32-bit word, of the four bits of
-# each of its 8 codes (code e of the word = channel 8 w + e of the row for
-# word w): signed codes (|c| bit 0, bit 1, bit 2, sign), unsigned codes
-# (bits 0-3).  Even words use the first table, odd words the second.  The
-# tables are the layout of the stored form (no page fixes one): read as a
-# pair, words 2j and 2j + 1 hold the 16 codes' FP6 E2M3 encodings (sign,
-# two zero exponent bits, the magnitude as subnormal mantissa: the value
-# c / 8; an unsigned u <= 15 is the E2M3 encoding of u / 8 with a zero
-# sign bit) such that, with f_k the 6-bit encoding of code k, the dense
-# 96-bit string sum_k f_k << 6 k splits into its three 32-bit words as
-#   D0 = W0 & A,  D2 = W1 & C,
-#   D1 = (rot16(V) & E) | (V & ~E),  V = (W0 & ~A) | (W1 & ~C)
-# with masks A = 0xE79E79E7, C = 0x9E79E79E, E = 0x18611861 (signed) and
-# A = 0xCF3CF3CF, C = 0x3CF3CF3C, E = 0x30C330C3 (unsigned).  The tests pin
-# the tables to this identity by brute force.
-SIGNED_LAYOUT = (
-    ((0, 1, 2, 5), (6, 7, 8, 11), (12, 13, 14, 17), (18, 19, 20, 23),
-     (24, 25, 26, 29), (30, 31, 16, 3), (4, 21, 22, 9), (10, 27, 28, 15)),
-    ((0, 17, 18, 5), (6, 23, 24, 11), (12, 29, 30, 1), (2, 3, 4, 7),
-     (8, 9, 10, 13), (14, 15, 16, 19), (20, 21, 22, 25), (26, 27, 28, 31)),
+# The stored form: 4 bits per code, 8 codes per little-endian 32-bit word
+# (code e of word w = channel 8 w + e of the row), the words of each 16-byte
+# chunk paired as (4 j, 4 j + 3) and (4 j + 1, 4 j + 2).  A pair holds the
+# 16 codes of its two words (k = 0..7 those of the first word, the one whose
+# index has bit 1 clear, 8..15 those of its partner); the table below gives,
+# for bit t of code k ((|c| bit 0, bit 1, bit 2, sign) signed, bits 0-3
+# unsigned), the word of the pair (0 first, 1 partner) and the bit position
+# in it.  No page fixes a layout.  This one is built so that, with f_k the
+# 6-bit FP6 E2M3 encoding of code k (sign, two zero exponent bits, the
+# magnitude as subnormal mantissa: the value c / 8; an unsigned u <= 15 is
+# the E2M3 encoding of u / 8 with a zero sign bit), the dense 96-bit string
+# sum_k f_k << 6 k splits into its three 32-bit words as
+#   D0 = a & A,  D2 = b & C,  D1 = (a & ~A) | (b & ~C)
+# for the pair's words a, b, with masks A = 0xE79E79E7, C = 0x9E79E79E
+# (signed) and A = 0xCF3CF3CF, C = 0x3CF3CF3C (unsigned).  The tests pin the
+# tables to this identity by brute force.
+SIGNED_PAIR_LAYOUT = (
+    ((0, 0), (0, 1), (0, 2), (0, 5)), ((0, 6), (0, 7), (0, 8), (0, 11)),
+    ((0, 12), (0, 13), (0, 14), (0, 17)), ((0, 18), (0, 19), (0, 20), (0, 23)),
+    ((0, 24), (0, 25), (0, 26), (0, 29)), ((0, 30), (0, 31), (1, 0), (0, 3)),
+    ((0, 4), (1, 5), (1, 6), (0, 9)), ((0, 10), (1, 11), (1, 12), (0, 15)),
+    ((0, 16), (1, 17), (1, 18), (0, 21)), ((0, 22), (1, 23), (1, 24), (0, 27)),
+    ((0, 28), (1, 29), (1, 30), (1, 1)), ((1, 2), (1, 3), (1, 4), (1, 7)),
+    ((1, 8), (1, 9), (1, 10), (1, 13)), ((1, 14), (1, 15), (1, 16), (1, 19)),
+    ((1, 20), (1, 21), (1, 22), (1, 25)), ((1, 26), (1, 27), (1, 28), (1, 31)),
 )
-UNSIGNED_LAYOUT = (
-    ((0, 1, 2, 3), (6, 7, 8, 9), (12, 13, 14, 15), (18, 19, 20, 21),
-     (24, 25, 26, 27), (30, 31, 16, 17), (4, 5, 22, 23), (10, 11, 28, 29)),
-    ((0, 1, 18, 19), (6, 7, 24, 25), (12, 13, 30, 31), (2, 3, 4, 5),
-     (8, 9, 10, 11), (14, 15, 16, 17), (20, 21, 22, 23), (26, 27, 28, 29)),
+UNSIGNED_PAIR_LAYOUT = (
+    ((0, 0), (0, 1), (0, 2), (0, 3)), ((0, 6), (0, 7), (0, 8), (0, 9)),
+    ((0, 12), (0, 13), (0, 14), (0, 15)), ((0, 18), (0, 19), (0, 20), (0, 21)),
+    ((0, 24), (0, 25), (0, 26), (0, 27)), ((0, 30), (0, 31), (1, 0), (1, 1)),
+    ((0, 4), (0, 5), (1, 6), (1, 7)), ((0, 10), (0, 11), (1, 12), (1, 13)),
+    ((0, 16), (0, 17), (1, 18), (1, 19)), ((0, 22), (0, 23), (1, 24), (1, 25)),
+    ((0, 28), (0, 29), (1, 30), (1, 31)), ((1, 2), (1, 3), (1, 4), (1, 5)),
+    ((1, 8), (1, 9), (1, 10), (1, 11)), ((1, 14), (1, 15), (1, 16), (1, 17)),
+    ((1, 20), (1, 21), (1, 22), (1, 23)), ((1, 26), (1, 27), (1, 28), (1, 29)),
 )
+# word pairs of a 16-byte chunk (first word, partner)
+CHUNK_PAIRS = ((0, 3), (1, 2))
 
 
 def _pack_words(bits: np.ndarray, layout) -> np.ndarray:
-    """bits [..., K, 4] (0/1) -> bytes [..., K/2] through the position tables."""
-    if bits.shape[-2] % 8:
-        raise ValueError("row length must be a multiple of 8")
-    nw = bits.shape[-2] // 8
-    b = bits.reshape(bits.shape[:-2] + (nw, 8, 4)).astype(np.uint64)
-    words = np.zeros(bits.shape[:-2] + (nw,), dtype=np.uint64)
-    for parity in (0, 1):
-        sel = words[..., parity::2]
-        bp = b[..., parity::2, :, :]
-        for e in range(8):
+    """bits [..., K, 4] (0/1) -> bytes [..., K/2] through the pair table."""
+    if bits.shape[-2] % 32:
+        raise ValueError("row length must be a multiple of 32 codes (16-byte chunks)")
+    nc = bits.shape[-2] // 32
+    b = bits.reshape(bits.shape[:-2] + (nc, 4, 8, 4)).astype(np.uint64)
+    words = np.zeros(bits.shape[:-2] + (nc, 4), dtype=np.uint64)
+    for first, partner in CHUNK_PAIRS:
+        own = (first, partner)
+        for k in range(16):
+            src = own[k // 8]
             for t in range(4):
-                sel |= bp[..., e, t] << np.uint64(layout[parity][e][t])
-        words[..., parity::2] = sel
+                role, pos = layout[k][t]
+                words[..., own[role]] |= b[..., src, k % 8, t] << np.uint64(pos)
     out = np.empty(words.shape + (4,), dtype=np.uint8)
     for k in range(4):
         out[..., k] = (words >> np.uint64(8 * k)) & np.uint64(0xFF)
-    return out.reshape(bits.shape[:-2] + (nw * 4,))
+    return out.reshape(bits.shape[:-2] + (nc * 16,))
 
 
 def _unpack_words(packed: np.ndarray, layout) -> np.ndarray:
-    """bytes [..., 4 W] -> bits [..., 8 W, 4] through the position tables."""
+    """bytes [..., 16 C] -> bits [..., 32 C, 4] through the pair table."""
     p = np.asarray(packed, dtype=np.uint8)
-    if p.shape[-1] % 4:
-        raise ValueError("packed row length must be a multiple of 4 bytes")
-    nw = p.shape[-1] // 4
-    q = p.reshape(p.shape[:-1] + (nw, 4)).astype(np.uint64)
+    if p.shape[-1] % 16:
+        raise ValueError("packed row length must be a multiple of 16 bytes")
+    nc = p.shape[-1] // 16
+    q = p.reshape(p.shape[:-1] + (nc, 4, 4)).astype(np.uint64)
     words = q[..., 0] | (q[..., 1] << np.uint64(8)) | (q[..., 2] << np.uint64(16)) | (q[..., 3] << np.uint64(24))
-    bits = np.zeros(p.shape[:-1] + (nw, 8, 4), dtype=np.int64)
-    for parity in (0, 1):
-        w = words[..., parity::2]
-        for e in range(8):
+    bits = np.zeros(p.shape[:-1] + (nc, 4, 8, 4), dtype=np.int64)
+    for first, partner in CHUNK_PAIRS:
+        own = (first, partner)
+        for k in range(16):
+            dst = own[k // 8]
             for t in range(4):
-                bits[..., parity::2, e, t] = ((w >> np.uint64(layout[parity][e][t])) & np.uint64(1)).astype(np.int64)
-    return bits.reshape(p.shape[:-1] + (nw * 8, 4))
+                role, pos = layout[k][t]
+                bits[..., dst, k % 8, t] = ((words[..., own[role]] >> np.uint64(pos)) & np.uint64(1)).astype(np.int64)
+    return bits.reshape(p.shape[:-1] + (nc * 32, 4))
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """[R, K] codes in [-7, 7] -> [R, K/2] bytes, K a multiple of 8.
+    """[R, K] codes in [-7, 7] -> [R, K/2] bytes, K a multiple of 32.
 
     Sign-magnitude, 4 bits per code, 8 codes c_0..c_7 per little-endian
-    32-bit word (bytes 4w..4w+3 of the row); the bits of code e (|c_e| bit
-    0, 1, 2 and the sign, 1 = negative) sit at SIGNED_LAYOUT[w % 2][e].
-    Zero is always stored with sign 0.
+    32-bit word (bytes 4w..4w+3 of the row); the bits of the codes of a word
+    pair (|c| bit 0, 1, 2 and the sign, 1 = negative) sit where
+    SIGNED_PAIR_LAYOUT puts them.  Zero is always stored with sign 0.
     """
     c = np.asarray(codes)
     if c.min(initial=0) < QMIN or c.max(initial=0) > QMAX:
@@ -500,31 +513,31 @@ def pack_int4(codes: np.ndarray) -> np.ndarray:
     c = c.astype(np.int64)
     mag = np.abs(c)
     bits = np.stack([mag & 1, (mag >> 1) & 1, (mag >> 2) & 1, (c < 0).astype(np.int64)], axis=-1)
-    return _pack_words(bits, SIGNED_LAYOUT)
+    return _pack_words(bits, SIGNED_PAIR_LAYOUT)
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
     """Inverse of pack_int4: int8 codes [R, 2 * bytes]."""
-    bits = _unpack_words(packed, SIGNED_LAYOUT)
+    bits = _unpack_words(packed, SIGNED_PAIR_LAYOUT)
     mag = bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
     return np.where(bits[..., 3] == 1, -mag, mag).astype(np.int8)
 
 
 def pack_uint4(codes: np.ndarray) -> np.ndarray:
     """[R, K] unsigned codes 0..15 -> [R, K/2] bytes (the asymmetric form), K a
-    multiple of 8: 8 codes per little-endian 32-bit word, bit t of code e at
-    UNSIGNED_LAYOUT[w % 2][e][t]."""
+    multiple of 32: 8 codes per little-endian 32-bit word, the bits of a word
+    pair's codes where UNSIGNED_PAIR_LAYOUT puts them."""
     c = np.asarray(codes)
     if c.min(initial=0) < 0 or c.max(initial=0) > UMAX:
         raise ValueError("code out of the unsigned INT4 range [0, 15]")
     c = c.astype(np.int64)
     bits = np.stack([(c >> t) & 1 for t in range(4)], axis=-1)
-    return _pack_words(bits, UNSIGNED_LAYOUT)
+    return _pack_words(bits, UNSIGNED_PAIR_LAYOUT)
 
 
 def unpack_uint4(packed: np.ndarray) -> np.ndarray:
     """Inverse of pack_uint4: uint8 codes [R, 2 * bytes]."""
-    bits = _unpack_words(packed, UNSIGNED_LAYOUT)
+    bits = _unpack_words(packed, UNSIGNED_PAIR_LAYOUT)
     return (bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2) | (bits[..., 3] << 3)).astype(np.uint8)
 
 

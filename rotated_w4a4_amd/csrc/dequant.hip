@@ -12,7 +12,8 @@
 // covers the row's words with blocks of 64 to 256 lanes.  The product
 // code * scale is rounded once to fp32, then to bf16 (round to nearest even)
 // when asked.  A word gives its 8 codes as 6-bit sign-magnitude fields
-// (stored_fields: the inverse of the stored form's fold).
+// (pair_fields: the inverse of the stored form's fold, from the word and
+// its partner w ^ 3 in the same 16-byte chunk, read by this lane too).
 #include "rw4_device.h"
 #include "rw4_internal.h"
 
@@ -25,10 +26,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // word of the row
   if (j >= K / 8) return;
   const int64_t row = row0 + blockIdx.y;
-  const uint32_t w = reinterpret_cast<const uint32_t*>(q + row * (K / 2))[j];
+  const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + row * (K / 2));
+  const uint32_t w = qrow[j], wp = qrow[j ^ 3];  // K / 8 is a multiple of 16
   const float sc = s[row * (K >> log2g) + ((j * 8) >> log2g)];
   uint32_t lo, hi;
-  stored_fields<true>(w, (j & 1) != 0, lo, hi);
+  pair_fields<true>(w, wp, (j & 2) != 0, lo, hi);
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -83,11 +85,12 @@ __global__ __launch_bounds__(256) void dequant_asym_kernel(const uint8_t* __rest
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j >= K / 8) return;
   const int64_t row = row0 + blockIdx.y;
-  const uint32_t w = reinterpret_cast<const uint32_t*>(q + row * (K / 2))[j];
+  const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + row * (K / 2));
+  const uint32_t w = qrow[j], wp = qrow[j ^ 3];
   const int64_t gi = row * (K / kGroup) + (j * 8) / kGroup;
   const float sc = s[gi], zp = z[gi];
   uint32_t lo, hi;
-  stored_fields<false>(w, (j & 1) != 0, lo, hi);
+  pair_fields<false>(w, wp, (j & 2) != 0, lo, hi);
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = (float(field6(lo, hi, e)) - zp) * sc;
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __
   int sum = 0;
   for (int k = 0; k < 16; ++k) {
     uint32_t lo, hi;
-    stored_fields<true>(w[k], (k & 1) != 0, lo, hi);
+    pair_fields<true>(w[k], w[k ^ 3], (k & 2) != 0, lo, hi);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t f = field6(lo, hi, e);

@@ -8,9 +8,9 @@
 // block's partial result; the QuIP#/QTIP page, section 4.2, folds the
 // rotation into the weights so the GEMM itself is a plain product.)
 //
-// Operands.  Two words of the stored form (16 codes) open into the dense
-// string of the codes' FP6 E2M3 encodings with three masks and one 16-bit
-// rotation (rw4_device.h): a signed code c becomes the subnormal c / 8, an
+// Operands.  A pair of words of the stored form (16 codes) opens into the
+// dense string of the codes' FP6 E2M3 encodings with two masks and four
+// instructions (rw4_device.h): a signed code c becomes the subnormal c / 8, an
 // unsigned code u (asymmetric activations) the value u / 8.  The scaled
 // MFMA with format FP6 E2M3 on both sides and E8M0 operand scale 2^3 on
 // both therefore returns acc itself, exactly (integer products, partial
@@ -54,26 +54,23 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int kF6Scale = 127 + 3;  // E8M0 encoding of 2^3: FP6 code c / 8 times 2^3 is c
 constexpr int kF6 = 2;             // MFMA operand format FP6 E2M3
 
-// 4 stored words (32 codes, two word pairs) -> the 6-register FP6 operand
-// (the last two registers of the vector are not read by an FP6 MFMA).
+// 4 stored words (32 codes: the pairs (w0, w3) and (w1, w2)) -> the
+// 6-register FP6 operand (the last two registers of the vector are not
+// read by an FP6 MFMA).  Four instructions per pair: X[0:32] = a & A,
+// X[64:96] = b & C, X[32:64] = (a & ~A) | (b & ~C).
 template <bool SIGNED>
-__device__ __forceinline__ void open_pair(uint32_t w0, uint32_t w1, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
-  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC, kE = SIGNED ? kSgnE : kUnsE;
-  // six instructions per word pair; written out because the compiler
-  // otherwise splits the two combining steps into three
-  const uint32_t t = w1 & ~kC;
-  uint32_t v;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(v) : "v"(w0), "s"(~kA), "v"(t));  // (w0 & ~A) | t
-  const uint32_t r = __builtin_amdgcn_alignbit(v, v, 16);
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d1) : "s"(kE), "v"(r), "v"(v));  // (r & E) | (v & ~E)
-  d0 = w0 & kA;
-  d2 = w1 & kC;
+__device__ __forceinline__ void open_pair(uint32_t a, uint32_t b, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC;
+  const uint32_t t = b & ~kC;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d1) : "v"(a), "s"(~kA), "v"(t));  // (a & ~A) | t
+  d0 = a & kA;
+  d2 = b & kC;
 }
 template <bool SIGNED = true, class W>
 __device__ __forceinline__ v8i f6_operand(const W& w) {
   uint32_t d[6];
-  open_pair<SIGNED>(uint32_t(w[0]), uint32_t(w[1]), d[0], d[1], d[2]);
-  open_pair<SIGNED>(uint32_t(w[2]), uint32_t(w[3]), d[3], d[4], d[5]);
+  open_pair<SIGNED>(uint32_t(w[0]), uint32_t(w[3]), d[0], d[1], d[2]);
+  open_pair<SIGNED>(uint32_t(w[1]), uint32_t(w[2]), d[3], d[4], d[5]);
   return v8i{int(d[0]), int(d[1]), int(d[2]), int(d[3]), int(d[4]), int(d[5]), 0, 0};
 }
 
@@ -1328,7 +1325,7 @@ __global__ __launch_bounds__(kSmallThreads) void decode_fused_kernel(
       const int ns = q & 1;
       const int64_t m = q >> 1;
       const int gl = wave * C::NS + ns;
-      const uint32_t packed = encode8_rcp(v, mx, s7, (word & 1) != 0);
+      const uint32_t packed = encode8_rcp(v, mx, s7, (word & 2) != 0);
       if (m < M && g0 + ns < SL) {
         *reinterpret_cast<uint32_t*>(Ab + gl * 64 + m * (C::AROW + 1) * 16 + word * 4) = packed;
         if (sub == 0) saT[gl * 16 + m] = mx * post;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void quant_h128_kernel(Src src, int64_t G, int
     if constexpr (GS == 256) m = max_x<16>(m);
     uint32_t b[8];
     encode<8>(v[u], m, b, flip);
-    const uint32_t packed = pack8_bits(b, (sub & 1) != 0);
+    const uint32_t packed = pack8_bits(b, (sub & 2) != 0);
     const int64_t grp = g_blk + (wave * U + u) * 4 + seg;
     if (grp < G) {
       reinterpret_cast<uint32_t*>(qrow + grp * 64)[sub] = packed;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   // the row's buffer range (their loads read zeros, their stores vanish)
   const uint32_t x_off = uint32_t((grp * kGroup + sub * 8) * ES);
   const uint32_t q_off = uint32_t(grp * 64 + h128_lane_word(sub) * 4);
-  const bool odd = (h128_lane_word(sub) & 1) != 0;  // word parity selects the stored form's table
+  const bool role = (h128_lane_word(sub) & 2) != 0;  // bit 1 of the word index: its place in the word pair
   // MIXED: rows of G + n8 groups; a listed group (slot_of_group >= 0) keeps
   // its h plane in place and its l plane in the extra group G + slot
   const int64_t GX = MIXED ? G + n8 : G;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
         hi = row16_max_dpp(hi);
         nlo = row16_max_dpp(nlo);
         uint32_t z;
-        const uint32_t packed = encode8_asym(v, hi, nlo, z, odd);
+        const uint32_t packed = encode8_asym(v, hi, nlo, z, role);
         const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row * (G * 64), live ? G * 64 : 0);
         const __amdgpu_buffer_rsrc_t rs = buf_rsrc(s + row * G, live ? G * 4 : 0);
         const __amdgpu_buffer_rsrc_t rz = buf_rsrc(zs + row * G, live ? G * 4 : 0);
@@ -330,12 +330,12 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
               bh[e] = kRoundMagicBits + uint32_t(h);
               bl[e] = kRoundMagicBits + uint32_t(q8 - 15 * h);
             }
-            packed = pack8_bits(bh, odd);
-            packed_l = pack8_bits(bl, odd);
+            packed = pack8_bits(bh, role);
+            packed_l = pack8_bits(bl, role);
             sc = m * post8h;
             sc_l = m * post8l;
           } else {
-            packed = encode8_rcp(v, m, s7, odd);
+            packed = encode8_rcp(v, m, s7, role);
           }
           __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b32(packed_l, rq, int(l_off), 0, 0);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
           continue;
         }
       }
-      const uint32_t packed = encode8_rcp(v, m, s7, odd);
+      const uint32_t packed = encode8_rcp(v, m, s7, role);
       __builtin_amdgcn_raw_buffer_store_b32(packed, rq, int(q_off), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m * post_scale), rs, int(s_off), 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void quant_rowh_kernel(Src src, int64_t M, int
         const float m = group_absmax<E>(v, c);
         uint32_t b[8];
         encode<8>(&v[c * 8], m, b);
-        qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
+        qrow[c * 64 + lane] = pack8_bits(b, (lane & 2) != 0);
         if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
       }
     } else {
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void quant_rowh_kernel(Src src, int64_t M, int
       for (int c = 0; c < NC; ++c) {
         uint32_t b[8];
         encode<8>(&v[c * 8], m, b);
-        qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
+        qrow[c * 64 + lane] = pack8_bits(b, (lane & 2) != 0);
         if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
       }
     }
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(256) void quant_rrs_full_kernel(const void* __restr
       uint32_t b[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[c][e], k);
-      __builtin_amdgcn_raw_buffer_store_b32(pack8_bits(b, (h128_lane_word(lane & 15) & 1) != 0), rq, int(q_off[c]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(pack8_bits(b, (h128_lane_word(lane & 15) & 2) != 0), rq, int(q_off[c]), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a_t * (sg[c] * post_scale)), rs, int(s_off[c]), 0, 0);
     }
   }
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(64) void quant_givens_kernel(Src src, int64_t M, in
     float xv[2] = {x0, x1};
     uint32_t b[2];
     encode<2>(xv, m, b);
-    const uint32_t byte = pack2_bits_quad(b[0], b[1], lane & 3, ((lane >> 2) & 1) != 0);
+    const uint32_t byte = pack2_bits_quad(b[0], b[1], lane & 3, (lane & 8) != 0);
     const int64_t row = row0 + r;
     q[row * (G * 64) + grp * 64 + lane] = uint8_t(byte);
     if (lane == 0) s[row * G + grp] = m * (1.0f / 7.0f);
@@ -1006,7 +1006,7 @@ __device__ __forceinline__ void rrs_order_encode(float* v, const float* inv_s, c
   for (int c = 0; c < NC; ++c) {
     uint32_t b[8];
     encode<8>(&v[c * 8], m, b);
-    qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
+    qrow[c * 64 + lane] = pack8_bits(b, (lane & 2) != 0);
     if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = a_t * (s_g[c] * post_scale);
   }
 }
@@ -1202,7 +1202,7 @@ __global__ __launch_bounds__(256) void quant_row_perchannel_kernel(Src src, int6
     for (int c = 0; c < NC; ++c) {
       uint32_t b[8];
       encode<8>(&v[c * 8], m, b);
-      qrow[c * 64 + lane] = pack8_bits(b, (lane & 1) != 0);
+      qrow[c * 64 + lane] = pack8_bits(b, (lane & 2) != 0);
       if (sub == 0) s[row * G + c * 4 + (lane >> 4)] = m * post_scale;
     }
   }
@@ -1258,7 +1258,7 @@ __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __res
         const int i = int(threadIdx.x) + 256 * u;
         if (r < nr && i < W) {
           uint32_t lo, hi;
-          stored_fields<true>(wv[r][u], (i & 1) != 0, lo, hi);
+          pair_fields<true>(wv[r][u], xchg_lanes<3>(wv[r][u]), (i & 2) != 0, lo, hi);
           uint32_t f[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = field6(lo, hi, e);
@@ -1280,7 +1280,7 @@ __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __res
         uint32_t f[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = fr[src[u][e]];
-        dst[i] = pack8_fields(f, (i & 1) != 0);
+        dst[i] = pack8_fields(f, (i & 2) != 0);
       }
     }
   }

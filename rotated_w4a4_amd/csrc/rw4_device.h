@@ -183,24 +183,25 @@ __device__ __forceinline__ uint32_t rne_code_bits(float v, float inv) {
 
 // ---------------------------------------------------------------------------
 // Stored form of the codes: 4 bits per code, 8 codes per 32-bit word (code
-// e of word w = channel 8 w + e of the row), at bit positions fixed by one
-// table for even and one for odd words.  Its purpose: the GEMM reads codes
-// as FP6 E2M3 values (the gfx950 FP6 matrix-core rate is about 1.5x the
-// FP8 rate), whose encodings are 6 bits wide.  Let f_k be the 6-bit E2M3
-// encoding of code k of a word pair (words 2j, 2j + 1; 16 codes): signed
-// codes c as the subnormal c / 8 (sign bit 5, exponent bits 3-4 zero,
-// mantissa |c| in bits 0-2), unsigned codes u (0..15) as u / 8, whose
-// encoding is u itself.  The stored words W0, W1 of the pair are the dense
-// 96-bit string X = sum_k f_k << 6 k folded into 64 bits: with masks A, C
-// and E (per code kind, below) and rot16 a rotation by 16 bits,
-//   X[0:32]  = W0 & A
-//   X[64:96] = W1 & C
-//   X[32:64] = (rot16(V) & E) | (V & ~E),  V = (W0 & ~A) | (W1 & ~C).
-// A marks the bits of X[0:32] that can be nonzero (fields 0-4 and the low
-// bits of field 5), C those of X[64:96]; the bits of X[32:64] that can be
-// nonzero are exactly the zero positions of the other two words, half of
-// them moved by 16 bits.  Each word depends on its own 8 codes only: W0
-// holds fields 0-7 (X bits 0-47), W1 fields 8-15 (X bits 48-95).
+// e of word w = channel 8 w + e of the row), and the words of each 16-byte
+// chunk paired as (4 j, 4 j + 3) and (4 j + 1, 4 j + 2): the first word of
+// a pair (bit 1 of its index clear, "role 0") and its partner w ^ 3 ("role
+// 1") share one bit pattern.  Its purpose: the GEMM reads codes as FP6
+// E2M3 values (the gfx950 FP6 matrix cores run about 1.5x the FP8 rate),
+// whose encodings are 6 bits wide.  Let f_k be the 6-bit E2M3 encoding of
+// code k of a pair (k = 0..7 the role-0 word's codes, 8..15 its partner's):
+// signed codes c as the subnormal c / 8 (sign bit 5, exponent bits 3-4
+// zero, mantissa |c| in bits 0-2), unsigned codes u (0..15) as u / 8, whose
+// encoding is u itself.  The pair's words a (role 0) and b (role 1) are the
+// dense 96-bit string X = sum_k f_k << 6 k folded into 64 bits: with masks
+// A and C (per code kind, below),
+//   X[0:32] = a & A,   X[64:96] = b & C,   X[32:64] = (a & ~A) | (b & ~C).
+// A marks the bits of X[0:32] that can be nonzero, C those of X[64:96];
+// the bits of X[32:64] that can be nonzero are exactly ~A | ~C, and ~A, ~C
+// are disjoint (signed: field offsets {3, 4} and {0, 5} of X[32:64]), so
+// the GEMM opens a pair with four instructions and no rotation.  A packing
+// lane holds one word's 8 codes and takes the 16 bits of X[32:64] it does
+// not own from its partner's lane.
 // ---------------------------------------------------------------------------
 // Bitfield insert (mask ? a : b, bit by bit) and a funnel shift by a lane's
 // own amount, written out: for masks and shifts that differ between lanes
@@ -228,37 +229,56 @@ __device__ __forceinline__ float signed_const(float c, float flip) {
   return __uint_as_float(r);
 }
 
-constexpr uint32_t kSgnA = 0xE79E79E7u, kSgnC = 0x9E79E79Eu, kSgnE = 0x18611861u;
-constexpr uint32_t kUnsA = 0xCF3CF3CFu, kUnsC = 0x3CF3CF3Cu, kUnsE = 0x30C330C3u;
+constexpr uint32_t kSgnA = 0xE79E79E7u, kSgnC = 0x9E79E79Eu;
+constexpr uint32_t kUnsA = 0xCF3CF3CFu, kUnsC = 0x3CF3CF3Cu;
+
+// The value of lane l ^ XOR of the 16-lane DPP row: XOR = 3 (quad_perm
+// [3,2,1,0]) for packers whose lane l holds word w and lane l ^ 3 word
+// w ^ 3; XOR = 12 (row_mirror, lane 15 - l, then the quad permutation) for
+// packers that spread a word over a quad of lanes.  Every lane of the row
+// must execute it.
+template <int XOR>
+__device__ __forceinline__ uint32_t xchg_lanes(uint32_t v) {
+  static_assert(XOR == 3 || XOR == 12, "partner lane patterns");
+  if constexpr (XOR == 3) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x1B, 0xF, 0xF, false));
+  } else {
+    const int t = __builtin_amdgcn_mov_dpp(int(v), 0x140, 0xF, 0xF, false);
+    return uint32_t(__builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, false));
+  }
+}
 
 // Stored word from the 48-bit field string of its 8 codes (lo: bits 0-31,
-// hi: bits 32-47): an even word keeps lo's A bits and takes the field bits
-// 32-47 into its spare (~A) positions, in place or moved up by 16; an odd
-// word holds X bits 48-95 = (hi:lo) >> 16 at its C positions and lo's low
-// half in its spare (~C) positions.
-template <bool SIGNED>
-__device__ __forceinline__ uint32_t stored_word(uint32_t lo, uint32_t hi, bool odd) {
-  constexpr uint32_t kZ0 = ~(SIGNED ? kSgnA : kUnsA), kZ2 = ~(SIGNED ? kSgnC : kUnsC);
-  const uint32_t src = odd ? lo : hi;
-  const uint32_t dup = __builtin_amdgcn_perm(src, src, 0x01000100u);  // low half in both halves
-  const uint32_t base = alignbit_v(hi, lo, odd ? 16u : 0u);
-  return bfi32(odd ? kZ2 : kZ0, dup, base);
+// hi: bits 32-47), role as above.  Role 0 holds X[0:48] (lo = X[0:32]) and
+// needs X[48:64], the low 16 bits of its partner's lo; role 1 holds X[48:96]
+// and needs X[32:48], its partner's hi.  Each lane offers both halves in
+// one word (its lo's low 16 bits, its hi) and reads its partner's.
+template <bool SIGNED, int XOR = 3>
+__device__ __forceinline__ uint32_t pair_word(uint32_t lo, uint32_t hi, bool role) {
+  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC;
+  // v_perm_b32(P, Q, sel): selector bytes 0-3 pick bytes of Q, 4-7 of P
+  const uint32_t mine = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // lo[0:16] | hi[0:16] << 16
+  const uint32_t theirs = xchg_lanes<XOR>(mine);
+  // X[32:64]: role 0 = hi[0:16] | partner lo[0:16] << 16, role 1 = partner hi | lo[0:16] << 16
+  const uint32_t mid = __builtin_amdgcn_perm(theirs, mine, role ? 0x01000706u : 0x05040302u);
+  const uint32_t own = alignbit_v(hi, lo, role ? 16u : 0u);  // X[0:32] or X[64:96]
+  return bfi32(role ? kC : kA, own, mid);
 }
 
 // The 48-bit field string of a stored word's 8 codes (the inverse of
-// stored_word): lo = fields 0-4 and bits 0-1 of field 5, hi = the rest.
+// pair_word) from the word w and its partner p.
 template <bool SIGNED>
-__device__ __forceinline__ void stored_fields(uint32_t w, bool odd, uint32_t& lo, uint32_t& hi) {
-  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC, kE = SIGNED ? kSgnE : kUnsE;
-  const uint32_t v = w & (odd ? ~kC : ~kA);
-  const uint32_t d1 = (__builtin_amdgcn_alignbit(v, v, 16) & kE) | (v & ~kE);  // X[32:64] (this word's half)
-  if (odd) {
-    const uint32_t d2 = w & kC;
-    lo = __builtin_amdgcn_alignbit(d2, d1, 16);
-    hi = d2 >> 16;
+__device__ __forceinline__ void pair_fields(uint32_t w, uint32_t p, bool role, uint32_t& lo, uint32_t& hi) {
+  constexpr uint32_t kA = SIGNED ? kSgnA : kUnsA, kC = SIGNED ? kSgnC : kUnsC;
+  const uint32_t a = role ? p : w, b = role ? w : p;
+  const uint32_t mid = (a & ~kA) | (b & ~kC);  // X[32:64]
+  if (role) {
+    const uint32_t x2 = b & kC;  // X[64:96]
+    lo = __builtin_amdgcn_alignbit(x2, mid, 16);
+    hi = x2 >> 16;
   } else {
-    lo = w & kA;
-    hi = d1 & 0xFFFFu;
+    lo = a & kA;
+    hi = mid & 0xFFFFu;
   }
 }
 // field k (0-7) of a 48-bit field string
@@ -294,36 +314,39 @@ __device__ __forceinline__ void horner6(const uint32_t b[8], uint32_t& lo, uint3
   hi = (((b[7] << 6) + b[6]) << 6) + b[5];
 }
 
-// Stored word of 8 signed codes from their magic-rounded patterns; odd:
-// the word's index in the row is odd.
-__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8], bool odd) {
+// Stored word of 8 signed codes from their magic-rounded patterns; role:
+// bit 1 of the word's index in the row (the partner word w ^ 3 is packed by
+// lane l ^ XOR at the same time).
+template <int XOR = 3>
+__device__ __forceinline__ uint32_t pack8_bits(const uint32_t b[8], bool role) {
   uint32_t lo, hi;
   horner6(b, lo, hi);
   constexpr uint32_t kOff = 32u - kRoundMagicBits;  // mod 2^32
   const uint32_t slo = fp6_sign_magnitude(lo + f6_rep(kOff, 6), f6_rep(1u, 5));
   const uint32_t shi = fp6_sign_magnitude(hi + f6_rep(kOff, 3), f6_rep(1u, 3));
-  return stored_word<true>((slo & 0x3FFFFFFFu) | (shi << 30), shi >> 2, odd);
+  return pair_word<true, XOR>((slo & 0x3FFFFFFFu) | (shi << 30), shi >> 2, role);
 }
 // Stored word of 8 signed codes given as their 6-bit sign-magnitude fields
 // (bits 0-2 |c|, bit 5 the sign, as field6 returns them).
-__device__ __forceinline__ uint32_t pack8_fields(const uint32_t f[8], bool odd) {
+__device__ __forceinline__ uint32_t pack8_fields(const uint32_t f[8], bool role) {
   uint32_t lo, hi;
   horner6(f, lo, hi);
-  return stored_word<true>(lo, hi >> 2, odd);
+  return pair_word<true>(lo, hi >> 2, role);
 }
 // Stored word of 8 unsigned codes (0..15) from their magic-rounded patterns.
-__device__ __forceinline__ uint32_t pack8_ubits(const uint32_t b[8], bool odd) {
+__device__ __forceinline__ uint32_t pack8_ubits(const uint32_t b[8], bool role) {
   uint32_t lo, hi;
   horner6(b, lo, hi);
   constexpr uint32_t kOff = 0u - kRoundMagicBits;
-  return stored_word<false>(lo + f6_rep(kOff, 6), (hi + f6_rep(kOff, 3)) >> 2, odd);
+  return pair_word<false>(lo + f6_rep(kOff, 6), (hi + f6_rep(kOff, 3)) >> 2, role);
 }
 
 // One byte of the stored form for codes 2l, 2l+1 of a word, held by lane l of
-// a quad (lanes 4w..4w+3 hold word w, odd: w is odd): the quad's 8 patterns
-// are gathered into every lane (quad broadcasts), each lane packs the whole
-// word and keeps byte l.
-__device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1, int l, bool odd) {
+// a quad (lanes 4w..4w+3 hold word w of a 16-word group, role: bit 1 of w):
+// the quad's 8 patterns are gathered into every lane (quad broadcasts),
+// each lane packs the whole word (its partner w ^ 3 lies in the quad of
+// lanes l ^ 12) and keeps byte l.
+__device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1, int l, bool role) {
   uint32_t b[8];
   b[0] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0x00, 0xF, 0xF, false));
   b[1] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0x00, 0xF, 0xF, false));
@@ -333,7 +356,7 @@ __device__ __forceinline__ uint32_t pack2_bits_quad(uint32_t b0, uint32_t b1, in
   b[5] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0xAA, 0xF, 0xF, false));
   b[6] = uint32_t(__builtin_amdgcn_mov_dpp(int(b0), 0xFF, 0xF, 0xF, false));
   b[7] = uint32_t(__builtin_amdgcn_mov_dpp(int(b1), 0xFF, 0xF, 0xF, false));
-  return (pack8_bits(b, odd) >> (8 * l)) & 0xFFu;
+  return (pack8_bits<12>(b, role) >> (8 * l)) & 0xFFu;
 }
 
 __device__ __forceinline__ float safe_inv(float m, float num) { return m > 0.0f ? num / m : 0.0f; }
@@ -430,7 +453,7 @@ __device__ __forceinline__ float row16_max_dpp(float m) {
 // results, so it is taken of m / 7, whose reciprocal is normal for every
 // finite m >= 2^-100; 1 / m is not, for m above 2^126.)  s7 is the lane's
 // signed 1/7, signed_const(1.0f / 7.0f, flip), made once by the caller.
-__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float s7, bool odd) {
+__device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float s7, bool role) {
   float mm = m;
   if (__builtin_amdgcn_ballot_w64(tiny_positive(m)) != 0) {
     if (tiny_positive(m)) {
@@ -445,7 +468,7 @@ __device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float s7
   uint32_t b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) b[e] = rne_code_bits(v[e], inv);
-  return pack8_bits(b, odd);
+  return pack8_bits(b, role);
 }
 
 // ---------------------------------------------------------------------------
@@ -456,7 +479,7 @@ __device__ __forceinline__ uint32_t encode8_rcp(float (&v)[8], float m, float s7
 // 0 < d < 2^-100 are lifted by 2^64 (exact) as in encode8_rcp; d = 0 gives
 // z = 0 and codes 0.  Returns the word; z in z_out.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float nlo, uint32_t& z_out, bool odd) {
+__device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float nlo, uint32_t& z_out, bool role) {
   float d = hi + nlo, nl = nlo;
   if (__builtin_amdgcn_ballot_w64(d > 0.0f && d < kTinyMax) != 0) {
     if (d > 0.0f && d < kTinyMax) {
@@ -477,7 +500,7 @@ __device__ __forceinline__ uint32_t encode8_asym(float (&t)[8], float hi, float 
     b[e] = b[e] > kRoundMagicBits + 15u ? kRoundMagicBits + 15u : b[e];
   }
   z_out = z;
-  return pack8_ubits(b, odd);
+  return pack8_ubits(b, role);
 }
 
 }  // namespace rw4

@@ -103,14 +103,18 @@ def test_asymmetric_beats_symmetric_on_one_sided_data():
 
 
 def test_pack_uint4_layout_and_round_trip():
-    # even-word table: 1 -> bit 0; 2 -> 7; 15 -> 12-15; 7 -> 24-26; 8 -> 17; 9 -> 4, 23; 10 -> 11, 29
-    codes = np.array([[1, 2, 15, 0, 7, 8, 9, 10]], dtype=np.uint8)
-    assert oracle.pack_uint4(codes).tolist() == [[0x91, 0xF8, 0x82, 0x27]]
+    # word 0 of a 32-code chunk (pair (0, 3), word 3 zero): unsigned fields f_k = u
+    # in X = sum_k f_k << 6k; 1 -> X 0; 2 -> 7; 15 -> 12-15; 7 -> 24-26; 8 -> 33;
+    # 9 -> 36, 39; 10 -> 43, 45.  X[32:64] bit q (= X - 32) goes to word 0 when
+    # q mod 6 is 4 or 5 (q = 4, 11), to word 3 when it is 0 or 1 (q = 1, 7, 13)
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, :8] = [1, 2, 15, 0, 7, 8, 9, 10]
+    assert oracle.pack_uint4(codes).tolist() == [[0x91, 0xF8, 0x00, 0x07] + [0] * 8 + [0x82, 0x20, 0x00, 0x00]]
     rng = np.random.default_rng(5)
     c = rng.integers(0, 16, size=(4, 256)).astype(np.uint8)
     np.testing.assert_array_equal(oracle.unpack_uint4(oracle.pack_uint4(c)), c)
     with pytest.raises(ValueError):
-        oracle.pack_uint4(np.array([[16, 0, 0, 0, 0, 0, 0, 0]]))
+        oracle.pack_uint4(np.array([[16] + [0] * 31]))
 
 
 def test_weight_code_sums_brute_force():

@@ -87,8 +87,7 @@ def test_pack_rejects_minus_8():
         c[0, 3] = bad
         with pytest.raises(ValueError):
             oracle.pack_int4(c)
-    c = np.arange(-7, 9, dtype=np.int8).reshape(1, 16)
-    c[0, -1] = 0
+    c = np.concatenate([np.arange(-7, 8), np.arange(7, -8, -1), [0, 0]]).astype(np.int8).reshape(1, 32)
     assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(c)), c)
 
 
@@ -115,30 +114,36 @@ def test_pack_unpack_roundtrip_and_positions():
     p = oracle.pack_int4(c)
     assert p.shape == (5, 128) and p.dtype == np.uint8
     assert np.array_equal(oracle.unpack_int4(p), c)
-    # single codes at the positions of the layout table: (|c| bits 0-2, sign)
-    word = np.zeros((1, 8), dtype=np.int8)
-    word[0, 0] = -1                     # bits 0 and 5
-    assert oracle.pack_int4(word)[0].tolist() == [0x21, 0, 0, 0]
-    word[0] = [0, -7, 0, 0, 0, 0, 0, 0]  # bits 6, 7, 8 and 11
-    assert oracle.pack_int4(word)[0].tolist() == [0xC0, 0x09, 0, 0]
-    word[0] = [0, 0, 0, 0, 0, 0, 0, -3]  # code 7: bits 10, 27 and sign 15
-    assert oracle.pack_int4(word)[0].tolist() == [0, 0x84, 0, 0x08]
-    word[0] = [0, 0, 0, 0, 0, 7, 0, 0]   # code 5: bits 30, 31, 16
-    assert oracle.pack_int4(word)[0].tolist() == [0, 0, 0x01, 0xC0]
-    # odd words use the second table: code 8 + 2 = 10 with value -5 -> bits 12, 30 and sign 1
-    two = np.zeros((1, 16), dtype=np.int8)
-    two[0, 10] = -5
-    assert oracle.pack_int4(two)[0].tolist() == [0, 0, 0, 0, 0x02, 0x10, 0, 0x40]
-    # words are independent: a code never reaches outside its 4 bytes
-    two[0] = 0
-    two[0, 7] = -2
-    assert oracle.pack_int4(two)[0, 4:].tolist() == [0, 0, 0, 0]
+    # single codes of a 32-code chunk (words 0-3; pairs (0, 3) and (1, 2)),
+    # bytes worked out from the dense FP6 string X = sum_k f_k << 6 k of the
+    # pair (0, 3): X[0:32] lies in word 0, X[64:96] in word 3, and of
+    # X[32:64] the field offsets 3, 4 go to word 0, offsets 0, 5 to word 3
+    row = np.zeros((1, 32), dtype=np.int8)
+    row[0, 0] = -1                     # f_0 = 100001b: X bits 0 and 5 -> word 0
+    assert oracle.pack_int4(row)[0].tolist() == [0x21, 0, 0, 0] + [0] * 12
+    row[0] = 0
+    row[0, 1] = -7                     # f_1 = 100111b: X bits 6, 7, 8, 11 -> word 0
+    assert oracle.pack_int4(row)[0].tolist() == [0xC0, 0x09, 0, 0] + [0] * 12
+    row[0] = 0
+    row[0, 7] = -3                     # f_7: X bits 42, 43 (|c|) and 47 (sign) = X[32:64] bits 10, 11, 15
+    assert oracle.pack_int4(row)[0].tolist() == [0, 0x84, 0, 0] + [0] * 8 + [0, 0x08, 0, 0]
+    row[0] = 0
+    row[0, 5] = 7                      # f_5: X bits 30, 31 -> word 0; X bit 32 (offset 2) -> word 3 bit 0
+    assert oracle.pack_int4(row)[0].tolist() == [0, 0, 0, 0xC0] + [0] * 8 + [0x01, 0, 0, 0]
+    row[0] = 0
+    row[0, 26] = -5                    # word 3's code 2 = f_10: X bits 60, 62, 65 -> word 0 bit 28, word 3 bits 30, 1
+    assert oracle.pack_int4(row)[0].tolist() == [0, 0, 0, 0x10] + [0] * 8 + [0x02, 0, 0, 0x40]
+    row[0] = 0
+    row[0, 15] = -2                    # pair (1, 2) never reaches words 0 and 3
+    assert oracle.pack_int4(row)[0, :4].tolist() == [0] * 4 and oracle.pack_int4(row)[0, 12:].tolist() == [0] * 4
     # a negative zero (sign bit set, magnitude 0) decodes to 0
-    assert oracle.unpack_int4(np.array([[0x20, 0, 0, 0]], dtype=np.uint8)).tolist() == [[0] * 8]
+    assert oracle.unpack_int4(np.array([[0x20] + [0] * 15], dtype=np.uint8)).tolist() == [[0] * 32]
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.array([[8, 0, 0, 0, 0, 0, 0, 0]]))
+        oracle.pack_int4(np.array([[8] + [0] * 31]))
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.array([[-8, 0, 0, 0, 0, 0, 0, 0]]))
+        oracle.pack_int4(np.array([[-8] + [0] * 31]))
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.zeros((1, 16), dtype=np.int8))  # half a chunk
 
 
 def _fp6_dense(codes, signed):
@@ -154,34 +159,34 @@ def _fp6_dense(codes, signed):
     return x
 
 
-def _open_pair(w0, w1, signed):
+def _open_pair(a, b, signed):
     """The three words of the dense FP6 string from a stored word pair, by the
-    mask identity the GEMM applies (three masks and one 16-bit rotation)."""
-    A, C, E = (0xE79E79E7, 0x9E79E79E, 0x18611861) if signed else (0xCF3CF3CF, 0x3CF3CF3C, 0x30C330C3)
+    mask identity the GEMM applies (two masks, no rotation)."""
+    A, C = (0xE79E79E7, 0x9E79E79E) if signed else (0xCF3CF3CF, 0x3CF3CF3C)
     full = 0xFFFFFFFF
-    d0, d2 = w0 & A, w1 & C
-    v = (w0 & ~A & full) | (w1 & ~C & full)
-    r = ((v >> 16) | (v << 16)) & full
-    d1 = (r & E) | (v & ~E & full)
+    d0, d2 = a & A, b & C
+    d1 = (a & ~A & full) | (b & ~C & full)
     return d0 | (d1 << 32) | (d2 << 64)
 
 
 @pytest.mark.parametrize("signed", [True, False])
 def test_packed_pairs_open_into_dense_fp6(signed):
-    """Brute force over random rows: every pair of stored words, opened with the
-    mask identity, is exactly the dense FP6 E2M3 string of its 16 codes, and
-    the two tables use each of the 32 bit positions once."""
-    layout = oracle.SIGNED_LAYOUT if signed else oracle.UNSIGNED_LAYOUT
-    for tab in layout:
-        assert sorted(p for code in tab for p in code) == list(range(32))
+    """Brute force over random rows: every word pair (4 j, 4 j + 3) and
+    (4 j + 1, 4 j + 2), opened with the mask identity, is exactly the dense
+    FP6 E2M3 string of its 16 codes (the first word's 8, then its
+    partner's), and the table uses each bit of both words once."""
+    layout = oracle.SIGNED_PAIR_LAYOUT if signed else oracle.UNSIGNED_PAIR_LAYOUT
+    assert sorted(pos for code in layout for pos in code) == [(r, b) for r in (0, 1) for b in range(32)]
     rng = np.random.default_rng(10 if signed else 11)
-    c = rng.integers(-7, 8, size=(32, 64)) if signed else rng.integers(0, 16, size=(32, 64))
+    c = rng.integers(-7, 8, size=(32, 128)) if signed else rng.integers(0, 16, size=(32, 128))
     p = (oracle.pack_int4(c) if signed else oracle.pack_uint4(c)).astype(np.uint64)
     w = p[:, 0::4] | (p[:, 1::4] << np.uint64(8)) | (p[:, 2::4] << np.uint64(16)) | (p[:, 3::4] << np.uint64(24))
     for row in range(32):
         for j in range(4):
-            got = _open_pair(int(w[row, 2 * j]), int(w[row, 2 * j + 1]), signed)
-            assert got == _fp6_dense(c[row, 16 * j:16 * j + 16], signed), (row, j)
+            for a, b in ((0, 3), (1, 2)):
+                got = _open_pair(int(w[row, 4 * j + a]), int(w[row, 4 * j + b]), signed)
+                codes = np.concatenate([c[row, 32 * j + 8 * a:32 * j + 8 * a + 8], c[row, 32 * j + 8 * b:32 * j + 8 * b + 8]])
+                assert got == _fp6_dense(codes, signed), (row, j, a)
 
 
 def test_rrs_golden(golden_dir):
