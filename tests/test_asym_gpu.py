@@ -89,6 +89,7 @@ def test_asym_path(case):
     xd = gu.x_to_device(x, xdt)
     qa, sa, za = rw4.quantize_act_asym(t, xd)
     u = oracle.unpack_uint4(gu.to_np(qa))
+    assert np.array_equal(oracle.pack_uint4(u), gu.to_np(qa))  # the stored bytes are the oracle's packing
     sa_np, za_np = gu.to_np(sa), gu.to_np(za)
     assert np.array_equal(za_np, np.rint(za_np)) and za_np.min() >= 0 and za_np.max() <= 15
     ref = oracle.quantize_act(x, spec, "group128_asym")

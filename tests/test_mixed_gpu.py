@@ -62,6 +62,7 @@ def test_mixed_path(case):
     xd = gu.x_to_device(x, xdt)
     qa, sa = rw4.quantize_act_mixed(t, xd, slot, n8)
     planes = oracle.unpack_int4(gu.to_np(qa)).astype(np.int64)
+    assert np.array_equal(oracle.pack_int4(planes), gu.to_np(qa))  # both planes in the canonical stored form
     sa_np = gu.to_np(sa)
     ref = oracle.quantize_act(x, spec, "group128_mixed", order=groups8)
     # rebuild the one-code form from the planes

@@ -26,6 +26,13 @@ if torch.cuda.is_available():
     from tests import gpu_util as gu  # noqa: E402
 
 
+def _check_bytes(q_gpu, what):
+    """The stored bytes are exactly the oracle's packing of the codes they hold
+    (the paired form, zero with sign 0), byte for byte."""
+    qb = gu.to_np(q_gpu)
+    assert np.array_equal(oracle.pack_int4(oracle.unpack_int4(qb)), qb), f"{what}: stored bytes not canonical"
+
+
 def _check_quant(codes_gpu, s_gpu, ref_codes, ref_ratio, ref_s, what):
     n, tot = compare_codes(codes_gpu, ref_codes, ref_ratio)
     s_gpu = np.asarray(s_gpu, dtype=np.float64)
@@ -49,6 +56,7 @@ def _quant_parity(wl, rows=None):
     t = gu.transform_for(wl)
     x = gu.x_to_device(wl.x, wl.x_dtype)
     qa, sa, ws = gu.quantize(t, x, wl.mode)
+    _check_bytes(qa, f"{wl.name} act")
     ref = oracle.quantize_act(wl.x if rows is None or wl.mode == "rrs" else wl.x[rows], spec, wl.mode)
     codes = _unpack(qa)
     sa_np = gu.to_np(sa)
@@ -69,6 +77,7 @@ def _weight_parity(wl, t, cols=None):
     spec = spec_of(wl)
     w = torch.from_numpy(wl.w).to(gu.DEV)
     qw, sw = rw4.pack_weight(t, w, "kn")
+    _check_bytes(qw, f"{wl.name} weight")
     wsel = wl.w if cols is None else wl.w[:, cols]
     ref = oracle.pack_weight(wsel, spec)
     codes = _unpack(qw)

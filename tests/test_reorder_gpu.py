@@ -63,6 +63,7 @@ def _run(name, x, xdt, K, block, signs, w, cols=None, rows=None):
     assert np.all(sw_np == sw_np[:, :1])  # one scale per output channel
     qw_ord = rw4.permute_codes(qw, order)
     qw_ord_np = gu.to_np(qw_ord)
+    assert np.array_equal(oracle.pack_int4(oracle.unpack_int4(qw_ord_np)), qw_ord_np)  # permuted codes repacked canonically
     assert np.array_equal(oracle.unpack_int4(qw_ord_np), oracle.permute_codes(oracle.unpack_int4(gu.to_np(qw)), order_np))
     # the product: identical codes element-wise, then end to end
     y = gu.to_np(rw4.w4a4_gemm(qa, sa, qw_ord, sw, torch.float32))
