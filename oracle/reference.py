@@ -46,10 +46,11 @@ reason in the design notes):
     range the packed form holds;
   * packed INT4 (the pages fix no layout): 4 bits per code, 8 codes per
     little-endian 32-bit word, each code as sign-magnitude (|c| in 3 bits,
-    sign 1 for negative, zero with sign 0) at bit positions given by a
-    fixed table, one table for even and one for odd words of a row (the
-    layout of the stored form, chosen so that a pair of words opens into
-    16 FP6 E2M3 values with a few masks);
+    sign 1 for negative, zero with sign 0); the words of each 16-byte
+    chunk pair up as (4j, 4j+3) and (4j+1, 4j+2), and a fixed table gives
+    the positions of a pair's 16 codes' bits in its two words (the layout
+    of the stored form, chosen so that a pair opens into 16 FP6 E2M3
+    values with two masks);
   * 8-bit groups for extreme outliers ([Paro] section 4.1, mixed
     precision): the caller names the 128-channel groups; their codes are
     symmetric with 225 levels, q8 in [-112, 112] (scale max / 112), split
