@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   if (j >= K / 8) return;
   const int64_t row = row0 + blockIdx.y;
   const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + row * (K / 2));
-  const uint32_t w = qrow[j], wp = qrow[j ^ 3];  // K / 8 is a multiple of 16
+  const uint32_t w = qrow[j], wp = qrow[j ^ 3];  // rows hold whole 16-byte chunks (K % 64 == 0)
   const float sc = s[row * (K >> log2g) + ((j * 8) >> log2g)];
   uint32_t lo, hi;
   pair_fields<true>(w, wp, (j & 2) != 0, lo, hi);
