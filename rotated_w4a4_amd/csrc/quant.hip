@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256) void quant_h128_act_kernel(const void* __restr
   // its h plane in place and its l plane in the extra group G + slot
   const int64_t GX = MIXED ? G + n8 : G;
   const int32_t slot = MIXED && grp < G ? slot_of_group[grp] : -1;
+  // uniform over a group's 16 lanes, so the packers' exchange with lane ^ 3 stays inside one branch
   const bool is8 = MIXED && slot >= 0 && slot < n8;
   const bool any8 = MIXED && __builtin_amdgcn_ballot_w64(is8) != 0;  // wave-uniform
   const uint32_t l_off = is8 ? uint32_t((G + slot) * 64 + h128_lane_word(sub) * 4) : kOutOfRange;
@@ -1256,7 +1257,7 @@ __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __res
 #pragma unroll
       for (int u = 0; u < kPermuteWords; ++u) {
         const int i = int(threadIdx.x) + 256 * u;
-        if (r < nr && i < W) {
+        if (r < nr && i < W) {  // uniform over each 16-lane row (W is a multiple of 16): the exchange below is safe
           uint32_t lo, hi;
           pair_fields<true>(wv[r][u], xchg_lanes<3>(wv[r][u]), (i & 2) != 0, lo, hi);
           uint32_t f[8];
@@ -1276,7 +1277,7 @@ __global__ __launch_bounds__(256) void permute_codes_kernel(const uint8_t* __res
 #pragma unroll
       for (int u = 0; u < kPermuteWords; ++u) {
         const int i = int(threadIdx.x) + 256 * u;
-        if (i >= W) break;
+        if (i >= W) break;  // uniform over each 16-lane row, as above (pack8_fields exchanges with lane ^ 3)
         uint32_t f[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = fr[src[u][e]];
