@@ -6,8 +6,11 @@ oracle (the same bars as tests/test_parity_gpu.py).
   troublesome for RRS: then those two tokens alone set every group's
   smoothing scale and every other token is smoothed by maxima far above its
   own.  The kernels must still match the oracle there.
-* Random shapes: 16 seeded cases with M in [1, 300], K = 128 * [1, 40],
-  N in [1, 300] over the transforms and modes each shape supports.
+* Random shapes: 48 seeded cases over the transforms and modes each shape
+  supports (block-128 Hadamard, with and without random signs, larger
+  blocks, Rotated Runtime Smooth, Givens): M in [1, 300], K = 128 * [1, 40],
+  N in [1, 300] on the small-M kernel, and every eighth case with M in
+  [600, 1100], N in [1600, 2300] on the tiled kernel.
 """
 import numpy as np
 import pytest
@@ -44,14 +47,15 @@ def test_rrs_two_outlier_tokens(K, block):
 def _random_cases():
     rng = np.random.default_rng(20260103)
     cases = []
-    for i in range(16):
-        M = int(rng.integers(1, 301))
-        N = int(rng.integers(1, 301))
-        kind = ["h128", "rrs", "givens", "hblock"][i % 4]
+    for i in range(48):
+        big = i % 8 == 7
+        M = int(rng.integers(600, 1101)) if big else int(rng.integers(1, 301))
+        N = int(rng.integers(1600, 2301)) if big else int(rng.integers(1, 301))
+        kind = ["h128", "rrs", "givens", "hblock", "signed"][i % 5]
         if kind == "rrs" or kind == "hblock":
             K = int(rng.choice([512, 1024, 2048, 4096]))
         else:
-            K = 128 * int(rng.integers(1, 41))
+            K = 128 * int(rng.integers(1, 9 if big else 41))
         xdt = "bf16" if rng.random() < 0.7 else "f32"
         cases.append((f"rand{i}_{kind}_M{M}_K{K}_N{N}_{xdt}", M, K, N, kind, xdt, int(rng.integers(1 << 30))))
     return cases
@@ -70,6 +74,11 @@ def test_random_shapes(case):
     kw = {}
     if kind == "h128":
         tr, mode = ("hadamard", 128), "group128"
+    elif kind == "signed":
+        # blocks above 128 need K in {512, ..., 8192}
+        block = int(rng.choice([128, 256])) if K in (512, 1024, 2048, 4096, 8192) else 128
+        tr, mode = ("hadamard", block), "group128"
+        kw = {"signs": datagen.random_signs(seed % 1000, K)}
     elif kind == "rrs":
         tr, mode = ("hadamard", int(rng.choice([128, K]))), "rrs"
     elif kind == "hblock":
