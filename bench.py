@@ -191,7 +191,7 @@ def capture_steps(torch, step, nsets):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="untimed sustained load before timing, at least (after the warm-up steps)")
